@@ -1,0 +1,143 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case patches one oracle routine with a plausible bug (wrong tie rule,
+dropped term, swapped axis, wrong sign, missing saturation, wrong GQA index)
+and checks that the corresponding pin test then fails.
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+import oracle.cache as C
+import oracle.quant as Q
+from tests import test_oracle_pins as P
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_round_half_away_is_caught(monkeypatch):
+    monkeypatch.setattr(Q.np, "rint", lambda x: np.trunc(x + np.copysign(0.5, x)))
+    assert _fails(P.test_asym_ties_round_to_even)
+
+
+def test_dropped_zero_point_is_caught(monkeypatch):
+    monkeypatch.setattr(Q, "asym_dequantize", lambda c, s, z: (c.astype(np.float32) * s).astype(np.float32))
+    assert _fails(P.test_asym_codes_range_error_bound_and_brute_force)
+
+
+def test_swapped_grouping_axis_is_caught(monkeypatch):
+    orig = C.quantize_part
+
+    def swapped(x, spec, fp8_scale=None):
+        if spec.axis == C.PER_CHANNEL:
+            spec = C.Spec(spec.scheme, spec.bits, C.PER_TOKEN, 0)
+        elif spec.axis == C.PER_TOKEN:
+            spec = C.Spec(spec.scheme, spec.bits, C.PER_CHANNEL, 0)
+        return orig(x, spec, fp8_scale)
+
+    monkeypatch.setattr(C, "quantize_part", swapped)
+    assert _fails(P.test_int8_table_reproduces_printed_digits)
+    assert _fails(P.test_int4_per_channel_beats_per_token)
+
+
+def test_symmetric_scale_off_by_one_level_is_caught(monkeypatch):
+    def sym128(x, axis):
+        x = np.asarray(x, dtype=np.float32)
+        a = np.abs(x).max(axis=axis, keepdims=True)
+        s = (np.maximum(a, Q.EPS) / np.float32(128.0)).astype(np.float32)
+        return np.clip(np.rint(x / s), -127, 127).astype(np.int8), s
+
+    monkeypatch.setattr(Q, "sym_quantize", sym128)
+    assert _fails(P.test_int8_table_reproduces_printed_digits)
+
+
+def test_missing_fp8_saturation_is_caught(monkeypatch):
+    orig = Q.e4m3_encode
+
+    def nosat(y):
+        y = np.asarray(y, dtype=np.float32)
+        out = orig(y)
+        return np.where(np.abs(y) > 464, np.uint8(0x7F) | (out & 0x80), out).astype(np.uint8)
+
+    monkeypatch.setattr(Q, "e4m3_encode", nosat)
+    assert _fails(P.test_e4m3_page_facts)
+
+
+def test_fp8_ties_away_is_caught(monkeypatch):
+    def away(y):
+        y = np.asarray(y, dtype=np.float32)
+        a = np.minimum(np.abs(y).astype(np.float64), 448.0)
+        d = np.abs(Q._GRID_VALS[None, :] - a[:, None])
+        best = d.min(axis=1, keepdims=True)
+        idx = np.where(d == best, np.arange(d.shape[1])[None, :], -1).max(axis=1)  # larger on ties
+        return (Q._GRID_CODES[idx] | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+
+    monkeypatch.setattr(Q, "e4m3_encode", away)
+    assert _fails(P.test_e4m3_encode_matches_library_cast_after_clamp)
+
+
+def test_rope_sign_flip_is_caught(monkeypatch):
+    orig = A.rope
+    monkeypatch.setattr(A, "rope", lambda x, pos, base: orig(x, -np.asarray(pos), base))
+    assert _fails(P.test_rope_closed_forms)
+
+
+def test_rope_pairing_halves_is_caught(monkeypatch):
+    def halves(x, positions, base):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        th = np.power(float(base), -2.0 * np.arange(D // 2) / D)
+        ang = np.asarray(positions, dtype=np.float64)[:, None] * th[None]
+        c, s = np.cos(ang), np.sin(ang)
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+    monkeypatch.setattr(A, "rope", halves)
+    assert _fails(P.test_rope_closed_forms)
+
+
+def test_wrong_gqa_mapping_is_caught(monkeypatch):
+    orig = A.decode_attention
+
+    def interleaved(q, K, V, sm, pre_rope_base=None, heads=None):
+        B, Hq, D = q.shape
+        Hkv = K.shape[1]
+        # query head h -> kv head h % Hkv instead of h // n_rep
+        perm = np.array([(h % Hkv) * (Hq // Hkv) + h // Hkv for h in range(Hq)])
+        out = orig(q[:, np.argsort(perm)], K, V, sm, pre_rope_base)
+        return out[:, perm]
+
+    monkeypatch.setattr(A, "decode_attention", interleaved)
+    assert _fails(P.test_attention_matches_library_sdpa_fp64)
+
+
+def test_transposed_attention_operand_is_caught(monkeypatch):
+    def bad(q, K, V, sm):
+        q = np.asarray(q, dtype=np.float64)
+        K = np.asarray(K, dtype=np.float64)
+        V = np.asarray(V, dtype=np.float64)
+        lg = (K @ q) * sm
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        return (V.T[:, :len(p)] @ p) if V.shape[0] == V.shape[1] else p @ V[::-1], lg
+
+    monkeypatch.setattr(A, "single_head", bad)
+    assert _fails(P.test_attention_matches_library_sdpa_fp64)
+
+
+@pytest.mark.parametrize("bug", ["window_off_by_one", "no_fp16_staging"])
+def test_residual_bugs_are_caught(monkeypatch, bug):
+    if bug == "window_off_by_one":
+        orig = C.quantized_tokens
+        monkeypatch.setattr(C, "quantized_tokens",
+                            lambda cfg, T: (orig(cfg, T + 1) if not C.one_shot(cfg) else T))
+        assert _fails(P.test_residual_split_properties, 32, 32)
+    else:
+        monkeypatch.setattr(C, "has_window", lambda cfg: False)
+        assert _fails(P.test_window_holds_fp16_values)

@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix (no GPU).
+
+Each test ties an oracle routine to something other than itself: a table the
+pages print, a closed form, a library routine used as an independent check,
+brute force on tiny inputs, or an invariant a plausible mistake would break.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import workloads as W
+from oracle import attention as A
+from oracle import cache as C
+from oracle import quant as Q
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# The printed INT8 table (FP8 KV cache page, "Why does the K cache break before
+# the V cache?") -- pins symmetric INT8, the three grouping axes and attention.
+# ---------------------------------------------------------------------------
+
+def _int8_table(sym_quant=None):
+    x = W.single_head_inputs("c1_int8_sym_single_head")
+    K, V, q = x["K"][None, None], x["V"][None, None], x["q"]
+
+    def qd(t, axis):
+        spec = C.Spec(C.INT_SYM, 8, axis, 0)
+        return C.quantize_part(t, spec)["deq"][0, 0]
+
+    Kt, Kc = qd(K, C.PER_TENSOR), qd(K, C.PER_CHANNEL)
+    Vt, Vk = qd(V, C.PER_TENSOR), qd(V, C.PER_TOKEN)
+    K0, V0 = K[0, 0], V[0, 0]
+    sm = 1.0 / math.sqrt(128)
+    ref, ref_lg = A.single_head(q, K0, V0, sm)
+    rows = {}
+    for name, (Kq, Vq) in {
+        "K+V per-tensor INT8": (Kt, Vt),
+        "K per-channel, V per-token": (Kc, Vk),
+        "V per-token only (K exact)": (K0, Vk),
+        "K per-tensor only (V exact)": (Kt, V0),
+    }.items():
+        out, lg = A.single_head(q, Kq, Vq, sm)
+        rows[name] = (A.rel_l2(out, ref), float(np.abs(lg - ref_lg).max()))
+    return rows
+
+
+def test_int8_table_reproduces_printed_digits():
+    g = _gold("int8_synthetic_head_table.json")
+    rows = _int8_table()
+    for name, (err, lg) in g["rows"].items():
+        got_err, got_lg = rows[name]
+        assert round(got_err, 4) == pytest.approx(err, abs=1e-12), (name, got_err)
+        assert round(got_lg, 3) == pytest.approx(lg, abs=1e-12), (name, got_lg)
+
+
+def test_int8_error_ordering_k_dominates():
+    """K error dominates: per-tensor >> per-channel K + per-token V > V only."""
+    r = _int8_table()
+    assert r["K+V per-tensor INT8"][0] > 4 * r["K per-channel, V per-token"][0]
+    assert r["K per-channel, V per-token"][0] > r["V per-token only (K exact)"][0]
+    assert r["V per-token only (K exact)"][1] == 0.0
+    # a logit error of 0.86 scales a weight by e^0.86 ~ 2.4
+    assert math.exp(r["K+V per-tensor INT8"][1]) == pytest.approx(2.37, abs=0.02)
+
+
+def test_absmax_over_median_about_130():
+    g = _gold("int8_synthetic_head_table.json")
+    K = W.single_head_inputs("c1_int8_sym_single_head")["K"]
+    r = np.abs(K).max() / np.median(np.abs(K))
+    assert round(r / 10) * 10 == g["also"]["absmax_over_median_K"]
+
+
+# ---------------------------------------------------------------------------
+# Asymmetric INT4 per-token vs per-channel keys ("...Need Different Axes" page,
+# "Why does per-token key quantization destroy accuracy?").  The page claims an
+# order of magnitude; the listing itself gives about 2x (reading recorded).
+# ---------------------------------------------------------------------------
+
+def test_int4_per_channel_beats_per_token():
+    x = W.single_head_inputs("c2_int4_asym_single_head")
+    K = x["K"][None, None]
+    tok = C.quantize_part(K, C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 0))["deq"][0, 0]
+    ch = C.quantize_part(K, C.Spec(C.INT_ASYM, 4, C.PER_CHANNEL, 0))["deq"][0, 0]
+    e_tok, e_ch = A.rel_l2(tok, K[0, 0]), A.rel_l2(ch, K[0, 0])
+    assert e_ch < e_tok
+    assert 1.6 < e_tok / e_ch < 2.6, (e_tok, e_ch)
+    q8 = x["q8"].astype(np.float64)
+    ref = q8 @ K[0, 0].astype(np.float64).T
+    l_tok = A.rel_l2(q8 @ tok.astype(np.float64).T, ref)
+    l_ch = A.rel_l2(q8 @ ch.astype(np.float64).T, ref)
+    assert l_ch < l_tok
+
+
+# ---------------------------------------------------------------------------
+# asymmetric min-max invariants and brute force
+# ---------------------------------------------------------------------------
+
+@settings(max_examples=200, deadline=None)
+@given(bits=st.sampled_from([2, 4, 8]),
+       vals=st.lists(st.floats(-1e3, 1e3, allow_nan=False, width=32), min_size=1, max_size=9))
+def test_asym_codes_range_error_bound_and_brute_force(bits, vals):
+    x = np.array(vals, dtype=np.float32)
+    c, s, z = Q.asym_quantize(x, bits, axis=0)
+    qmax = 2 ** bits - 1
+    assert c.min() >= 0 and c.max() <= qmax
+    xh = Q.asym_dequantize(c, s, z)
+    s64 = float(s[0])
+    ulp = np.spacing(np.abs(x).max() + abs(float(z[0])) + s64 * qmax).astype(np.float64)
+    err = np.abs(xh.astype(np.float64) - x)
+    assert np.all(err <= s64 / 2 + 4 * ulp)
+    # the minimum maps to code 0 and reconstructs exactly
+    i = int(np.argmin(x))
+    assert c[i] == 0 and xh[i] == x[i]
+    # brute force: the chosen level is the nearest of all 2^b levels (up to rounding)
+    levels = np.arange(qmax + 1, dtype=np.float64) * s64 + float(z[0])
+    best = np.abs(x[:, None].astype(np.float64) - levels[None, :]).min(axis=1)
+    mine = np.abs(x.astype(np.float64) - (c.astype(np.float64) * s64 + float(z[0])))
+    assert np.all(mine <= best + 4 * ulp)
+
+
+def test_asym_ties_round_to_even():
+    # (x - min)/scale lands exactly on k + 1/2: 0.5 -> 0, 2.5 -> 2 (half-to-even)
+    x = np.array([0.0, 0.5, 2.5, 3.0], dtype=np.float32)
+    c, s, z = Q.asym_quantize(x, 2, axis=0)
+    assert float(s[0]) == 1.0 and float(z[0]) == 0.0
+    assert c.tolist() == [0, 0, 2, 3]
+
+
+def test_asym_constant_group_uses_epsilon_floor():
+    x = np.full(8, 3.25, dtype=np.float32)
+    c, s, z = Q.asym_quantize(x, 4, axis=0)
+    assert np.all(c == 0)
+    assert float(s[0]) == float(np.float32(np.float32(1e-8) / np.float32(15)))
+    assert np.all(Q.asym_dequantize(c, s, z) == x)
+
+
+# ---------------------------------------------------------------------------
+# symmetric INT8
+# ---------------------------------------------------------------------------
+
+@settings(max_examples=200, deadline=None)
+@given(vals=st.lists(st.floats(-1e4, 1e4, allow_nan=False, width=32), min_size=1, max_size=12))
+def test_sym_int8_range_and_bound(vals):
+    x = np.array(vals, dtype=np.float32)
+    c, s = Q.sym_quantize(x, axis=0)
+    assert c.min() >= -127 and c.max() <= 127
+    if np.abs(x).max() >= 1e-8:          # below the floor every code is 0
+        i = int(np.argmax(np.abs(x)))
+        assert abs(int(c[i])) == 127
+    xh = Q.sym_dequantize(c, s)
+    s64 = float(s[0])
+    assert np.all(np.abs(xh.astype(np.float64) - x) <= s64 / 2 + 4 * np.spacing(np.float32(np.abs(x).max() + s64)))
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3: closed-form grid, page facts, library cross-check
+# ---------------------------------------------------------------------------
+
+def test_e4m3_grid_matches_library_decode():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = Q.e4m3_value_of_code(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(nan, np.isnan(mine))
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(mine[~nan], lib[~nan])
+
+
+def test_e4m3_page_facts():
+    g = _gold("e4m3_format_facts.json")["facts"]
+    vals = Q.e4m3_value_of_code(np.arange(0x7F))
+    assert vals.max() == g["e4m3_max_finite"]
+    # <= 6.25% relative rounding error in the normal range (3 mantissa bits)
+    rng = np.random.default_rng(1)
+    y = np.exp(rng.uniform(np.log(2.0 ** -6), np.log(448.0), 20000)).astype(np.float32)
+    rel = np.abs(Q.e4m3_decode(Q.e4m3_encode(y)) - y) / y
+    assert rel.max() <= g["e4m3_max_relative_step_error"] + 1e-9
+    assert rel.max() > 0.05
+    # saturation instead of NaN beyond the range
+    big = np.array([448, 460, 464, 465, 1e6, -1e6], dtype=np.float32)
+    assert Q.e4m3_encode(big).tolist() == [0x7E] * 4 + [0x7E, 0xFE]
+    # E5M2 max finite from its own closed form: (1 + 3/4) * 2^(30 - 15)
+    assert (1 + 3 / 4) * 2.0 ** 15 == g["e5m2_max_finite"]
+
+
+def test_e4m3_encode_matches_library_cast_after_clamp():
+    rng = np.random.default_rng(2)
+    y = np.concatenate([
+        rng.standard_normal(50000).astype(np.float32) * 40,
+        rng.standard_normal(20000).astype(np.float32) * 1e-2,
+        (Q.e4m3_value_of_code(np.arange(0x7F))).astype(np.float32),
+        # midpoints between neighbours (exact ties) and their neighbours
+        ((Q.e4m3_value_of_code(np.arange(0x7E)) + Q.e4m3_value_of_code(np.arange(1, 0x7F))) / 2).astype(np.float32),
+        np.array([0.0, -0.0, 2.0 ** -10, 1.5 * 2.0 ** -9, -(2.0 ** -10), 3 * 2.0 ** -11], dtype=np.float32),
+    ])
+    y = np.concatenate([y, -y])
+    mine = Q.e4m3_encode(y)
+    lib = torch.from_numpy(np.clip(y, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, lib)
+    # spot values (ties to even, signed zero)
+    sp = Q.e4m3_encode(np.array([-0.0, 2.0 ** -10, 1.5 * 2.0 ** -9], dtype=np.float32)).tolist()
+    assert sp == [0x80, 0x00, 0x02]
+
+
+def test_fp8_scale_calibration():
+    assert float(Q.fp8_scale_from_absmax(np.float32(448.0))) == 1.0
+    assert float(Q.fp8_scale_from_absmax(np.float32(0.0))) == 1.0
+    x = np.array([[[[1.0, -896.0]]]], dtype=np.float32)
+    s = C.fp8_calibrate(x)
+    assert s.tolist() == [2.0]
+    assert Q.fp8_quantize(np.float32(-896.0), s[0]).item() == 0xFE
+
+
+# ---------------------------------------------------------------------------
+# attention: plain definition vs library, closed forms
+# ---------------------------------------------------------------------------
+
+def test_attention_matches_library_sdpa_fp64():
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, T, D = 2, 8, 2, 37, 16
+    q = rng.standard_normal((B, Hq, D))
+    K = rng.standard_normal((B, Hkv, T, D))
+    V = rng.standard_normal((B, Hkv, T, D))
+    out = A.decode_attention(q, K, V, 1 / math.sqrt(D))
+    n_rep = Hq // Hkv
+    Kt = torch.from_numpy(np.repeat(K, n_rep, axis=1))
+    Vt = torch.from_numpy(np.repeat(V, n_rep, axis=1))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], Kt, Vt).numpy()[:, :, 0]
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((50, 8))
+    V = rng.standard_normal((50, 8))
+    out, _ = A.single_head(np.zeros(8), K, V, 0.3)
+    assert np.allclose(out, V.mean(axis=0), atol=1e-14)
+    Ke = np.tile(rng.standard_normal(8), (50, 1))
+    out, _ = A.single_head(rng.standard_normal(8), Ke, V, 0.3)
+    assert np.allclose(out, V.mean(axis=0), atol=1e-14)
+    # one dominant logit -> that token's value
+    q = np.zeros(8); q[0] = 1.0
+    Kd = np.zeros((50, 8)); Kd[17, 0] = 1e4
+    out, _ = A.single_head(q, Kd, V, 1.0)
+    assert np.allclose(out, V[17], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# RoPE: closed forms fixing sign, pairing and frequencies
+# ---------------------------------------------------------------------------
+
+def test_rope_closed_forms():
+    # D = 2, theta_0 = 1: [1, 0] at position j -> [cos j, sin j]
+    pos = np.arange(6)
+    r = A.rope(np.tile([1.0, 0.0], (6, 1)), pos, 10000.0)
+    assert np.allclose(r, np.stack([np.cos(pos), np.sin(pos)], axis=1), atol=1e-15)
+    # D = 4, base 10000: theta_1 = 10000^(-2/4) = 0.01 -> position 100 is 1 radian on pair 1
+    x = np.array([[0.0, 0.0, 0.0, 1.0]])
+    r = A.rope(x, np.array([100]), 10000.0)
+    assert np.allclose(r[0], [0, 0, -math.sin(1.0), math.cos(1.0)], atol=1e-15)
+    # position 0 is the identity; rotations keep pair norms; relative-position property
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((5, 16))
+    assert np.allclose(A.rope(k, np.zeros(5), 10000.0), k)
+    rk = A.rope(k, np.arange(5) * 1000, 10000.0)
+    assert np.allclose(np.hypot(rk[:, 0::2], rk[:, 1::2]), np.hypot(k[:, 0::2], k[:, 1::2]))
+    q = rng.standard_normal(16)
+    d1 = A.rope(q[None], np.array([40]), 500.0) @ A.rope(k, np.full(5, 33), 500.0).T
+    d2 = A.rope(q[None], np.array([7]), 500.0) @ A.rope(k, np.zeros(5), 500.0).T
+    assert np.allclose(d1, d2)
+
+
+# ---------------------------------------------------------------------------
+# residual window, grouping, byte accounting
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,G", [(0, 1), (32, 32), (128, 128), (64, 1), (0, 32), (96, 32)])
+def test_residual_split_properties(R, G):
+    cfg = C.Cfg(1, 1, 1, 16, C.Spec(C.INT_ASYM, 4, C.PER_CHANNEL if G > 1 else C.PER_TOKEN, G if G > 1 else 0),
+                C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 0), R=R)
+    for T in range(0, 700, 7):
+        tq = C.quantized_tokens(cfg, T)
+        assert tq % G == 0 and 0 <= tq <= T
+        if T >= R:
+            assert R <= T - tq <= R + G - 1
+        else:
+            assert tq == 0
+        if C.has_window(cfg):
+            assert T - tq < C.ring_slots(cfg)
+
+
+def test_fold_equals_one_shot_quantization():
+    """Quantizing a later cache state from scratch must agree, on the earlier
+    state's quantized groups, with the earlier state (blocks are independent)."""
+    K, V = W.random_case(1, 1, 2, 200, 32)
+    cfg = C.Cfg(1, 2, 2, 32, C.Spec(C.INT_ASYM, 2, C.PER_CHANNEL, 32), C.Spec(C.INT_ASYM, 2, C.PER_TOKEN, 16), R=32)
+    a = C.quantize_cache(cfg, K[0], V[0], 130)
+    b = C.quantize_cache(cfg, K[0], V[0], 199)
+    tq = a["Tq"]
+    assert tq == 96 and b["Tq"] == 160
+    assert np.array_equal(a["k"]["codes"], b["k"]["codes"][:, :, :tq])
+    assert np.array_equal(a["k"]["scale"], b["k"]["scale"][:, :, :tq // 32])
+    assert np.array_equal(a["v"]["zero"], b["v"]["zero"][:, :, :tq])
+
+
+def test_kv_bytes_facts():
+    g = _gold("kv_bytes_facts.json")
+    L, H, D = g["llama70b"]["layers"], g["llama70b"]["kv_heads"], g["llama70b"]["head_dim"]
+    per = C.cache_bytes_per_token(L, H, D, 2)
+    assert per == g["fp16_bytes_per_token"] == 320 * 1024
+    assert per * 131072 / 2 ** 30 == g["fp16_gib_at_128k"]
+    assert C.cache_bytes_per_token(L, H, D, 1) * 131072 / 2 ** 30 == g["fp8_gib_at_128k"]
+    assert per * 32768 * 8 / 2 ** 30 == g["fp16_gb_32k_batch8"]
+    assert C.cache_bytes_per_token(L, H, D, 1) * 32768 * 8 / 2 ** 30 == g["int8_gb_32k_batch8"]
+    a, b = g["vllm_capacity_tokens"]
+    assert b == 2 * a
+
+
+# ---------------------------------------------------------------------------
+# byte layout: hand-derived bytes from the layout definition
+# ---------------------------------------------------------------------------
+
+def test_row_packing_hand_bytes():
+    c4 = (np.arange(16) % 16).astype(np.uint8)[None]
+    assert C.pack_rows(c4, 4)[0].tolist() == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    c2 = (np.arange(8) % 4).astype(np.uint8)[None]
+    assert C.pack_rows(c2, 2)[0].tolist() == [0xE4, 0xE4]
+    s8 = np.array([[-1, 127, -127, 0]], dtype=np.int8)
+    assert C.pack_rows(s8, 8)[0].tolist() == [0xFF, 0x7F, 0x81, 0x00]
+
+
+def test_vblock_packing_hand_bytes():
+    D, T = 16, 32
+    t, c = np.meshgrid(np.arange(T), np.arange(D), indexing="ij")
+    codes = ((t + c) % 16).astype(np.uint8)
+    blk = C.pack_vblocks(codes, 4)
+    assert blk.shape == (1, 32 * 16 * 4 // 8)
+    # lane 0 (g=0, n=0): channel 0, tokens 0..7 -> codes 0..7
+    assert blk[0, 0:4].tolist() == [0x10, 0x32, 0x54, 0x76]
+    # lane 17 (g=1, n=1): channel 1, tokens 8..15 -> codes 9..15, 0
+    assert blk[0, 68:72].tolist() == [0xA9, 0xCB, 0xED, 0x0F]
+    # int2, D=32: lane 5 (g=0, n=5) word i=1 -> channel 21, tokens 0..7 -> codes (t+21)%4
+    codes2 = ((t[:, :1] + np.arange(32)[None]) % 4).astype(np.uint8)
+    b2 = C.pack_vblocks(codes2, 2)
+    off = (5 * 2 + 1) * 2
+    vals = [(k + 21) % 4 for k in range(8)]
+    assert b2[0, off] == vals[0] | vals[1] << 2 | vals[2] << 4 | vals[3] << 6
+    assert b2[0, off + 1] == vals[4] | vals[5] << 2 | vals[6] << 4 | vals[7] << 6
+    # round trip with a ragged tail
+    r = np.random.default_rng(3).integers(0, 4, size=(2, 45, 32)).astype(np.uint8)
+    assert np.array_equal(C.unpack_vblocks(C.pack_vblocks(r, 2), 2, 32, 45), r)
+    f = np.random.default_rng(4).standard_normal((45, 32)).astype(np.float16)
+    u = C.unpack_vblocks(C.pack_vblocks(f, 16), 16, 32, 45)
+    assert np.array_equal(u.view(np.float16), f)
+
+
+def test_window_holds_fp16_values():
+    """The residual window is fp16 (configs: 'fp16 residual window'): window
+    tokens dequantize to fp16-rounded inputs and quantized groups are formed
+    from the same staged values (reading: one staging rule for every token)."""
+    D, T = 16, 80
+    x = np.full((1, 1, T, D), 1.0 + 2.0 ** -12, dtype=np.float32)   # not an fp16 value
+    x[..., 0] = np.linspace(-3, 3, T, dtype=np.float32) + np.float32(2.0 ** -13)
+    cfg = C.Cfg(1, 1, 1, D, C.Spec(C.INT_ASYM, 4, C.PER_CHANNEL, 32), C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 0), R=32)
+    st = C.quantize_cache(cfg, x, x, T)
+    tq = st["Tq"]
+    assert tq == 32
+    assert np.array_equal(st["k_hat"][:, :, tq:], x[:, :, tq:].astype(np.float16).astype(np.float32))
+    assert np.array_equal(st["k_window"], x[:, :, tq:].astype(np.float16))
+    mn = x[0, 0, :32, 0].astype(np.float16).astype(np.float32).min()
+    assert st["k"]["zero"][0, 0, 0, 0] == mn

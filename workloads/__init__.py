@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the five workloads (shapes, seeds, value
+distributions only).
+
+This module holds none of the quantization or attention arithmetic: it draws
+Gaussian tensors, plants the outlier channels the pages describe, and rounds
+to the storage dtype of the workload (bf16 by round-to-nearest-even on the
+bit pattern).  Both the CPU oracle and the GPU path consume exactly the bytes
+produced here.
+
+Workload sources (page titles and sections):
+  * "FP8 KV Cache Quantization: Why Keys Break Before Values", section
+    "Why does the K cache break before the V cache?" (synthetic head d=128,
+    4096 tokens, channels 7, 23, 88 scaled by 20).
+  * "KV Cache Quantization: Why Keys and Values Need Different Axes",
+    section "Why does per-token key quantization destroy accuracy?"
+    (T=512, channels 3, 17, 44, 91 scaled by 60).
+  * The three serving-shaped workloads (FP8 GQA batch 16 at 8K context,
+    Llama-3.1-70B-shaped INT4 at 128K, KIVI-style INT2 at 32K) use the
+    head counts and context lengths the pages discuss for Llama-3.x-70B/8B.
+
+Large workloads are drawn chunk by chunk with a counter-style seed
+``default_rng((seed, tensor_id, b, h))`` so any (sequence, kv-head) chunk can
+be regenerated on its own for sampled parity checks.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# tensor ids for the per-chunk seeds
+_TID_K, _TID_V, _TID_Q, _TID_KNEW, _TID_VNEW, _TID_OUTLIER = 1, 2, 3, 4, 5, 6
+
+# ----------------------------------------------------------------------------
+# dtype helpers (bit-pattern conversions of generated inputs)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    r = (b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Workload table.  'k'/'v' give the cache spec of each side; 'schemes' lists
+# the variants a workload compares.  Dtype names: f32, bf16.
+# ----------------------------------------------------------------------------
+
+WORKLOADS = {
+    # single head, symmetric absmax INT8, four K/V scheme variants
+    "c1_int8_sym_single_head": dict(
+        B=1, Hq=1, Hkv=1, D=128, T=4096, dtype="f32", seed=0,
+        outliers=[7, 23, 88], outlier_scale=20.0,
+    ),
+    # single head, 4-bit asymmetric min-max, K per-token vs per-channel
+    "c2_int4_asym_single_head": dict(
+        B=1, Hq=1, Hkv=1, D=128, T=512, dtype="f32", seed=0,
+        outliers=[3, 17, 44, 91], outlier_scale=60.0,
+    ),
+    # FP8 E4M3 with calibrated per-head scales, GQA 32/8, 8K context
+    "c3_fp8_e4m3_gqa_8k": dict(
+        B=16, Hq=32, Hkv=8, D=128, T=8192, n_new=1, dtype="bf16", seed=3,
+        n_outliers=4, outlier_scale=30.0,
+    ),
+    # Llama-3.1-70B shaped layer: INT4 K per-channel G128 + INT4 V per-token, R=128
+    "c4_int4_llama70b_128k": dict(
+        B=1, Hq=64, Hkv=8, D=128, T=131072, n_new=0, dtype="bf16", seed=4,
+        n_outliers=6, outlier_scale=50.0,
+    ),
+    # KIVI-style INT2, pre-RoPE K, R=32, GQA 32/8, 32K context, decode + append
+    "c5_int2_kivi_prerope_32k": dict(
+        B=32, Hq=32, Hkv=8, D=128, T=32768, n_new=1, dtype="bf16", seed=5,
+        outliers=[7, 23, 88], outlier_scale=20.0, rope_base=10000.0,
+    ),
+}
+
+
+def single_head_inputs(name: str):
+    """Inputs of the two single-head workloads, drawn in the pages' order.
+
+    Returns float32 arrays K [T, D], V [T, D], q [D] and, for the T=512
+    workload, the 8 extra queries q8 [8, D] used for the logit comparison.
+    The first workload reproduces the printed INT8 table of the FP8 KV cache
+    page when drawn with numpy's default_rng(0) in this order.
+    """
+    w = WORKLOADS[name]
+    rng = np.random.default_rng(w["seed"])
+    T, D = w["T"], w["D"]
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    q = rng.standard_normal(D)
+    extra = rng.standard_normal((8, D)) if name.startswith("c2") else None
+    K[:, w["outliers"]] *= w["outlier_scale"]
+    out = dict(K=K.astype(np.float32), V=V.astype(np.float32), q=q.astype(np.float32))
+    if extra is not None:
+        out["q8"] = extra.astype(np.float32)
+    return out
+
+
+def outlier_channels(name: str) -> np.ndarray:
+    """[Hkv, n] outlier channel indices, fixed per kv head for the whole run."""
+    w = WORKLOADS[name]
+    if "outliers" in w:
+        return np.tile(np.asarray(w["outliers"], dtype=np.int64), (w["Hkv"], 1))
+    rng = np.random.default_rng((w["seed"], _TID_OUTLIER))
+    return np.stack([rng.choice(w["D"], size=w["n_outliers"], replace=False)
+                     for _ in range(w["Hkv"])]).astype(np.int64)
+
+
+def _chunk(seed, tid, b, h, shape):
+    return np.random.default_rng((seed, tid, b, h)).standard_normal(shape, dtype=np.float32)
+
+
+def kv_chunk(name: str, b: int, h: int, which: str, t_begin: int = 0, n: int | None = None):
+    """bf16 bits [n, D] of the prefill K or V chunk of (sequence b, kv head h).
+
+    Keys carry the fixed outlier channels of head h.  The full chunk is drawn
+    (so sub-ranges stay consistent) and then sliced.
+    """
+    w = WORKLOADS[name]
+    T, D = w["T"], w["D"]
+    x = _chunk(w["seed"], _TID_K if which == "k" else _TID_V, b, h, (T, D))
+    if which == "k":
+        x[:, outlier_channels(name)[h]] *= np.float32(w["outlier_scale"])
+    n = T - t_begin if n is None else n
+    return f32_to_bf16_bits(x[t_begin:t_begin + n])
+
+
+def new_token_chunk(name: str, b: int, h: int, which: str):
+    """bf16 bits [n_new, D] of the decode-time appended token(s) of (b, h)."""
+    w = WORKLOADS[name]
+    x = _chunk(w["seed"], _TID_KNEW if which == "k" else _TID_VNEW, b, h, (w["n_new"], w["D"]))
+    if which == "k":
+        x[:, outlier_channels(name)[h]] *= np.float32(w["outlier_scale"])
+    return f32_to_bf16_bits(x)
+
+
+def query(name: str) -> np.ndarray:
+    """bf16 bits [B, Hq, D] of the decode query (already rotated when keys are pre-RoPE)."""
+    w = WORKLOADS[name]
+    x = np.random.default_rng((w["seed"], _TID_Q)).standard_normal((w["B"], w["Hq"], w["D"]),
+                                                                   dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def full_prefill(name: str, which: str) -> np.ndarray:
+    """bf16 bits [B, Hkv, T, D] of the whole prefill K or V (large: 2 bytes/element)."""
+    w = WORKLOADS[name]
+    out = np.empty((w["B"], w["Hkv"], w["T"], w["D"]), dtype=np.uint16)
+    for b in range(w["B"]):
+        for h in range(w["Hkv"]):
+            out[b, h] = kv_chunk(name, b, h, which)
+    return out
+
+
+def full_new_tokens(name: str, which: str) -> np.ndarray:
+    w = WORKLOADS[name]
+    out = np.empty((w["B"], w["Hkv"], w["n_new"], w["D"]), dtype=np.uint16)
+    for b in range(w["B"]):
+        for h in range(w["Hkv"]):
+            out[b, h] = new_token_chunk(name, b, h, which)
+    return out
+
+
+def random_case(seed: int, B: int, Hkv: int, T: int, D: int, n_outliers: int = 3,
+                outlier_scale: float = 20.0, dtype: str = "f32"):
+    """Small random K, V [B, Hkv, T, D] with fixed outlier channels, for parity sweeps.
+
+    Returns (K, V) as float32 arrays whose values are exactly representable in
+    ``dtype`` (f32, bf16 or f16), plus the raw device-dtype payloads.
+    """
+    rng = np.random.default_rng((seed, 77))
+    K = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    V = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    for h in range(Hkv):
+        ch = rng.choice(D, size=min(n_outliers, D), replace=False)
+        K[:, h][..., ch] *= np.float32(outlier_scale)
+    return _as_dtype(K, dtype), _as_dtype(V, dtype)
+
+
+def random_queries(seed: int, B: int, Hq: int, D: int, dtype: str = "f32"):
+    rng = np.random.default_rng((seed, 78))
+    return _as_dtype(rng.standard_normal((B, Hq, D), dtype=np.float32), dtype)
+
+
+def _as_dtype(x: np.ndarray, dtype: str):
+    """Return (float32 values, raw payload array in the device dtype)."""
+    if dtype == "f32":
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        return x, x
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return bf16_bits_to_f32(bits), bits
+    if dtype == "f16":
+        h = x.astype(np.float16)
+        return h.astype(np.float32), h
+    raise ValueError(dtype)
