@@ -249,6 +249,8 @@ def pack_vblocks(codes: np.ndarray, bits: int) -> np.ndarray:
     u = _code_bytes_le(codes, bits)
     *lead, T, D = u.shape
     nblk = -(-T // VBLOCK)
+    if nblk == 0:
+        return np.zeros((*lead, 0, VBLOCK * D * bits // 8), dtype=np.uint8)
     pad = nblk * VBLOCK - T
     if pad:
         u = np.concatenate([u, np.zeros((*lead, pad, D), dtype=u.dtype)], axis=-2)

@@ -1,0 +1,192 @@
+"""ctypes binding of libkvq.so (include/kvq.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels.  Torch tensors are used
+for device memory and streams: the wrappers pass ``data_ptr()`` and the
+current HIP stream.  Importing this module fails loudly when the library has
+not been built (``python -m quantized_decode_attention_05_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+# torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading it first
+# makes libkvq.so bind to that same runtime instead of a second copy from
+# /opt/rocm, which would fail to see the device once torch has opened it.
+import torch  # noqa: F401  (device memory and streams)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      f"`python -m quantized_decode_attention_05_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+# ---- constants (mirror include/kvq.h) ------------------------------------------
+KVQ_OK = 0
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_CAPACITY",
+          -4: "KVQ_ERR_ALIGN", -5: "KVQ_ERR_NULL", -6: "KVQ_ERR_WORKSPACE", -7: "KVQ_ERR_HIP"}
+NONE, INT_ASYM, INT_SYM, FP8_E4M3 = 0, 1, 2, 3
+PER_TENSOR, PER_CHANNEL, PER_TOKEN = 0, 1, 2
+F32, F16, BF16 = 0, 1, 2
+CALIBRATE = 1
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA = 0, 1, 2
+
+
+class TensorSpec(C.Structure):
+    _fields_ = [("scheme", C.c_int32), ("bits", C.c_int32), ("axis", C.c_int32), ("group", C.c_int32)]
+
+
+class Config(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("max_tokens", C.c_int64), ("in_dtype", C.c_int32),
+                ("out_dtype", C.c_int32), ("k", TensorSpec), ("v", TensorSpec),
+                ("residual", C.c_int32), ("pre_rope_k", C.c_int32), ("rope_base", C.c_float),
+                ("reserved", C.c_int32)]
+
+
+class Layout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
+                                          "v_zero", "ring_k", "ring_v", "rope", "fp8_calib",
+                                          "total_bytes")] + \
+               [("token_capacity", C.c_int64), ("k_row_bytes", C.c_int32), ("v_block_bytes", C.c_int32),
+                ("ring_slots", C.c_int32), ("token_group", C.c_int32), ("k_meta_cols", C.c_int32),
+                ("v_meta_cols", C.c_int32)]
+
+
+class AttnOptions(C.Structure):
+    _fields_ = [("kernel", C.c_int32), ("num_splits", C.c_int32), ("reserved", C.c_int32 * 6)]
+
+
+_P = C.c_void_p
+_CFG = C.POINTER(Config)
+_sig = {
+    "kvq_validate_config": (C.c_int, [_CFG]),
+    "kvq_arena_layout": (C.c_int, [_CFG, C.POINTER(Layout)]),
+    "kvq_arena_bytes": (C.c_int, [_CFG, C.POINTER(C.c_size_t)]),
+    "kvq_quantized_tokens": (C.c_int64, [_CFG, C.c_int64]),
+    "kvq_quantize_append": (C.c_int, [_CFG, _P, C.c_int64, C.c_int32, _P, _P, _P, _P, C.c_uint32, _P]),
+    "kvq_workspace_bytes": (C.c_int, [_CFG, C.c_int64, C.POINTER(AttnOptions), C.POINTER(C.c_size_t)]),
+    "kvq_decode_attention": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, C.c_float, _P, C.c_size_t,
+                                       C.POINTER(AttnOptions), _P]),
+    "kvq_dequantize": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P]),
+    "kvq_status_string": (C.c_char_p, [C.c_int]),
+    "kvq_abi_version": (C.c_int, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_sig)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({_lib.kvq_status_string(status).decode()})")
+
+
+def _check(st: int, where: str) -> int:
+    if st != KVQ_OK:
+        raise KvqError(st, where)
+    return st
+
+
+def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, k, v,
+                in_dtype=BF16, out_dtype=F32, residual=0, pre_rope_k=False,
+                rope_base=10000.0) -> Config:
+    """k, v: (scheme, bits, axis, group) tuples."""
+    return Config(batch, num_q_heads, num_kv_heads, head_dim, max_tokens, in_dtype, out_dtype,
+                  TensorSpec(*k), TensorSpec(*v), residual, int(bool(pre_rope_k)), rope_base, 0)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return C.c_void_p(stream)
+    import torch
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return C.c_void_p(0)
+
+
+def _opts(kernel=0, num_splits=0):
+    o = AttnOptions()
+    o.kernel, o.num_splits = kernel, num_splits
+    return o
+
+
+def kvq_abi_version() -> int:
+    return _lib.kvq_abi_version()
+
+
+def kvq_status_string(status: int) -> str:
+    return _lib.kvq_status_string(status).decode()
+
+
+def kvq_validate_config(cfg: Config) -> int:
+    return _lib.kvq_validate_config(C.byref(cfg))
+
+
+def kvq_arena_layout(cfg: Config) -> Layout:
+    lay = Layout()
+    _check(_lib.kvq_arena_layout(C.byref(cfg), C.byref(lay)), "kvq_arena_layout")
+    return lay
+
+
+def kvq_arena_bytes(cfg: Config) -> int:
+    n = C.c_size_t()
+    _check(_lib.kvq_arena_bytes(C.byref(cfg), C.byref(n)), "kvq_arena_bytes")
+    return n.value
+
+
+def kvq_quantized_tokens(cfg: Config, T: int) -> int:
+    r = _lib.kvq_quantized_tokens(C.byref(cfg), T)
+    if r < 0:
+        raise KvqError(int(r), "kvq_quantized_tokens")
+    return int(r)
+
+
+def kvq_workspace_bytes(cfg: Config, T: int, kernel: int = 0, num_splits: int = 0) -> int:
+    n = C.c_size_t()
+    o = _opts(kernel, num_splits)
+    _check(_lib.kvq_workspace_bytes(C.byref(cfg), T, C.byref(o), C.byref(n)), "kvq_workspace_bytes")
+    return n.value
+
+
+def kvq_quantize_append(cfg: Config, arena, t0: int, k_new, v_new, k_scale=None, v_scale=None,
+                        flags: int = 0, stream=None) -> None:
+    """k_new, v_new: device tensors [B, Hkv, n_new, D] in cfg.in_dtype."""
+    n_new = int(k_new.shape[2])
+    st = _lib.kvq_quantize_append(C.byref(cfg), _ptr(arena), t0, n_new, _ptr(k_new), _ptr(v_new),
+                                  _ptr(k_scale), _ptr(v_scale), flags,
+                                  _stream(stream, arena, k_new))
+    _check(st, "kvq_quantize_append")
+
+
+def kvq_decode_attention(cfg: Config, arena, T: int, q, out, sm_scale: float, workspace,
+                         kernel: int = 0, num_splits: int = 0, stream=None) -> None:
+    """q: [B, Hq, D] in cfg.in_dtype; out: [B, Hq, D] in cfg.out_dtype."""
+    o = _opts(kernel, num_splits)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.kvq_decode_attention(C.byref(cfg), _ptr(arena), T, _ptr(q), _ptr(out), sm_scale,
+                                   _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
+    _check(st, "kvq_decode_attention")
+
+
+def kvq_dequantize(cfg: Config, arena, T: int, k_out=None, v_out=None, stream=None) -> None:
+    """k_out, v_out: fp32 device tensors [B, Hkv, T, D] (either may be None)."""
+    st = _lib.kvq_dequantize(C.byref(cfg), _ptr(arena), T, _ptr(k_out), _ptr(v_out),
+                             _stream(stream, arena))
+    _check(st, "kvq_dequantize")
+
+
+# raw entry points for tests that pass pointers directly
+raw = _lib

@@ -1,0 +1,245 @@
+// Split-K decode attention over the quantized cache: pass 1 (per token split)
+// and pass 2 (merge of the splits).
+//
+// Per query head h (kv head h / n_rep), over tokens j of one split:
+//   logit_j = (q . k_hat_j) * sm_scale      [k_hat rotated by RoPE at position j
+//                                             when keys are cached pre-RoPE]
+//   running max m, running sum l = sum exp(logit - m), o = sum exp(logit - m) v_hat_j
+// ("FP8 KV Cache Quantization: Why Keys Break Before Values", section "Why does
+// the K cache break before the V cache?").  Logits are kept in log2 units
+// (pre-multiplied by log2 e) so the exponentials are exp2.  Pass 2 combines
+// splits with M = max m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+//
+// This file holds the generic kernel: it dequantizes 64-token tiles of any
+// supported format into LDS (fp32) and does the dot products on the vector
+// ALUs.  The MFMA kernel for the hot formats lives in kvq_attn_mfma.hip.
+#include "kvq_internal.h"
+#include "kvq_launch.h"
+#include "kvq_device.h"
+
+namespace kvq {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;     // logit of masked / absent tokens
+constexpr int kTile = 64;
+
+struct AttnArgs {
+  const uint8_t* arena;
+  const void* q;
+  float* ws_o;
+  float* ws_ml;
+  int64_t T, Tq, chunk;
+  int32_t S;
+  float qscale;            // sm_scale * log2(e)
+};
+
+// cos/sin of position * theta_i from the two-level table (fine: pos mod 32,
+// coarse: 32 * floor(pos / 32)), combined with the angle-addition formula.
+__device__ __forceinline__ float2 rope_cs(const Plan& p, const float2* tab, int64_t pos, int pair) {
+  const int half = p.D >> 1;
+  const float2 f = tab[(pos & 31) * half + pair];
+  const float2 c = tab[(kVBlock + (pos >> 5)) * half + pair];
+  return make_float2(c.x * f.x - c.y * f.y, c.y * f.x + c.x * f.y);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
+  __shared__ float q_s[16][D];
+  __shared__ float kv_s[kTile][D + 1];
+  __shared__ float p_s[16][kTile];
+  __shared__ float m_s[16], l_s[16], alpha_s[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int n_rep = p.n_rep;
+  const int64_t t_begin = (int64_t)split * a.chunk;
+  int64_t t_end = t_begin + a.chunk;
+  if (t_end > a.T) t_end = a.T;
+
+  for (int e = tid; e < n_rep * D; e += 256) {
+    const int r = e / D, c = e % D;
+    const int64_t qi = ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c;
+    q_s[r][c] = load_in(a.q, qi, p.in_dtype) * a.qscale;
+  }
+  if (tid < 16) { m_s[tid] = kNegBig; l_s[tid] = 0.0f; }
+
+  constexpr int kOut = 16 * D / 256;       // (head, channel) outputs per thread, max
+  float o_acc[kOut];
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) o_acc[j] = 0.0f;
+  const float2* rtab = p.pre_rope ? (const float2*)(a.arena + p.rope) : nullptr;
+  __syncthreads();
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTile) {
+    // 1. keys of the tile -> LDS (dequantized, rotated)
+    for (int e = tid; e < kTile * (D / 2); e += 256) {
+      const int tt = e / (D / 2), pr = e % (D / 2);
+      const int64_t t = t0 + tt;
+      float k0 = 0.0f, k1 = 0.0f;
+      if (t < t_end) {
+        k0 = dequant_elem<SIDE_K>(p, a.arena, b, kvh, t, 2 * pr, a.Tq);
+        k1 = dequant_elem<SIDE_K>(p, a.arena, b, kvh, t, 2 * pr + 1, a.Tq);
+        if (rtab) {
+          const float2 cs = rope_cs(p, rtab, t, pr);
+          const float r0 = k0 * cs.x - k1 * cs.y;
+          const float r1 = k0 * cs.y + k1 * cs.x;
+          k0 = r0; k1 = r1;
+        }
+      }
+      kv_s[tt][2 * pr] = k0;
+      kv_s[tt][2 * pr + 1] = k1;
+    }
+    __syncthreads();
+    // 2. logits
+    for (int e = tid; e < n_rep * kTile; e += 256) {
+      const int r = e / kTile, tt = e % kTile;
+      float acc = 0.0f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) acc += q_s[r][c] * kv_s[tt][c];
+      p_s[r][tt] = (t0 + tt < t_end) ? acc : kNegBig;
+    }
+    __syncthreads();
+    // 3. online softmax, one wave per head (heads strided over the 4 waves)
+    for (int r = wave; r < n_rep; r += 4) {
+      const float x = p_s[r][lane];
+      float mx = x;
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      const float m_old = m_s[r];
+      const float m_new = fmaxf(m_old, mx);
+      const float pv = (x <= kNegBig) ? 0.0f : exp2f(x - m_new);
+      float sum = pv;
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      p_s[r][lane] = pv;
+      if (lane == 0) {
+        const float alpha = exp2f(m_old - m_new);
+        alpha_s[r] = alpha;
+        l_s[r] = l_s[r] * alpha + sum;
+        m_s[r] = m_new;
+      }
+    }
+    // 4. values of the tile -> LDS (reuses the key buffer)
+    __syncthreads();
+    for (int e = tid; e < kTile * D; e += 256) {
+      const int tt = e / D, c = e % D;
+      const int64_t t = t0 + tt;
+      kv_s[tt][c] = (t < t_end) ? dequant_elem<SIDE_V>(p, a.arena, b, kvh, t, c, a.Tq) : 0.0f;
+    }
+    __syncthreads();
+    // 5. o = alpha * o + p . V
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int e = tid + 256 * j;
+      const int r = e / D, c = e % D;
+      if (r < n_rep) {
+        float acc = o_acc[j] * alpha_s[r];
+#pragma unroll 8
+        for (int tt = 0; tt < kTile; ++tt) acc += p_s[r][tt] * kv_s[tt][c];
+        o_acc[j] = acc;
+      }
+    }
+    __syncthreads();
+  }
+
+  // partials of this split
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) {
+    const int e = tid + 256 * j;
+    const int r = e / D, c = e % D;
+    if (r < n_rep) {
+      const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + r;
+      a.ws_o[(hq * a.S + split) * D + c] = o_acc[j];
+    }
+  }
+  if (tid < n_rep) {
+    const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + tid;
+    a.ws_ml[(hq * a.S + split) * 2 + 0] = m_s[tid];
+    a.ws_ml[(hq * a.S + split) * 2 + 1] = l_s[tid];
+  }
+}
+
+// Pass 2: one block per (query head, sequence), one thread per channel.
+__global__ void attn_merge(Plan p, const float* ws_o, const float* ws_ml, int S, void* out) {
+  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int64_t row = (int64_t)b * p.Hq + hq;
+  const float* ml = ws_ml + row * S * 2;
+  float M = kNegBig;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.0f, acc = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float w = exp2f(ml[2 * s] - M);
+    L += w * ml[2 * s + 1];
+    acc += w * ws_o[(row * S + s) * p.D + c];
+  }
+  const float v = acc / L;
+  const int64_t oi = row * p.D + c;
+  if (p.out_dtype == KVQ_F32) ((float*)out)[oi] = v;
+  else if (p.out_dtype == KVQ_F16) ((_Float16*)out)[oi] = (_Float16)v;
+  else {
+    const uint32_t u = __float_as_uint(v);
+    ((uint16_t*)out)[oi] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+
+// ---- planning and launch ----------------------------------------------------------
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPlan* ap) {
+  int kernel = 0, splits = 0;
+  if (opt) {
+    for (int i = 0; i < 6; ++i) if (opt->reserved[i]) return KVQ_ERR_INVALID_ARG;
+    kernel = opt->kernel;
+    splits = opt->num_splits;
+    if (kernel < 0 || kernel > 2 || splits < 0) return KVQ_ERR_INVALID_ARG;
+  }
+  if (kernel == 2 && !mfma_supported(p)) return KVQ_ERR_UNSUPPORTED;
+  if (kernel == 0) kernel = mfma_supported(p) ? 2 : 1;
+  const int64_t unit = 64;
+  const int64_t max_splits = cdiv(T, unit);
+  if (splits == 0) {
+    // enough work-groups to cover the 256 CUs a few times over
+    const int64_t bh = (int64_t)p.B * p.Hkv;
+    int64_t want = cdiv(1024, bh);
+    const int64_t min_tokens = (kernel == 2) ? 256 : 128;
+    const int64_t by_len = cdiv(T, min_tokens);
+    splits = (int)(want < by_len ? want : by_len);
+  }
+  if (splits > max_splits) splits = (int)max_splits;
+  if (splits < 1) splits = 1;
+  int64_t chunk = cdiv(cdiv(T, splits), unit) * unit;
+  splits = (int)cdiv(T, chunk);
+  ap->kernel = kernel;
+  ap->splits = splits;
+  ap->chunk = chunk;
+  ap->T = T;
+  ap->Tq = quantized_tokens(p, T);
+  const uint64_t rows = (uint64_t)p.B * p.Hq * splits;
+  ap->ws_o = 0;
+  ap->ws_ml = (rows * p.D * 4 + 255) & ~(uint64_t)255;
+  ap->workspace_bytes = ap->ws_ml + ((rows * 2 * 4 + 255) & ~(uint64_t)255);
+  return KVQ_OK;
+}
+
+hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
+                                 float sm_scale, void* ws, hipStream_t s);
+
+hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
+                            void* out, float sm_scale, void* ws, hipStream_t s) {
+  float* ws_o = (float*)((uint8_t*)ws + ap.ws_o);
+  float* ws_ml = (float*)((uint8_t*)ws + ap.ws_ml);
+  if (ap.kernel == 2) {
+    hipError_t e = launch_attention_mfma(p, ap, arena, q, sm_scale, ws, s);
+    if (e != hipSuccess) return e;
+  } else {
+    AttnArgs a{(const uint8_t*)arena, q, ws_o, ws_ml, ap.T, ap.Tq, ap.chunk, ap.splits,
+               sm_scale * kLog2e};
+    dim3 grid(ap.splits, p.Hkv, p.B);
+    if (p.D == 128) hipLaunchKernelGGL(attn_generic<128>, grid, dim3(256), 0, s, p, a);
+    else hipLaunchKernelGGL(attn_generic<64>, grid, dim3(256), 0, s, p, a);
+  }
+  hipLaunchKernelGGL(attn_merge, dim3(p.Hq, p.B), dim3(p.D), 0, s, p, (const float*)ws_o,
+                     (const float*)ws_ml, ap.splits, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

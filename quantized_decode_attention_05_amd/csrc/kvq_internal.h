@@ -1,0 +1,89 @@
+// Internal plan of a cache config: resolved groups, section offsets and the
+// residual split, computed once on the host and passed to kernels by value.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kVBlock = 32;      // tokens per V code block
+constexpr int kRingAlign = 32;   // ring slots are a multiple of this
+constexpr float kE4M3Max = 448.0f;
+
+// One side (K or V) of the cache.
+struct SideFmt {
+  int32_t scheme;     // enum kvq_scheme
+  int32_t bits;       // code bits (2, 4, 8, 16, 32)
+  int32_t axis;       // enum kvq_axis (INT schemes)
+  int32_t group;      // resolved: PER_CHANNEL tokens per group (0 = whole axis), PER_TOKEN channels
+  int32_t meta_cols;  // innermost extent of scale/zero
+  int32_t pad_;
+  int64_t meta_rows;  // rows of scale/zero per (b, h)
+  uint64_t codes, scale, zero;  // byte offsets in the arena (UINT64_MAX = absent)
+};
+
+struct Plan {
+  int32_t B, Hq, Hkv, D, n_rep;
+  int32_t in_dtype, out_dtype;
+  int32_t R, Gt, Rs;      // residual, token group, ring slots
+  int32_t window;         // every token staged through fp16
+  int32_t one_shot;       // whole-axis / per-tensor groups
+  int32_t pre_rope;
+  float rope_base;
+  int64_t Tc;             // token capacity (rounded)
+  int64_t max_tokens;
+  int32_t k_row_bytes, v_block_bytes;
+  int64_t v_nblk;         // V code blocks per (b, h)
+  SideFmt k, v;
+  uint64_t ring_k, ring_v, rope, fp8_calib, total;
+  int64_t rope_rows;      // coarse rope rows (Tc/32 + 1)
+};
+
+// Builds the plan; returns KVQ_OK or an error status.
+int make_plan(const kvq_config* cfg, Plan* p);
+
+inline int64_t quantized_tokens(const Plan& p, int64_t T) {
+  if (p.one_shot) return T;
+  int64_t r = T - p.R;
+  if (r < 0) r = 0;
+  return (int64_t)p.Gt * (r / p.Gt);
+}
+
+// ---- device helpers shared by the kernels ----------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float load_in(const void* p, int64_t i, int dtype) {
+  if (dtype == KVQ_F32) return ((const float*)p)[i];
+  if (dtype == KVQ_F16) return (float)((const _Float16*)p)[i];
+  return bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+// fp32 -> fp16 (round to nearest even) -> fp32
+__device__ __forceinline__ float stage_f16(float x) { return (float)(_Float16)x; }
+
+// Value of an E4M3FN code byte (finite codes; NaN codes never produced).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  float mag = (e == 0) ? (float)m * 0.001953125f                      // m * 2^-9
+                       : __uint_as_float(((e + 120u) << 23) | (m << 20)); // (1+m/8) 2^(e-7)
+  return (c & 0x80) ? -mag : mag;
+}
+
+// V block layout: byte offset of the word holding (t, c), and bit offset of
+// code k inside that word.  Word = 8 codes of `bits` bits.
+__device__ __forceinline__ int64_t vblock_word_byte(int64_t t, int c, int D, int bits,
+                                                    int block_bytes) {
+  int64_t blk = t >> 5;
+  int tau = (int)(t & 31);
+  int g = tau >> 3, n = c & 15, i = c >> 4;
+  int lane = 16 * g + n;
+  int64_t word = (int64_t)lane * (D >> 4) + i;
+  return blk * block_bytes + word * bits;   // a word is 8*bits bits = bits bytes
+}
+
+}  // namespace kvq

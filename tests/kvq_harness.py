@@ -1,0 +1,215 @@
+"""Parity harness: run the HIP library through the C ABI and compare it with
+the CPU oracle on the same seeded inputs.
+
+Comparisons (the bar):
+  * integer / byte results bit-exact: K code rows, V code blocks (unpacked with
+    the oracle's own unpacker), scales and zero-points, FP8 scales, fp16 window
+    slots, and the dequantized fp32 values;
+  * decode attention within a max (over sequence x query head) relative L2 of
+    2e-3 against the oracle's fp64 attention on the oracle's dequantized cache.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import quantized_decode_attention_05_amd as K
+from oracle import attention as OA
+from oracle import cache as OC
+
+ATTN_TOL = 2e-3
+_DT = {"f32": (K.F32, torch.float32), "f16": (K.F16, torch.float16), "bf16": (K.BF16, torch.bfloat16)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Case:
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    k: tuple
+    v: tuple
+    R: int = 0
+    pre_rope: bool = False
+    rope_base: float = 10000.0
+    dtype: str = "f32"
+    cap: int = 0
+
+    def lib_cfg(self, cap):
+        return K.make_config(batch=self.B, num_q_heads=self.Hq, num_kv_heads=self.Hkv, head_dim=self.D,
+                             max_tokens=cap, k=self.k, v=self.v, in_dtype=_DT[self.dtype][0],
+                             out_dtype=K.F32, residual=self.R, pre_rope_k=self.pre_rope,
+                             rope_base=self.rope_base)
+
+    def oracle_cfg(self, B=None, Hq=None, Hkv=None):
+        return OC.Cfg(B or self.B, Hq or self.Hq, Hkv or self.Hkv, self.D, OC.Spec(*self.k),
+                      OC.Spec(*self.v), self.R, self.pre_rope, self.rope_base)
+
+
+def to_dev(payload: np.ndarray, dtype: str) -> torch.Tensor:
+    """Upload a device-dtype payload (f32 values, f16 values or bf16 bits)."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(payload).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(payload)).cuda()
+
+
+class GpuCache:
+    """A cache arena on cuda:0 driven through the C ABI."""
+
+    def __init__(self, case: Case, cap: int, fill: int = 0x5A):
+        self.case = case
+        self.cfg = case.lib_cfg(cap)
+        self.layout = K.kvq_arena_layout(self.cfg)
+        self.arena = torch.full((self.layout.total_bytes,), fill, dtype=torch.uint8, device="cuda")
+        self.T = 0
+
+    def append(self, k_payload, v_payload, flags=0, k_scale=None, v_scale=None):
+        kd, vd = to_dev(k_payload, self.case.dtype), to_dev(v_payload, self.case.dtype)
+        ks = None if k_scale is None else torch.as_tensor(k_scale, dtype=torch.float32).cuda()
+        vs = None if v_scale is None else torch.as_tensor(v_scale, dtype=torch.float32).cuda()
+        K.kvq_quantize_append(self.cfg, self.arena, self.T, kd, vd, ks, vs, flags)
+        self.T += int(kd.shape[2])
+
+    def attention(self, q_payload, sm_scale=None, kernel=0, num_splits=0, T=None):
+        T = self.T if T is None else T
+        c = self.case
+        q = to_dev(q_payload, c.dtype)
+        out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(K.kvq_workspace_bytes(self.cfg, T, kernel, num_splits), dtype=torch.uint8,
+                         device="cuda")
+        sm = 1.0 / math.sqrt(c.D) if sm_scale is None else sm_scale
+        K.kvq_decode_attention(self.cfg, self.arena, T, q, out, sm, ws, kernel, num_splits)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def dequantize(self, T=None, bh_sel=None):
+        T = self.T if T is None else T
+        c = self.case
+        ko = torch.empty((c.B, c.Hkv, T, c.D), dtype=torch.float32, device="cuda")
+        vo = torch.empty_like(ko)
+        K.kvq_dequantize(self.cfg, self.arena, T, ko, vo)
+        torch.cuda.synchronize()
+        if bh_sel is not None:
+            b, h = bh_sel
+            ko, vo = ko[b:b + 1, h:h + 1], vo[b:b + 1, h:h + 1]
+        out = ko.cpu().numpy(), vo.cpu().numpy()
+        del ko, vo
+        return out
+
+    def section(self, name, nbytes, offset=0):
+        off = getattr(self.layout, name)
+        return self.arena[off + offset: off + offset + nbytes].cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# section comparisons
+# ---------------------------------------------------------------------------
+
+def _meta_shape(spec, B, H, D, Tc, Tq):
+    scheme, bits, axis, group = spec
+    if scheme == OC.FP8_E4M3:
+        return None
+    if axis == OC.PER_TENSOR:
+        return (B, H, 1, 1), (B, H, 1, 1)
+    if axis == OC.PER_CHANNEL:
+        rows = Tc // group if group else 1
+        used = Tq // group if group else 1
+        return (B, H, rows, D), (B, H, used, D)
+    gc = group or D
+    return (B, H, Tc, D // gc), (B, H, Tq, D // gc)
+
+
+def compare_sections(gc: GpuCache, st: dict, bh_sel=None):
+    """Bit-exact comparison of the arena with oracle state ``st``.  With bh_sel =
+    (b, h) the oracle state covers that single (sequence, kv head) and only its
+    slices are copied off the device."""
+    c, lay = gc.case, gc.layout
+    B, H, D, Tc = c.B, c.Hkv, c.D, lay.token_capacity
+    Tq, T = st["Tq"], st["T"]
+    arena = gc.arena
+
+    def sl(off, per_bh, dtype):
+        """[B', H', *per_bh] view of a [B][H][*per_bh] section (B' = H' = 1 with bh_sel)."""
+        n = int(np.prod(per_bh)) * np.dtype(dtype).itemsize
+        if bh_sel is None:
+            raw = arena[off: off + n * B * H]
+            return raw.cpu().numpy().view(dtype).reshape((B, H) + tuple(per_bh))
+        b, h = bh_sel
+        o = off + (b * H + h) * n
+        return arena[o: o + n].cpu().numpy().view(dtype).reshape((1, 1) + tuple(per_bh))
+
+    bits_k = OC.code_bits(OC.Spec(*c.k))
+    rows = sl(lay.k_codes, (Tc, lay.k_row_bytes), np.uint8)[:, :, :Tq]
+    exp_rows = OC.pack_rows(st["k"]["codes"], bits_k)
+    assert np.array_equal(rows, exp_rows), "K code rows differ"
+
+    bits_v = OC.code_bits(OC.Spec(*c.v))
+    vb = sl(lay.v_codes, (Tc // 32, lay.v_block_bytes), np.uint8)
+    got_v = OC.unpack_vblocks(vb, bits_v, D, Tq)
+    exp_v = OC.unpack_vblocks(OC.pack_vblocks(st["v"]["codes"], bits_v), bits_v, D, Tq)
+    assert np.array_equal(got_v, exp_v), "V code blocks differ"
+
+    for side, spec in (("k", c.k), ("v", c.v)):
+        part = st[side]
+        if spec[0] == OC.FP8_E4M3:
+            off = getattr(lay, side + "_scale")
+            s = arena[off: off + 4 * H].cpu().numpy().view(np.float32)
+            if bh_sel is not None:
+                s = s[bh_sel[1]:bh_sel[1] + 1]
+            exp = np.asarray(part["scale"], np.float32)
+            assert np.array_equal(s.view(np.uint32), exp.view(np.uint32)), \
+                f"{side} fp8 scale differs: {s} vs {exp}"
+            continue
+        if spec[0] == OC.NONE:
+            continue
+        full, used = _meta_shape(spec, B, H, D, Tc, Tq)
+        idx = (slice(None), slice(None)) + tuple(slice(0, u) for u in used[2:])
+        sc = sl(getattr(lay, side + "_scale"), full[2:], np.float32)[idx]
+        assert np.array_equal(sc.view(np.uint32), part["scale"].reshape(sc.shape).view(np.uint32)), \
+            f"{side} scales differ"
+        if spec[0] == OC.INT_ASYM:
+            zz = sl(getattr(lay, side + "_zero"), full[2:], np.float32)[idx]
+            assert np.array_equal(zz, part["zero"].reshape(zz.shape)), f"{side} zero-points differ"
+
+    if T > Tq:
+        Rs = lay.ring_slots
+        slots = OC.window_slots(c.oracle_cfg(), Tq, T)
+        rk = sl(lay.ring_k, (Rs, D), np.float16)[:, :, slots]
+        assert np.array_equal(rk.view(np.uint16), st["k_window"].view(np.uint16)), "ring K differs"
+        rvb = sl(lay.ring_v, (Rs // 32, 32 * D * 2), np.uint8)
+        rv = OC.unpack_vblocks(rvb, 16, D, Rs)[:, :, slots]
+        assert np.array_equal(rv.view(np.uint16), st["v_window"].view(np.uint16)), "ring V differs"
+
+
+def compare_dequant(gc: GpuCache, st: dict, bh_sel=None):
+    kd, vd = gc.dequantize(st["T"], bh_sel)
+    assert np.array_equal(kd, st["k_hat"]), "dequantized K differs"
+    assert np.array_equal(vd, st["v_hat"]), "dequantized V differs"
+
+
+def attention_error(out_gpu: np.ndarray, q_f32: np.ndarray, st: dict, case: Case, heads=None,
+                    sm_scale=None) -> float:
+    sm = 1.0 / math.sqrt(case.D) if sm_scale is None else sm_scale
+    ref = OA.decode_attention(q_f32, st["k_hat"], st["v_hat"], sm,
+                              pre_rope_base=case.rope_base if case.pre_rope else None, heads=heads)
+    return OA.max_rel_l2_per_head(out_gpu, ref, heads)
+
+
+def payload_of(values_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """Device payload whose value is exactly values_f32 (which must be representable)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(values_f32, dtype=np.float32)
+    if dtype == "f16":
+        return values_f32.astype(np.float16)
+    u = np.ascontiguousarray(values_f32, dtype=np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)

@@ -1,0 +1,186 @@
+"""C-ABI checks that need no GPU: symbols, validation, layout, byte accounting.
+
+Every call here either fails validation (which runs on the host before any HIP
+call) or is a host-only query, so nothing is launched.
+"""
+import ctypes as C
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_decode_attention_05_amd as K
+from quantized_decode_attention_05_amd import _lib
+from oracle import cache as OC
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _cfg(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=1024,
+                k=(K.INT_ASYM, 4, K.PER_CHANNEL, 32), v=(K.INT_ASYM, 4, K.PER_TOKEN, 32),
+                residual=32)
+    base.update(kw)
+    return K.make_config(**base)
+
+
+def test_header_symbols_exported():
+    text = open(HDR).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kvq_\w+)\s*\(", text, re.M))
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(_lib.raw, name), name
+    assert set(K.EXPORTED) == declared
+
+
+def test_struct_sizes_match_c_layout():
+    assert C.sizeof(K.Config) == 80
+    assert C.sizeof(K.TensorSpec) == 16
+    assert C.sizeof(K.AttnOptions) == 32
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert K.kvq_status_string(s) != "unknown status"
+    assert K.kvq_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=96), dict(num_q_heads=7), dict(num_kv_heads=0), dict(num_q_heads=64, num_kv_heads=2),
+    dict(k=(K.INT_ASYM, 3, K.PER_CHANNEL, 32)), dict(k=(K.INT_SYM, 4, K.PER_CHANNEL, 0)),
+    dict(v=(K.INT_ASYM, 4, K.PER_TOKEN, 24)), dict(v=(K.INT_ASYM, 4, K.PER_TOKEN, 4)),
+    dict(k=(K.NONE, 8, 0, 0)), dict(k=(K.FP8_E4M3, 4, 0, 0)), dict(k=(7, 8, 0, 0)),
+    dict(residual=48),                                     # R % G != 0
+    dict(residual=-1), dict(max_tokens=0), dict(in_dtype=5),
+    dict(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 0), residual=0),  # whole axis with a per-channel V group? no: with G V token
+    dict(k=(K.INT_ASYM, 4, K.PER_TENSOR, 0), residual=32),
+    dict(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 32), v=(K.INT_ASYM, 4, K.PER_CHANNEL, 64)),
+    dict(pre_rope_k=True, rope_base=0.0),
+])
+def test_invalid_configs(bad):
+    cfg = _cfg(**bad)
+    if bad == dict(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 0), residual=0):
+        # whole-axis K with a per-token V group is fine; make V per-channel grouped to be invalid
+        cfg = _cfg(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 0), v=(K.INT_ASYM, 4, K.PER_CHANNEL, 32), residual=0)
+    assert K.kvq_validate_config(cfg) == -1
+    n = C.c_size_t()
+    assert _lib.raw.kvq_arena_bytes(C.byref(cfg), C.byref(n)) == -1
+
+
+def _append(cfg, arena=0x100000, t0=0, n=4, k=0x200000, v=0x300000, ks=None, vs=None, flags=0):
+    return _lib.raw.kvq_quantize_append(C.byref(cfg), arena, t0, n, k, v, ks, vs, flags, None)
+
+
+def test_append_validation_paths():
+    cfg = _cfg()
+    assert _append(cfg, t0=1020, n=8) == -3                      # capacity
+    assert _append(cfg, t0=-1) == -1
+    assert _append(cfg, n=-2) == -1
+    assert _append(cfg, n=0) == 0                                # no-op, no HIP call
+    assert _append(cfg, arena=None) == -5
+    assert _append(cfg, arena=0x100010) == -4                    # arena not 256-aligned
+    assert _append(cfg, k=0x200004) == -4                        # input not 16-aligned
+    assert _append(cfg, flags=K.CALIBRATE) == -1                 # calibrate without FP8
+    assert _append(cfg, flags=8) == -1
+    fp8 = _cfg(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0), residual=0)
+    assert _append(fp8, t0=8, flags=K.CALIBRATE) == -1           # calibrate only at t0 == 0
+    assert _append(fp8, t0=8, ks=0x400000) == -1                 # scales only at t0 == 0
+    assert _append(fp8, ks=0x400000, flags=K.CALIBRATE) == -1
+    whole = _cfg(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 0), v=(K.INT_ASYM, 4, K.PER_TOKEN, 0), residual=0)
+    assert _append(whole, t0=16) == -2                           # would rescale history
+    tens = _cfg(k=(K.INT_SYM, 8, K.PER_TENSOR, 0), v=(K.NONE, 16, 0, 0), residual=0)
+    assert _append(tens, t0=1) == -2
+
+
+def test_attention_validation_paths():
+    cfg = _cfg()
+    raw = _lib.raw
+    opt = K.AttnOptions()
+    ws = K.kvq_workspace_bytes(cfg, 500)
+
+    def call(T=500, arena=0x100000, q=0x200000, out=0x300000, sm=0.088, w=0x400000, wb=ws, o=opt):
+        return raw.kvq_decode_attention(C.byref(cfg), arena, T, q, out, sm, w, wb, C.byref(o), None)
+
+    assert call(T=0) == -3
+    assert call(T=1025) == -3
+    assert call(sm=0.0) == -1
+    assert call(sm=float("nan")) == -1
+    assert call(q=None) == -5
+    assert call(out=0x300008) == -4
+    assert call(w=0x400010) == -4
+    assert call(wb=ws - 1) == -6
+    bad = K.AttnOptions(); bad.kernel = 5
+    assert call(o=bad) == -1
+    bad = K.AttnOptions(); bad.reserved[2] = 1
+    assert call(o=bad) == -1
+    bad = K.AttnOptions(); bad.kernel = 2
+    fp32none = _cfg(k=(K.NONE, 32, 0, 0), v=(K.NONE, 32, 0, 0), residual=0)
+    assert raw.kvq_decode_attention(C.byref(fp32none), 0x100000, 10, 0x200000, 0x300000, 0.1,
+                                    0x400000, 1 << 20, C.byref(bad), None) == -2
+
+
+def test_dequantize_validation_paths():
+    cfg = _cfg()
+    raw = _lib.raw
+    assert raw.kvq_dequantize(C.byref(cfg), 0x100000, 2000, 0x200000, None, None) == -3
+    assert raw.kvq_dequantize(C.byref(cfg), 0x100000, 0, 0x200000, None, None) == 0
+    assert raw.kvq_dequantize(C.byref(cfg), 0x100000, 10, None, None, None) == 0
+    assert raw.kvq_dequantize(C.byref(cfg), None, 10, 0x200000, None, None) == -5
+    assert raw.kvq_dequantize(C.byref(cfg), 0x100000, 10, 0x200008, None, None) == -4
+
+
+def test_layout_sections_disjoint_and_sized():
+    for cfg in [_cfg(), _cfg(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0), residual=0),
+                _cfg(pre_rope_k=True, k=(K.INT_ASYM, 2, K.PER_CHANNEL, 32), v=(K.INT_ASYM, 2, K.PER_TOKEN, 32)),
+                _cfg(k=(K.INT_SYM, 8, K.PER_TENSOR, 0), v=(K.NONE, 32, 0, 0), residual=0)]:
+        lay = K.kvq_arena_layout(cfg)
+        B, H, D, Tc = cfg.batch, cfg.num_kv_heads, cfg.head_dim, lay.token_capacity
+        assert Tc % 32 == 0 and Tc >= cfg.max_tokens
+        bk = cfg.k.bits if cfg.k.scheme in (K.NONE, K.INT_ASYM) else 8
+        bv = cfg.v.bits if cfg.v.scheme in (K.NONE, K.INT_ASYM) else 8
+        assert lay.k_row_bytes == D * bk // 8 and lay.v_block_bytes == 32 * D * bv // 8
+        secs = [(n, getattr(lay, n)) for n in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
+                                               "v_zero", "ring_k", "ring_v", "rope", "fp8_calib")]
+        present = [(n, o) for n, o in secs if o != 2 ** 64 - 1]
+        offs = [o for _, o in present]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert lay.total_bytes == K.kvq_arena_bytes(cfg)
+        assert present[1][1] - present[0][1] >= B * H * Tc * lay.k_row_bytes
+
+
+def test_fp16_cache_bytes_per_token_pin():
+    """Scheme NONE at fp16 reproduces 2 * kv_heads * head_dim * 2 bytes per token per
+    layer, i.e. 327,680 bytes/token for 80 Llama-3.1-70B layers."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_bytes_facts.json")))
+    T = 131072
+    cfg = K.make_config(batch=1, num_q_heads=64, num_kv_heads=8, head_dim=128, max_tokens=T,
+                        k=(K.NONE, 16, 0, 0), v=(K.NONE, 16, 0, 0))
+    per_layer = K.kvq_arena_bytes(cfg)
+    assert per_layer * 80 / T == g["fp16_bytes_per_token"]
+    assert per_layer * 80 / 2 ** 30 == g["fp16_gib_at_128k"]
+    fp8 = K.make_config(batch=1, num_q_heads=64, num_kv_heads=8, head_dim=128, max_tokens=T,
+                        k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0))
+    lay = K.kvq_arena_layout(fp8)
+    code_bytes = lay.k_scale - lay.k_codes + (lay.v_scale - lay.v_codes)
+    assert code_bytes * 80 / 2 ** 30 == g["fp8_gib_at_128k"]
+
+
+@pytest.mark.parametrize("k,v,R", [
+    ((K.INT_ASYM, 4, K.PER_CHANNEL, 128), (K.INT_ASYM, 4, K.PER_TOKEN, 0), 128),
+    ((K.INT_ASYM, 2, K.PER_CHANNEL, 32), (K.INT_ASYM, 2, K.PER_TOKEN, 32), 32),
+    ((K.INT_ASYM, 2, K.PER_CHANNEL, 32), (K.INT_ASYM, 2, K.PER_TOKEN, 32), 0),
+    ((K.FP8_E4M3, 8, 0, 0), (K.FP8_E4M3, 8, 0, 0), 0),
+    ((K.INT_ASYM, 4, K.PER_TOKEN, 0), (K.INT_ASYM, 4, K.PER_TOKEN, 0), 64),
+    ((K.INT_SYM, 8, K.PER_CHANNEL, 0), (K.INT_SYM, 8, K.PER_TOKEN, 0), 0),
+])
+def test_quantized_tokens_matches_oracle(k, v, R):
+    cfg = _cfg(k=k, v=v, residual=R, max_tokens=5000)
+    ocfg = OC.Cfg(2, 8, 2, 128, OC.Spec(*k), OC.Spec(*v), R=R)
+    assert K.kvq_arena_layout(cfg).ring_slots == OC.ring_slots(ocfg)
+    for T in list(range(0, 300)) + [4095, 4096, 4097, 5000]:
+        assert K.kvq_quantized_tokens(cfg, T) == OC.quantized_tokens(ocfg, T)
+    with pytest.raises(K.KvqError):
+        K.kvq_quantized_tokens(cfg, 5001)

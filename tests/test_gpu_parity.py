@@ -1,0 +1,172 @@
+"""GPU parity on small shapes: quantize-append, dequantize and decode attention
+through the C ABI against the CPU oracle (bit-exact codes, scales, window and
+dequantized values; attention within 2e-3 max relative L2)."""
+import zlib
+
+import numpy as np
+import pytest
+
+import quantized_decode_attention_05_amd as K
+import workloads as W
+from oracle import cache as OC
+from tests.kvq_harness import (ATTN_TOL, Case, GpuCache, attention_error, compare_dequant,
+                               compare_sections, say)
+
+pytestmark = pytest.mark.gpu
+
+A, S, F8, NO = K.INT_ASYM, K.INT_SYM, K.FP8_E4M3, K.NONE
+CH, TOK, TEN = K.PER_CHANNEL, K.PER_TOKEN, K.PER_TENSOR
+
+# (name, case, T, append schedule, kernels)
+FORMATS = [
+    ("int4ch128_int4tok_R128", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128)),
+    ("int2ch32_int2tok32_R32", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32)),
+    ("int2ch32_int2tok32_R0", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=0)),
+    ("int8ch64_int8tok16_R64", dict(k=(A, 8, CH, 64), v=(A, 8, TOK, 16), R=64)),
+    ("int4tok_int4tok_R0", dict(k=(A, 4, TOK, 0), v=(A, 4, TOK, 0), R=0)),
+    ("int4tok32_int2tok_R64", dict(k=(A, 4, TOK, 32), v=(A, 2, TOK, 64), R=64)),
+    ("fp8_fp8", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0)),
+    ("fp8_fp8_R32", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=32)),
+    ("sym8tok_sym8tok", dict(k=(S, 8, TOK, 0), v=(S, 8, TOK, 32), R=0)),
+    ("none16_int4tok", dict(k=(NO, 16, 0, 0), v=(A, 4, TOK, 0), R=0)),
+    ("int2ch32_none32", dict(k=(A, 2, CH, 32), v=(NO, 32, 0, 0), R=32)),
+    ("prerope_int2ch32_int2tok32_R32", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True)),
+    ("prerope_int4ch128_R128", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128, pre_rope=True,
+                                    rope_base=500.0)),
+]
+ONE_SHOT = [
+    ("sym8ten_sym8ten", dict(k=(S, 8, TEN, 0), v=(S, 8, TEN, 0))),
+    ("sym8chwhole_sym8tok", dict(k=(S, 8, CH, 0), v=(S, 8, TOK, 0))),
+    ("int4chwhole_int4tok", dict(k=(A, 4, CH, 0), v=(A, 4, TOK, 0))),
+    ("int4ten_none32", dict(k=(A, 4, TEN, 0), v=(NO, 32, 0, 0))),
+]
+
+
+def _schedule(kind, T):
+    if kind == "oneshot":
+        return [T]
+    # prefill, a run of single-token appends across fold boundaries, then chunks
+    first = max(1, T // 2)
+    rest = T - first
+    sched = [first]
+    singles = min(rest, 37)
+    sched += [1] * singles
+    rest -= singles
+    while rest > 0:
+        n = min(rest, 19)
+        sched.append(n)
+        rest -= n
+    return sched
+
+
+def run_case(case: Case, T: int, schedule, seed=0, kernels=(K.KERNEL_GENERIC,), fp8_mode="calibrate",
+             num_splits=0):
+    say(f"[case] {case} T={T} sched={schedule[:4]}... seed={seed}")
+    (Kf, Kp), (Vf, Vp) = W.random_case(seed, case.B, case.Hkv, T, case.D, dtype=case.dtype)
+    qf, qp = W.random_queries(seed, case.B, case.Hq, case.D, dtype=case.dtype)
+    gc = GpuCache(case, cap=T + 5)
+    fp8 = case.k[0] == F8 or case.v[0] == F8
+    ks = vs = None
+    t = 0
+    for i, n in enumerate(schedule):
+        flags = 0
+        if fp8 and i == 0 and fp8_mode == "calibrate":
+            flags = K.CALIBRATE
+        if fp8 and i == 0 and fp8_mode == "given":
+            ks = np.linspace(0.05, 0.2, case.Hkv).astype(np.float32)
+            vs = np.linspace(0.01, 0.02, case.Hkv).astype(np.float32)
+            gc.append(Kp[:, :, t:t + n], Vp[:, :, t:t + n], 0, ks, vs)
+        else:
+            gc.append(Kp[:, :, t:t + n], Vp[:, :, t:t + n], flags)
+        t += n
+    ocfg = case.oracle_cfg()
+    st = OC.quantize_cache(ocfg, Kf, Vf, T, k_scale=ks, v_scale=vs,
+                           calibrate_tokens=schedule[0] if (fp8 and fp8_mode == "calibrate") else 0)
+    compare_sections(gc, st)
+    compare_dequant(gc, st)
+    errs = {}
+    for kern in kernels:
+        out = gc.attention(qp, kernel=kern, num_splits=num_splits)
+        errs[kern] = attention_error(out, qf, st, case)
+        assert errs[kern] <= ATTN_TOL, (kern, errs[kern])
+    say(f"[ok] attention max rel-L2 {errs}")
+    return gc, st, errs
+
+
+@pytest.mark.parametrize("name,fmt", FORMATS, ids=[f[0] for f in FORMATS])
+@pytest.mark.parametrize("sched", ["oneshot", "stream"])
+def test_formats(name, fmt, sched):
+    case = Case(B=2, Hq=8, Hkv=2, D=128, dtype="bf16", **fmt)
+    T = 333
+    run_case(case, T, _schedule(sched, T), seed=zlib.crc32(name.encode()) % 1000)
+
+
+@pytest.mark.parametrize("name,fmt", ONE_SHOT, ids=[f[0] for f in ONE_SHOT])
+def test_one_shot_formats(name, fmt):
+    case = Case(B=2, Hq=4, Hkv=2, D=128, dtype="f32", **fmt)
+    run_case(case, 300, [300], seed=3)
+
+
+@pytest.mark.parametrize("D,n_rep,dtype", [(64, 1, "f32"), (64, 4, "f16"), (128, 1, "f16"),
+                                           (128, 8, "bf16"), (128, 16, "bf16")])
+def test_shapes_and_dtypes(D, n_rep, dtype):
+    case = Case(B=2, Hq=2 * n_rep, Hkv=2, D=D, dtype=dtype, k=(A, 4, CH, 32), v=(A, 4, TOK, 32), R=32)
+    run_case(case, 257, _schedule("stream", 257), seed=D + n_rep)
+
+
+@pytest.mark.parametrize("T", [1, 5, 31, 32, 33, 64, 65])
+def test_short_caches_all_in_window(T):
+    """T below the window keeps every token in fp16 (Tq = 0 for T < R + G)."""
+    case = Case(B=1, Hq=4, Hkv=1, D=128, dtype="bf16", k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32)
+    run_case(case, T, _schedule("stream", T) if T > 1 else [1], seed=T)
+
+
+@pytest.mark.parametrize("mode", ["given", "unit"])
+def test_fp8_scale_modes(mode):
+    case = Case(B=2, Hq=4, Hkv=2, D=128, dtype="bf16", k=(F8, 8, 0, 0), v=(F8, 8, 0, 0))
+    run_case(case, 200, [120, 1, 1, 78], seed=9, fp8_mode=mode)
+
+
+def test_fp8_saturation_of_later_appends():
+    """Tokens appended after calibration reuse the stored scale and saturate."""
+    case = Case(B=1, Hq=4, Hkv=1, D=128, dtype="f32", k=(F8, 8, 0, 0), v=(F8, 8, 0, 0))
+    (Kf, Kp), (Vf, Vp) = W.random_case(4, 1, 1, 40, 128, dtype="f32")
+    Kf = Kf.copy(); Kf[:, :, 30:] *= 50.0          # far beyond the calibrated range
+    gc = GpuCache(case, cap=64)
+    gc.append(Kf[:, :, :30], Vf[:, :, :30], K.CALIBRATE)
+    gc.append(Kf[:, :, 30:], Vf[:, :, 30:])
+    st = OC.quantize_cache(case.oracle_cfg(), Kf, Vf, 40, calibrate_tokens=30)
+    compare_sections(gc, st)
+    codes = st["k"]["codes"][0, 0, 30:]
+    assert np.any((codes & 0x7F) == 0x7E)           # saturated to +-448 * scale
+    compare_dequant(gc, st)
+
+
+def test_e4m3_decode_all_codes():
+    """Write every finite E4M3 byte into the K code rows and dequantize."""
+    case = Case(B=1, Hq=1, Hkv=1, D=128, dtype="f32", k=(F8, 8, 0, 0), v=(F8, 8, 0, 0))
+    gc = GpuCache(case, cap=64)
+    ks = np.array([1.0], np.float32)
+    z = np.zeros((1, 1, 2, 128), np.float32)
+    gc.append(z, z, 0, ks, ks)                     # scale 1.0 stored, T = 2
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    rows = codes.reshape(2, 127)
+    buf = np.zeros((2, 128), np.uint8)
+    buf[:, :127] = rows
+    import torch
+    gc.arena[gc.layout.k_codes: gc.layout.k_codes + 256] = torch.from_numpy(buf.reshape(-1)).cuda()
+    kd, _ = gc.dequantize(2)
+    from oracle import quant as OQ
+    assert np.array_equal(kd[0, 0, :, :127], OQ.e4m3_decode(rows))
+
+
+def test_attention_deterministic_and_split_invariant():
+    case = Case(B=2, Hq=8, Hkv=2, D=128, dtype="bf16", k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128)
+    gc, st, _ = run_case(case, 1000, [1000], seed=11)
+    (qf, qp) = W.random_queries(11, case.B, case.Hq, case.D, dtype="bf16")
+    a = gc.attention(qp)
+    b = gc.attention(qp)
+    assert np.array_equal(a, b)
+    for s in (1, 3, 16):
+        o = gc.attention(qp, num_splits=s, kernel=K.KERNEL_GENERIC)
+        assert attention_error(o, qf, st, case) <= ATTN_TOL

@@ -148,13 +148,19 @@ def query(name: str) -> np.ndarray:
     return f32_to_bf16_bits(x)
 
 
-def full_prefill(name: str, which: str) -> np.ndarray:
-    """bf16 bits [B, Hkv, T, D] of the whole prefill K or V (large: 2 bytes/element)."""
+def full_prefill(name: str, which: str, threads: int = 8) -> np.ndarray:
+    """bf16 bits [B, Hkv, T, D] of the whole prefill K or V (large: 2 bytes/element).
+    Chunks are independent streams, drawn on a few threads."""
+    from concurrent.futures import ThreadPoolExecutor
     w = WORKLOADS[name]
     out = np.empty((w["B"], w["Hkv"], w["T"], w["D"]), dtype=np.uint16)
-    for b in range(w["B"]):
-        for h in range(w["Hkv"]):
-            out[b, h] = kv_chunk(name, b, h, which)
+
+    def fill(bh):
+        b, h = divmod(bh, w["Hkv"])
+        out[b, h] = kv_chunk(name, b, h, which)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fill, range(w["B"] * w["Hkv"])))
     return out
 
 
