@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the quantized KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch: quantize-append of
+the new token of every sequence (folding the fp16 window into the quantized
+cache when a block fills) followed by split-K decode attention over all cached
+tokens (pass 1 + merge).  Inputs are synthetic, seeded, and resident in HBM
+before the timed region.
+
+Prints one JSON line.  ``value`` is algorithmic bytes per step / step time
+(GB/s); ``roofline`` prices the decode-attention launches (pass 1 + merge)
+against MI355X's 8 TB/s HBM peak with their durations measured by HIP events
+on the launch stream; ``cpu_baseline`` times the CPU oracle (dequantize from
+codes + fp64 attention) on a bounded sample of (sequence, kv head) pairs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+# cache format of each workload: (k spec, v spec, residual, pre-RoPE, calibrate)
+FORMATS = {
+    "c3_fp8_e4m3_gqa_8k": ((3, 8, 0, 0), (3, 8, 0, 0), 0, False, True),
+    "c4_int4_llama70b_128k": ((1, 4, 1, 128), (1, 4, 2, 0), 128, False, False),
+    "c5_int2_kivi_prerope_32k": ((1, 2, 1, 32), (1, 2, 2, 32), 32, True, False),
+}
+DESCR = {
+    "c3_fp8_e4m3_gqa_8k": "FP8 E4M3 K/V, per-kv-head calibrated scales",
+    "c4_int4_llama70b_128k": "INT4 K per-channel G128 + INT4 V per-token, fp16 window 128",
+    "c5_int2_kivi_prerope_32k": "INT2 K per-channel G32 (pre-RoPE) + INT2 V per-token G32, fp16 window 32",
+}
+
+
+def code_bits(spec):
+    scheme, bits = spec[0], spec[1]
+    return bits if scheme in (0, 1) else 8
+
+
+def algorithmic_bytes(w, fmt, T):
+    """Bytes one decode attention over T tokens must move: every packed code, its
+    fp32 scale/zero and the fp16 window read once, q (bf16) read, out (fp32) written."""
+    kspec, vspec, R, _, _ = fmt
+    B, Hq, Hkv, D = w["B"], w["Hq"], w["Hkv"], w["D"]
+    G = kspec[3] if (kspec[0] in (1, 2) and kspec[2] == 1 and kspec[3] > 0) else 1
+    Tq = G * (max(T - R, 0) // G) if (R > 0 or G > 1) else T
+    per = 0.0
+    per += Tq * D * code_bits(kspec) / 8 + Tq * D * code_bits(vspec) / 8
+    for spec in (kspec, vspec):
+        nmeta = 2 if spec[0] == 1 else 1
+        if spec[0] in (1, 2):
+            if spec[2] == 1:
+                per += (Tq // spec[3] if spec[3] else 1) * D * 4 * nmeta
+            elif spec[2] == 2:
+                per += Tq * (D // (spec[3] or D)) * 4 * nmeta
+            else:
+                per += 4 * nmeta
+    per += (T - Tq) * D * 2 * 2
+    total = per * B * Hkv
+    fp8_scales = 8 * Hkv if kspec[0] == 3 else 0
+    return total + fp8_scales + B * Hq * D * 2 + B * Hq * D * 4, Tq
+
+
+def cpu_baseline(name, w, fmt, T, bytes_per_step, budget_s=12.0):
+    """The oracle as it stands, on host cores: per sampled (sequence, kv head),
+    dequantize the cache from its codes and run fp64 attention for its query
+    heads; scaled to the whole step."""
+    import numpy as np
+    import workloads as W
+    from oracle import attention as OA
+    from oracle import cache as OC
+
+    kspec, vspec, R, pre_rope, calibrate = fmt
+    n_rep = w["Hq"] // w["Hkv"]
+    sub = OC.Cfg(1, n_rep, 1, w["D"], OC.Spec(*kspec), OC.Spec(*vspec), R, pre_rope, w.get("rope_base", 1e4))
+    q = W.bf16_bits_to_f32(W.query(name))
+    sm = 1.0 / math.sqrt(w["D"])
+    done, spent = 0, 0.0
+    pairs = [(b, h) for b in range(w["B"]) for h in range(w["Hkv"])]
+    for (b, h) in pairs:
+        kb, vb = W.kv_chunk(name, b, h, "k"), W.kv_chunk(name, b, h, "v")
+        if w.get("n_new", 0):
+            kb = np.concatenate([kb, W.new_token_chunk(name, b, h, "k")])
+            vb = np.concatenate([vb, W.new_token_chunk(name, b, h, "v")])
+        Kf, Vf = W.bf16_bits_to_f32(kb)[None, None], W.bf16_bits_to_f32(vb)[None, None]
+        st = OC.quantize_cache(sub, Kf, Vf, T, k_scale=np.ones(1, np.float32), v_scale=np.ones(1, np.float32))
+        Tq = st["Tq"]
+        t0 = time.perf_counter()
+        kh = np.concatenate([OC.dequantize_part(st["k"], sub.k), Kf[:, :, Tq:T].astype(np.float16).astype(np.float32)
+                             if OC.has_window(sub) else Kf[:, :, Tq:T]], axis=2)
+        vh = np.concatenate([OC.dequantize_part(st["v"], sub.v), Vf[:, :, Tq:T].astype(np.float16).astype(np.float32)
+                             if OC.has_window(sub) else Vf[:, :, Tq:T]], axis=2)
+        OA.decode_attention(q[b:b + 1, h * n_rep:(h + 1) * n_rep], kh, vh, sm,
+                            pre_rope_base=sub.rope_base if pre_rope else None)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    per_pair = spent / done
+    step_s = per_pair * len(pairs)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    return {
+        "value": round(bytes_per_step / step_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(pairs)} (sequence, kv head) pairs: numpy dequantize from codes + fp64 "
+                  f"attention ({'with RoPE, ' if pre_rope else ''}{n_rep} query heads each), "
+                  f"{per_pair:.3f} s/pair, scaled to the full step ({step_s:.1f} s/step, "
+                  f"{1.0 / step_s:.4f} steps/s); host os.cpu_count()={os.cpu_count()}",
+        "seconds_per_step": round(step_s, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5_int2_kivi_prerope_32k", choices=list(FORMATS))
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 MFMA")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
+              f"(the path shards over (sequence, kv head) pairs without communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_decode_attention_05_amd as K
+    import workloads as W
+
+    name = a.workload
+    w = W.WORKLOADS[name]
+    fmt = FORMATS[name]
+    kspec, vspec, R, pre_rope, calibrate = fmt
+    B, Hq, Hkv, D, T0 = w["B"], w["Hq"], w["Hkv"], w["D"], w["T"]
+    n_new = w.get("n_new", 0)
+    steps_total = a.warmup + a.steps
+    cap = T0 + n_new * (steps_total + 1) + 64
+    cfg = K.make_config(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_tokens=cap,
+                        k=kspec, v=vspec, in_dtype=K.BF16, out_dtype=K.F32, residual=R,
+                        pre_rope_k=pre_rope, rope_base=w.get("rope_base", 10000.0))
+    dev = torch.device("cuda:0")
+    print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+    kp = torch.from_numpy(W.full_prefill(name, "k").view(np.int16)).view(torch.bfloat16).to(dev)
+    vp = torch.from_numpy(W.full_prefill(name, "v").view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(W.query(name).view(np.int16)).view(torch.bfloat16).to(dev)
+    if n_new:
+        kn = torch.from_numpy(W.full_new_tokens(name, "k").view(np.int16)).view(torch.bfloat16).to(dev)
+        vn = torch.from_numpy(W.full_new_tokens(name, "v").view(np.int16)).view(torch.bfloat16).to(dev)
+    arena = torch.empty(K.kvq_arena_bytes(cfg), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kvq_workspace_bytes(cfg, cap, a.kernel, a.splits), dtype=torch.uint8, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    print(f"[bench] prefill T={T0}", file=sys.stderr, flush=True)
+    K.kvq_quantize_append(cfg, arena, 0, kp, vp, flags=K.CALIBRATE if calibrate else 0)
+    del kp, vp
+    torch.cuda.synchronize()
+    T = T0
+
+    def step(T):
+        if n_new:
+            K.kvq_quantize_append(cfg, arena, T, kn, vn)
+            T += n_new
+        K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel, a.splits)
+        return T
+
+    for _ in range(a.warmup):
+        T = step(T)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    T_first = T + n_new
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        if n_new:
+            K.kvq_quantize_append(cfg, arena, T, kn, vn)
+            T += n_new
+        ev[i][0].record(stream)
+        K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel, a.splits)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / a.steps
+    attn_ms = [s.elapsed_time(e) for s, e in ev]
+    attn_us = 1000.0 * float(np.mean(attn_ms))
+    T_mid = (T_first + T) // 2
+    bytes_step, Tq = algorithmic_bytes(w, fmt, T_mid)
+    achieved = bytes_step / (attn_us * 1e-6) / 1e9
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    used_kernel = a.kernel
+    if used_kernel == 0:
+        try:
+            K.kvq_workspace_bytes(cfg, T, K.KERNEL_MFMA)
+            used_kernel = 2
+        except K.KvqError:
+            used_kernel = 1
+    res = {
+        "metric": "quantized decode-attention HBM GB/s (% of peak) + decode steps/s at 32K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2+fp32" if kspec[1] == 2 else ("fp8+fp32" if kspec[0] == 3 else "int4+fp32"),
+        "data": "synthetic (seeded Gaussian K/V with fixed outlier key channels, bf16)",
+        "config": {
+            "workload": name, "format": DESCR[name], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+            "head_dim": D, "context_start": T_first, "context_end": T, "append_tokens_per_step": n_new,
+            "attention_kernel": {1: "generic", 2: "mfma"}[used_kernel],
+        },
+        "decode_steps_per_s": round(1000.0 / ms_per_step, 2),
+        "attention_us": round(attn_us, 3),
+        "attention_pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes_per_step": int(bytes_step),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode attention launch: pass 1 (split-K) + merge, HIP-event timed",
+        },
+    }
+    if not a.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(name, w, fmt, T_first, algorithmic_bytes(w, fmt, T_first)[0],
+                                           a.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

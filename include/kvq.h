@@ -185,7 +185,9 @@ typedef struct kvq_attn_options {
   int32_t reserved[6];  /* must be 0                                             */
 } kvq_attn_options;
 
-/* Workspace bytes needed by kvq_decode_attention for T tokens (host only). */
+/* Workspace bytes needed by kvq_decode_attention for T tokens (host only).  The
+ * size never decreases with T, so the size for the largest T a caller will use
+ * (e.g. max_tokens) serves every smaller T with the same options. */
 int kvq_workspace_bytes(const kvq_config* cfg, int64_t T, const kvq_attn_options* opt,
                         size_t* bytes);
 

@@ -302,3 +302,35 @@ def cache_bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes
     ("KV Cache Quantization: Why Keys and Values Need Different Axes", section
     "Why is the KV cache the thing that actually runs out of memory?")."""
     return 2 * layers * kv_heads * head_dim * dtype_bytes
+
+
+def dequantize_part(part: dict, spec: Spec) -> np.ndarray:
+    """Rebuild x_hat [B, H, Tq, D] from a quantize_part result's codes and
+    (scale, zero) alone, by the same element rules (used to time a decode step
+    of the oracle from stored codes)."""
+    codes = part["codes"]
+    B, H, T, D = codes.shape
+    if spec.scheme == NONE:
+        return codes.astype(np.float32)
+    if spec.scheme == FP8_E4M3:
+        return Q.fp8_dequantize(codes, part["scale"].reshape(1, H, 1, 1))
+    s, z = part["scale"], part["zero"]
+    if spec.axis == PER_TENSOR:
+        sb = s.reshape(B, H, 1, 1)
+        zb = None if z is None else z.reshape(B, H, 1, 1)
+        cg = codes
+    elif spec.axis == PER_CHANNEL:
+        G = spec.group if spec.group > 0 else T
+        cg = codes.reshape(B, H, T // G, G, D)
+        sb = s[:, :, :, None, :]
+        zb = None if z is None else z[:, :, :, None, :]
+    else:
+        Gc = spec.group if spec.group > 0 else D
+        cg = codes.reshape(B, H, T, D // Gc, Gc)
+        sb = s[..., None]
+        zb = None if z is None else z[..., None]
+    if spec.scheme == INT_ASYM:
+        out = Q.asym_dequantize(cg, sb, zb)
+    else:
+        out = Q.sym_dequantize(cg, sb)
+    return out.reshape(B, H, T, D)

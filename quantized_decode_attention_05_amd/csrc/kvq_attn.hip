@@ -199,13 +199,16 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
   if (splits == 0) {
     // enough work-groups to cover the 256 CUs a few times over
     const int64_t bh = (int64_t)p.B * p.Hkv;
-    int64_t want = cdiv(1024, bh);
+    const int64_t want = cdiv(1024, bh);
     const int64_t min_tokens = (kernel == 2) ? 256 : 128;
     const int64_t by_len = cdiv(T, min_tokens);
     splits = (int)(want < by_len ? want : by_len);
   }
   if (splits > max_splits) splits = (int)max_splits;
   if (splits < 1) splits = 1;
+  // The workspace is sized for the target split count, which never decreases
+  // with T; rounding the chunk to whole 64-token units can only lower the count.
+  const int64_t target = splits;
   int64_t chunk = cdiv(cdiv(T, splits), unit) * unit;
   splits = (int)cdiv(T, chunk);
   ap->kernel = kernel;
@@ -213,7 +216,7 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
   ap->chunk = chunk;
   ap->T = T;
   ap->Tq = quantized_tokens(p, T);
-  const uint64_t rows = (uint64_t)p.B * p.Hq * splits;
+  const uint64_t rows = (uint64_t)p.B * p.Hq * target;
   ap->ws_o = 0;
   ap->ws_ml = (rows * p.D * 4 + 255) & ~(uint64_t)255;
   ap->workspace_bytes = ap->ws_ml + ((rows * 2 * 4 + 255) & ~(uint64_t)255);

@@ -1,19 +1,673 @@
-// MFMA decode attention for the hot cache formats (placeholder: no format is
-// routed here yet).
+// MFMA split-K decode attention for the hot cache formats on gfx950.
+//
+// Same computation as the generic kernel (per query head: logits q . k_hat /
+// sqrt(d) in log2 units, online softmax, p . v_hat; "FP8 KV Cache
+// Quantization: Why Keys Break Before Values", section "Why does the K cache
+// break before the V cache?"), organised for 64-wide wavefronts and the
+// 16x16x32 fp16 matrix instruction:
+//
+//  * QK^T as S^T = K_tile . Q^T: A = 16 tokens x 32 channels of codes, B = the
+//    query heads of one kv head as columns (hi and lo fp16 halves of the fp32
+//    query in separate columns, so fp16 operands lose nothing).  Codes are
+//    exact in fp16; with per-channel keys the per-channel scale folds into the
+//    query columns and the zero-point into a per-head bias:
+//      logit = sum_c (q_c s_c) x_c + sum_c q_c z_c.
+//    A code becomes fp16 by ORing its bits into the mantissa of 1024 and
+//    subtracting 1024 (exact), so the accumulation never carries an offset.
+//  * With pre-RoPE keys ("KV Cache Quantization: Why Keys and Values Need
+//    Different Axes", section "Where does RoPE break this?") each lane
+//    dequantizes its 32 channels to fp32, rotates the channel pairs by
+//    position * theta_i and packs fp16 operands (dequantize -> rotate -> dot).
+//  * PV as O = P . V_tile: A = probabilities of 8 tokens per lane (times the
+//    per-token value scale of the N-tile's channel group), B = value codes
+//    read straight from the 32-token block layout, whose lane order is exactly
+//    this instruction's B-operand order; zero-points enter through per-(head,
+//    group) bias sums.
+//  * The S^T accumulator of two 16-token tiles (token rows permuted so that
+//    lane (n, g) holds tokens 8g..8g+7) is already the PV A operand of head n:
+//    no data moves between QK^T and PV.
+//
+// Each work-group (4 wavefronts) takes one (sequence, kv head, token split);
+// wavefronts walk disjoint runs of 32-token steps and their softmax states
+// are combined through LDS before one partial per split is written.
+#include <type_traits>
+
 #include "kvq_internal.h"
 #include "kvq_launch.h"
 
 namespace kvq {
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32;
+
+namespace mf {
+
+constexpr float kNegBig = -1.0e30f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+constexpr u32 kMagic = 0x64006400u;    // fp16 1024 in both halves
+
+enum Fmt { INT2 = 2, INT4 = 4, INT8 = 8, FP8 = 9 };
+
+struct Args {
+  const uint8_t* arena;
+  const void* q;
+  float* ws_o;
+  float* ws_ml;
+  int64_t T, Tq, chunk;
+  int32_t S;
+  float qscale;
+};
+
+__device__ __forceinline__ half8 pack8(u32 a, u32 b, u32 c, u32 d) {
+  union { u32 u[4]; half8 h; } x;
+  x.u[0] = a; x.u[1] = b; x.u[2] = c; x.u[3] = d;
+  return x.h;
+}
+__device__ __forceinline__ u32 h2u(half2v h) { return __builtin_bit_cast(u32, h); }
+__device__ __forceinline__ u32 pk_f16(float a, float b) {
+  float2v v = {a, b};
+  return h2u(__builtin_convertvector(v, half2v));
+}
+// (1024 + x) as fp16 -> x, exactly (both are fp16 integers)
+__device__ __forceinline__ u32 unmagic(u32 v) {
+  const half2v m = {(_Float16)1024.0f, (_Float16)1024.0f};
+  return h2u(__builtin_bit_cast(half2v, v) - m);
+}
+__device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float lo_f(u32 x) { return (float)__builtin_bit_cast(half2v, x)[0]; }
+__device__ __forceinline__ float hi_f(u32 x) { return (float)__builtin_bit_cast(half2v, x)[1]; }
+
+// Position of the e-th fp16 of k-step j inside a lane's 32 key channels, for
+// the register order each code width unpacks into.
+template <int KF, bool ROPE>
+__device__ __forceinline__ int kslot(int j, int e) {
+  if (ROPE || KF == INT8 || KF == FP8) return 8 * j + e;                  // natural
+  if (KF == INT4) return 8 * j + (e >> 1) + 4 * (e & 1);                   // (c, c+4) pairs
+  return 16 * (j >> 1) + 4 * (j & 1) + (e >> 1) + 8 * (e & 1);             // INT2: (c, c+8) pairs
+}
+
+template <int F> struct Bits { static constexpr int v = (F == FP8) ? 8 : F; };
+
+// ---- key operand unpacking -------------------------------------------------------
+
+// Codes (1024 + x) of one lane's 32 channels in kslot order, from KB dwords.
+template <int KF>
+__device__ __forceinline__ void unpack_k_magic(const u32* w, half8* A) {
+  if constexpr (KF == INT4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = unmagic(((w[j] >> (4 * i)) & 0x000F000Fu) | kMagic);
+      A[j] = pack8(r[0], r[1], r[2], r[3]);
+    }
+  } else if constexpr (KF == INT2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      u32 r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = unmagic(((w[d] >> (2 * i)) & 0x00030003u) | kMagic);
+      A[2 * d] = pack8(r[0], r[1], r[2], r[3]);
+      A[2 * d + 1] = pack8(r[4], r[5], r[6], r[7]);
+    }
+  } else {  // INT8: natural pairs (c, c+1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32 src = w[2 * j + (i >> 1)];
+        const int sh = 16 * (i & 1);
+        r[i] = unmagic((((src >> sh) & 0xFFu) | (((src >> (sh + 8)) & 0xFFu) << 16)) | kMagic);
+      }
+      A[j] = pack8(r[0], r[1], r[2], r[3]);
+    }
+  }
+}
+
+// Exact fp16 values of 32 E4M3 codes (natural order).
+__device__ __forceinline__ void unpack_k_fp8(const u32* w, half8* A) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    A[j] = pack8(h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j], 1.0f, false)),
+                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j], 1.0f, true)),
+                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j + 1], 1.0f, false)),
+                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j + 1], 1.0f, true)));
+  }
+}
+
+// Integer code of channel e (0..31) of a lane's key data.
+template <int KF>
+__device__ __forceinline__ u32 kcode(const u32* w, int e) {
+  constexpr int B = Bits<KF>::v;
+  const int bit = e * B;
+  return (w[bit >> 5] >> (bit & 31)) & ((1u << B) - 1u);
+}
+
+// ---- value operand unpacking -----------------------------------------------------
+
+// Tile i of a lane's value chunk as the B operand (token pairs (r, r+4)).
+template <int VF>
+__device__ __forceinline__ half8 unpack_v(const u32* w, int i) {
+  if constexpr (VF == INT4) {
+    const u32 x = w[i];
+    return pack8(unmagic((x & 0x000F000Fu) | kMagic), unmagic(((x >> 4) & 0x000F000Fu) | kMagic),
+                 unmagic(((x >> 8) & 0x000F000Fu) | kMagic), unmagic(((x >> 12) & 0x000F000Fu) | kMagic));
+  } else if constexpr (VF == INT2) {
+    // word i = 16 bits at half (i & 1) of dword i/2; token k at bit 2k
+    const u32 x = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const u32 y = (x & 0xFFu) | ((x & 0xFF00u) << 8);       // tokens 0..3 low half, 4..7 high half
+    return pack8(unmagic((y & 0x00030003u) | kMagic), unmagic(((y >> 2) & 0x00030003u) | kMagic),
+                 unmagic(((y >> 4) & 0x00030003u) | kMagic), unmagic(((y >> 6) & 0x00030003u) | kMagic));
+  } else if constexpr (VF == INT8) {
+    const u32 d0 = w[2 * i], d1 = w[2 * i + 1];
+    u32 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = unmagic((((d0 >> (8 * k)) & 0xFFu) | (((d1 >> (8 * k)) & 0xFFu) << 16)) | kMagic);
+    return pack8(r[0], r[1], r[2], r[3]);
+  } else {  // FP8
+    const u32 d0 = w[2 * i], d1 = w[2 * i + 1];
+    const u32 y0 = (d0 & 0xFFu) | ((d1 & 0xFFu) << 8) | ((d0 & 0xFF00u) << 8) | ((d1 & 0xFF00u) << 16);
+    const u32 y1 = ((d0 >> 16) & 0xFFu) | ((d1 >> 8) & 0xFF00u) | ((d0 >> 8) & 0xFF0000u) | (d1 & 0xFF000000u);
+    return pack8(h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 1.0f, false)),
+                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 1.0f, true)),
+                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 1.0f, false)),
+                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 1.0f, true)));
+  }
+}
+
+// fp16 window values: word i = 8 fp16 (tokens 0..7) in dwords 4i..4i+3.
+__device__ __forceinline__ half8 unpack_v_f16(const u32* w, int i) {
+  const u32 a = w[4 * i], b = w[4 * i + 1], c = w[4 * i + 2], d = w[4 * i + 3];
+  return pack8((a & 0xFFFFu) | (c << 16), (a >> 16) | (c & 0xFFFF0000u),
+               (b & 0xFFFFu) | (d << 16), (b >> 16) | (d & 0xFFFF0000u));
+}
+
+// keep only fp16 halves whose token is valid (bit k of `valid` = token k of 8)
+__device__ __forceinline__ half8 mask_tokens(half8 h, u32 valid) {
+  union { half8 h; u32 u[4]; } x;
+  x.h = h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32 m = ((valid >> r) & 1u ? 0x0000FFFFu : 0u) | ((valid >> (r + 4)) & 1u ? 0xFFFF0000u : 0u);
+    x.u[r] &= m;
+  }
+  return x.h;
+}
+
+template <int N>
+__device__ __forceinline__ void load_dw(const uint8_t* p, u32* w) {
+  if constexpr (N == 2) {
+    const uint2 v = *(const uint2*)p;
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 v = ((const uint4*)p)[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_max16(float x) {   // max over lanes n, n+16, n+32, n+48
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_sum16(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+}  // namespace mf
+
+using namespace mf;
+
+// One decode-attention pass-1 work-group.  KF/VF: key/value code format;
+// ROPE: keys cached before RoPE; VG: value channel groups (INT values);
+// KSPLIT: rotated keys enter the matrix unit as hi + lo fp16 halves.
+// D = 128, n_rep <= 8.
+template <int KF, int VF, bool ROPE, int VG, bool KSPLIT>
+__global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
+  constexpr int D = 128;
+  constexpr int KB = Bits<KF>::v, VB = Bits<VF>::v;
+  constexpr int KDW = KB;                 // dwords of key data per lane (32 channels)
+  constexpr int VDW = 2 * VB;             // dwords of value data per lane per 32-token block
+  constexpr bool KINT = KF != FP8, VINT = VF != FP8;
+  constexpr int VGC = D / VG;             // value channels per group
+
+  __shared__ float q_s[8][D];
+  __shared__ float2 fine_s[ROPE ? 32 : 1][ROPE ? 64 : 1];
+  __shared__ float red_o[kWaves][8][D];
+  __shared__ float red_ml[kWaves][8][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int n_rep = p.n_rep;
+  const int64_t bh = (int64_t)b * p.Hkv + kvh;
+  const uint8_t* arena = a.arena;
+
+  for (int e = tid; e < n_rep * D; e += 256) {
+    const int r = e / D, c = e % D;
+    q_s[r][c] = load_in(a.q, ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c, p.in_dtype);
+  }
+  if constexpr (ROPE) {
+    const float2* tab = (const float2*)(arena + p.rope);
+    for (int e = tid; e < 32 * 64; e += 256) fine_s[e >> 6][e & 63] = tab[e];
+  }
+  __syncthreads();
+
+  // token range of this split and of this wavefront
+  const int64_t lo = (int64_t)split * a.chunk;
+  const int64_t hi = lo + a.chunk < a.T ? lo + a.chunk : a.T;
+  const int64_t q_end = hi < a.Tq ? hi : a.Tq;                 // quantized part [lo, q_end)
+  const int64_t w_beg = lo > a.Tq ? lo : a.Tq;                 // window part [w_beg, hi)
+  const int64_t nq = q_end > lo ? (q_end - lo + 31) / 32 : 0;  // quantized steps
+  const int64_t s_w0 = w_beg & ~(int64_t)31;
+  const int64_t nw = hi > w_beg ? (hi - s_w0 + 31) / 32 : 0;   // window steps
+  const int64_t nsteps = nq + nw;
+  const int64_t per_wave = (nsteps + kWaves - 1) / kWaves;
+  const int64_t st_beg = wave * per_wave;
+  const int64_t st_end = st_beg + per_wave < nsteps ? st_beg + per_wave : nsteps;
+
+  // query columns: n < n_rep -> hi half of head n, n_rep <= n < 2 n_rep -> lo half
+  const int head = n < n_rep ? n : (n < 2 * n_rep ? n - n_rep : 0);
+  const bool is_hi = n < n_rep;
+  const bool is_col = n < 2 * n_rep;
+  const float qs = a.qscale;
+
+  half8 Bq[4];          // query operand of the current key group / window
+  float kbias = 0.0f;   // per-column logit bias from the key zero-points
+  int64_t cur_grp = -1;
+  int b_mode = -1;      // 0: quantized keys, 1: window keys
+
+  // Bq for per-channel factors sc (or 1); returns this lane's part of sum_c q_c z_c
+  auto build_b = [&](const float* sc, const float* zc, float uniform, bool natural) {
+    float qz = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32 r[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float v2[2];
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int e = 2 * e2 + hlf;
+          const int cl = natural ? 8 * j + e : kslot<KF, ROPE>(j, e);
+          const float qv = q_s[head][32 * g + cl] * qs;
+          const float full = qv * (sc ? sc[cl] : uniform);
+          const float h = (float)(_Float16)full;
+          const float v = is_hi ? h : (float)(_Float16)(full - h);
+          v2[hlf] = is_col ? v : 0.0f;
+          if (zc) qz += qv * zc[cl];
+        }
+        r[e2] = pk_f16(v2[0], v2[1]);
+      }
+      Bq[j] = pack8(r[0], r[1], r[2], r[3]);
+    }
+    return is_hi ? qz : 0.0f;
+  };
+
+  // softmax / output state (lane (n, g): head n for n < n_rep)
+  float m_run = kNegBig, l_run = 0.0f;
+  float vbias[VG];
+#pragma unroll
+  for (int i = 0; i < VG; ++i) vbias[i] = 0.0f;
+  floatx4 O[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const float2* coarse = ROPE ? (const float2*)(arena + p.rope) + 32 * 64 : nullptr;
+  const float* kscale = (const float*)(arena + p.k.scale);
+  const float* kzero = KINT ? (const float*)(arena + p.k.zero) : nullptr;
+
+  // One 32-token step: tokens [t0, t0 + 32), valid within [v_lo, v_hi).
+  // RING: the tokens come from the fp16 window instead of the quantized cache.
+  auto step = [&](auto ring_tag, int64_t t0, int64_t v_lo, int64_t v_hi) {
+    constexpr bool RING = decltype(ring_tag)::value;
+    const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
+
+    // ---- issue the step's code loads ----------------------------------------------
+    constexpr int KW = RING ? 16 : KDW;
+    constexpr int VW = RING ? 32 : VDW;
+    u32 kw0[KW], kw1[KW], vw[VW];
+    if constexpr (!RING) {
+      const uint8_t* kb = arena + p.k.codes + (bh * p.Tc + t0 + tok_in0) * (D * KB / 8) + g * (4 * KDW);
+      load_dw<KDW>(kb, kw0);
+      load_dw<KDW>(kb + 4 * (D * KB / 8), kw1);
+      load_dw<VDW>(arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * (32 * D * VB / 8) + lane * (4 * VDW), vw);
+    } else {
+      load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0) % p.Rs)) * D + 32 * g) * 2, kw0);
+      load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0 + 4) % p.Rs)) * D + 32 * g) * 2, kw1);
+      load_dw<32>(arena + p.ring_v + (bh * (p.Rs / 32) + ((t0 % p.Rs) >> 5)) * (32 * D * 2) + lane * 128, vw);
+    }
+
+    // ---- query operand of this step ---------------------------------------------
+    if constexpr (!RING) {
+      if constexpr (KINT && !ROPE) {
+        const int64_t grp = t0 / p.k.group;
+        if (b_mode != 0 || grp != cur_grp) {
+          const float* sc = kscale + (bh * p.k.meta_rows + grp) * D + 32 * g;
+          const float* zc = kzero + (bh * p.k.meta_rows + grp) * D + 32 * g;
+          kbias = wave_sum16(build_b(sc, zc, 1.0f, false));
+          cur_grp = grp;
+          b_mode = 0;
+        }
+      } else if (b_mode != 0) {
+        const float ks = (KF == FP8) ? kscale[kvh] : 1.0f;
+        build_b(nullptr, nullptr, ks, true);
+        kbias = 0.0f;
+        b_mode = 0;
+      }
+    } else if (b_mode != 1) {
+      build_b(nullptr, nullptr, 1.0f, true);
+      kbias = 0.0f;
+      b_mode = 1;
+    }
+
+    // ---- S^T = K . Q^T for the two 16-token tiles ----------------------------
+    floatx4 S[2];
+    if constexpr (ROPE) {
+      const float* sc = RING ? nullptr : kscale + (bh * p.k.meta_rows + t0 / p.k.group) * D + 32 * g;
+      const float* zc = RING ? nullptr : kzero + (bh * p.k.meta_rows + t0 / p.k.group) * D + 32 * g;
+      const float2* crow = coarse + (t0 >> 5) * 64 + 16 * g;
+      floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // this k-step's 8 channels: scale / zero and coarse angles
+        float s8[8], z8[8];
+        if constexpr (!RING) {
+          const float4 sa = ((const float4*)sc)[2 * j], sb = ((const float4*)sc)[2 * j + 1];
+          const float4 za = ((const float4*)zc)[2 * j], zb = ((const float4*)zc)[2 * j + 1];
+          s8[0] = sa.x; s8[1] = sa.y; s8[2] = sa.z; s8[3] = sa.w; s8[4] = sb.x; s8[5] = sb.y; s8[6] = sb.z; s8[7] = sb.w;
+          z8[0] = za.x; z8[1] = za.y; z8[2] = za.z; z8[3] = za.w; z8[4] = zb.x; z8[5] = zb.y; z8[6] = zb.z; z8[7] = zb.w;
+        }
+        const float4 ca = ((const float4*)crow)[2 * j], cb = ((const float4*)crow)[2 * j + 1];
+        const float2 cc[4] = {make_float2(ca.x, ca.y), make_float2(ca.z, ca.w), make_float2(cb.x, cb.y),
+                              make_float2(cb.z, cb.w)};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32* w = u ? kw1 : kw0;
+          const int dt = tok_in0 + 4 * u;               // token offset in the step (t0 is 32-aligned)
+          u32 r[4], rl[4];
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const int e = 8 * j + 2 * pr;
+            float k0, k1;
+            if constexpr (!RING) {
+              k0 = (float)kcode<KF>(w, e) * s8[2 * pr] + z8[2 * pr];
+              k1 = (float)kcode<KF>(w, e + 1) * s8[2 * pr + 1] + z8[2 * pr + 1];
+            } else {
+              k0 = lo_f(w[e >> 1]);
+              k1 = hi_f(w[e >> 1]);
+            }
+            const float2 ff = fine_s[dt][16 * g + (e >> 1)];
+            const float cs = cc[pr].x * ff.x - cc[pr].y * ff.y;
+            const float sn = cc[pr].y * ff.x + cc[pr].x * ff.y;
+            const float r0 = k0 * cs - k1 * sn, r1 = k0 * sn + k1 * cs;
+            r[pr] = pk_f16(r0, r1);
+            if constexpr (KSPLIT) rl[pr] = pk_f16(r0 - lo_f(r[pr]), r1 - hi_f(r[pr]));
+          }
+          floatx4& acc = u ? acc1 : acc0;
+          acc = mfma(pack8(r[0], r[1], r[2], r[3]), Bq[j], acc);
+          if constexpr (KSPLIT) acc = mfma(pack8(rl[0], rl[1], rl[2], rl[3]), Bq[j], acc);
+        }
+      }
+      S[0] = acc0;
+      S[1] = acc1;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32* w = u ? kw1 : kw0;
+        half8 A[4];
+        if constexpr (RING) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) A[j] = pack8(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+        } else if constexpr (KF == FP8) {
+          unpack_k_fp8(w, A);
+        } else {
+          unpack_k_magic<KF>(w, A);
+        }
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma(A[j], Bq[j], acc);
+        S[u] = acc;
+      }
+    }
+
+    // ---- logits of lane (n, g): head n, tokens 8g + k -------------------------
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = S[u][i] + kbias;
+        const float other = __shfl_down(v, n_rep, 16);      // lo column of the same head
+        x[4 * u + i] = v + other;
+      }
+    }
+    u32 valid = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t t = t0 + 8 * g + k;
+      const bool ok = t >= v_lo && t < v_hi && n < n_rep;
+      valid |= (ok ? 1u : 0u) << k;
+      if (!ok) x[k] = kNegBig;
+    }
+
+    // ---- online softmax ----------------------------------------------------------
+    float mx = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
+    mx = wave_max16(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float pk[8], psum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pk[k] = ((valid >> k) & 1u) ? exp2f(x[k] - m_new) : 0.0f;
+      psum += pk[k];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < VG; ++i) vbias[i] *= alpha;
+    {   // rescale O: lane (c, g') holds rows (heads) 4g'+i
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 15, 64);
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[t8][i] *= al[i];
+    }
+
+    // ---- PV -------------------------------------------------------------------------
+    if constexpr (!RING && VINT) {
+      // A = p * s (hi and lo fp16 halves), z enters through the per-group bias.
+      // Only lanes that own a query head read the per-token scale / zero.
+      const float* vsp = (const float*)(arena + p.v.scale) + (bh * p.Tc + t0 + 8 * g) * VG;
+      const float* vzp = (const float*)(arena + p.v.zero) + (bh * p.Tc + t0 + 8 * g) * VG;
+      half8 Ah[VG], Al[VG];
+#pragma unroll
+      for (int gr = 0; gr < VG; ++gr) {
+        float sv[8], zv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { sv[k] = 0.0f; zv[k] = 0.0f; }
+        if (n < n_rep) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) { sv[k] = vsp[k * VG + gr]; zv[k] = vzp[k * VG + gr]; }
+        }
+        u32 rh[4], rl[4];
+        float zsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float av[2];
+#pragma unroll
+          for (int hlf = 0; hlf < 2; ++hlf) {
+            const int k = i + 4 * hlf;
+            const bool ok = (valid >> k) & 1u;
+            av[hlf] = ok ? pk[k] * sv[k] : 0.0f;
+            zsum += ok ? pk[k] * zv[k] : 0.0f;
+          }
+          rh[i] = pk_f16(av[0], av[1]);
+          rl[i] = pk_f16(av[0] - lo_f(rh[i]), av[1] - hi_f(rh[i]));
+        }
+        Ah[gr] = pack8(rh[0], rh[1], rh[2], rh[3]);
+        Al[gr] = pack8(rl[0], rl[1], rl[2], rl[3]);
+        vbias[gr] += zsum;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const half8 bv = unpack_v<VF>(vw, i);
+        O[i] = mfma(Ah[(16 * i) / VGC], bv, O[i]);
+        O[i] = mfma(Al[(16 * i) / VGC], bv, O[i]);
+      }
+    } else {
+      // FP8 values: A = p * v_scale; window values: A = p
+      const u32 vv = __shfl(valid, 16 * g, 64);   // validity of the B lane's tokens 8g..8g+7
+      const float vsc = (!RING && VF == FP8) ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
+      u32 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = pk_f16(pk[i] * vsc, pk[i + 4] * vsc);
+      const half8 Ap = pack8(r[0], r[1], r[2], r[3]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // invalid tokens' bytes may not be finite values: zero them
+        half8 bv;
+        if constexpr (RING) bv = unpack_v_f16(vw, i);
+        else bv = unpack_v<VF>(vw, i);
+        O[i] = mfma(Ap, mask_tokens(bv, vv), O[i]);
+      }
+    }
+  };
+
+  const int64_t qs_end = st_end < nq ? st_end : nq;
+  for (int64_t st = st_beg; st < qs_end; ++st) step(std::false_type{}, lo + st * 32, lo, q_end);
+  for (int64_t st = (st_beg > nq ? st_beg : nq); st < st_end; ++st)
+    step(std::true_type{}, s_w0 + (st - nq) * 32, w_beg, hi);
+
+  // ---- combine the wavefronts of the work-group ------------------------------------
+  l_run = wave_sum16(l_run);
+#pragma unroll
+  for (int i = 0; i < VG; ++i) vbias[i] = wave_sum16(vbias[i]);
+  if (g == 0 && n < n_rep) {
+    red_ml[wave][n][0] = m_run;
+    red_ml[wave][n][1] = l_run;
+  }
+  // O rows -> LDS with the value bias of the channel's group added.  Row r of
+  // this lane is head 4g + r; its per-group bias lives in lane (4g + r) mod 16.
+  float rbias[4][VG];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q2 = 0; q2 < VG; ++q2) rbias[r][q2] = __shfl(vbias[q2], (4 * g + r) & 15, 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = 16 * i + n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hrow = 4 * g + r;
+      if (hrow < n_rep) red_o[wave][hrow][c] = O[i][r] + (VINT ? rbias[r][(16 * i) / VGC] : 0.0f);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < n_rep * D; e += 256) {
+    const int r = e / D, c = e % D;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][r][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2f(red_ml[w][r][0] - M);
+      L += f * red_ml[w][r][1];
+      acc += f * red_o[w][r][c];
+    }
+    const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + r;
+    a.ws_o[(hq * a.S + split) * D + c] = acc;
+    if (c == 0) {
+      a.ws_ml[(hq * a.S + split) * 2 + 0] = M;
+      a.ws_ml[(hq * a.S + split) * 2 + 1] = L;
+    }
+  }
+}
+
+// ---- dispatch ---------------------------------------------------------------------------
+
+static int kfmt(const Plan& p) {
+  if (p.k.scheme == KVQ_FP8_E4M3) return FP8;
+  if (p.k.scheme == KVQ_INT_ASYM && p.k.axis == KVQ_PER_CHANNEL && p.k.group > 0 && p.k.group % 32 == 0)
+    return p.k.bits;
+  return -1;
+}
+static int vfmt(const Plan& p) {
+  if (p.v.scheme == KVQ_FP8_E4M3) return FP8;
+  if (p.v.scheme == KVQ_INT_ASYM && p.v.axis == KVQ_PER_TOKEN && p.v.group >= 16) return p.v.bits;
+  return -1;
+}
+
 bool mfma_supported(const Plan& p) {
-  (void)p;
-  return false;
+  if (p.D != 128 || p.n_rep > 8) return false;
+  const int kf = kfmt(p), vf = vfmt(p);
+  if (kf < 0 || vf < 0) return false;
+  if (p.pre_rope && kf == FP8) return false;
+  return true;
+}
+
+static int vgroups(const Plan& p) { return p.v.scheme == KVQ_FP8_E4M3 ? 1 : 128 / p.v.group; }
+
+template <int KF, int VF, int VG>
+static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
+  if (p.pre_rope) {
+    if constexpr (KF != FP8) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true>), grid, dim3(256), 0, s, p, a);
+  } else {
+    hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false>), grid, dim3(256), 0, s, p, a);
+  }
+}
+
+template <int KF, int VF>
+static void launch_kv(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
+  if constexpr (VF == FP8) {
+    launch_kvg<KF, VF, 1>(p, grid, s, a);
+  } else {
+    switch (vgroups(p)) {
+      case 1: launch_kvg<KF, VF, 1>(p, grid, s, a); break;
+      case 2: launch_kvg<KF, VF, 2>(p, grid, s, a); break;
+      case 4: launch_kvg<KF, VF, 4>(p, grid, s, a); break;
+      default: launch_kvg<KF, VF, 8>(p, grid, s, a); break;
+    }
+  }
+}
+
+template <int KF>
+static void launch_k(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
+  switch (vfmt(p)) {
+    case INT2: launch_kv<KF, INT2>(p, grid, s, a); break;
+    case INT4: launch_kv<KF, INT4>(p, grid, s, a); break;
+    case INT8: launch_kv<KF, INT8>(p, grid, s, a); break;
+    default: launch_kv<KF, FP8>(p, grid, s, a); break;
+  }
 }
 
 hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
                                  float sm_scale, void* ws, hipStream_t s) {
-  (void)p; (void)ap; (void)arena; (void)q; (void)sm_scale; (void)ws; (void)s;
-  return hipErrorInvalidValue;
+  Args a{(const uint8_t*)arena, q, (float*)((uint8_t*)ws + ap.ws_o), (float*)((uint8_t*)ws + ap.ws_ml),
+         ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e};
+  dim3 grid(ap.splits, p.Hkv, p.B);
+  switch (kfmt(p)) {
+    case INT2: launch_k<INT2>(p, grid, s, a); break;
+    case INT4: launch_k<INT4>(p, grid, s, a); break;
+    case INT8: launch_k<INT8>(p, grid, s, a); break;
+    default: launch_k<FP8>(p, grid, s, a); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -184,3 +184,15 @@ def test_quantized_tokens_matches_oracle(k, v, R):
         assert K.kvq_quantized_tokens(cfg, T) == OC.quantized_tokens(ocfg, T)
     with pytest.raises(K.KvqError):
         K.kvq_quantized_tokens(cfg, 5001)
+
+
+@pytest.mark.parametrize("fmt", [dict(), dict(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0), residual=0)])
+def test_workspace_monotone_in_T(fmt):
+    for B, H in [(1, 8), (2, 2), (32, 8)]:
+        cfg = _cfg(batch=B, num_kv_heads=H, num_q_heads=4 * H, max_tokens=140000, **fmt)
+        prev = 0
+        for T in list(range(1, 2000, 13)) + [8193, 32769, 131072, 131136, 140000]:
+            for kern in (1,):
+                ws = K.kvq_workspace_bytes(cfg, T, kern)
+                assert ws >= prev
+                prev = ws

@@ -59,7 +59,7 @@ def _schedule(kind, T):
     return sched
 
 
-def run_case(case: Case, T: int, schedule, seed=0, kernels=(K.KERNEL_GENERIC,), fp8_mode="calibrate",
+def run_case(case: Case, T: int, schedule, seed=0, kernels=None, fp8_mode="calibrate",
              num_splits=0):
     say(f"[case] {case} T={T} sched={schedule[:4]}... seed={seed}")
     (Kf, Kp), (Vf, Vp) = W.random_case(seed, case.B, case.Hkv, T, case.D, dtype=case.dtype)
@@ -84,6 +84,13 @@ def run_case(case: Case, T: int, schedule, seed=0, kernels=(K.KERNEL_GENERIC,), 
                            calibrate_tokens=schedule[0] if (fp8 and fp8_mode == "calibrate") else 0)
     compare_sections(gc, st)
     compare_dequant(gc, st)
+    if kernels is None:
+        kernels = [K.KERNEL_GENERIC]
+        try:
+            K.kvq_workspace_bytes(gc.cfg, T, K.KERNEL_MFMA)
+            kernels.append(K.KERNEL_MFMA)
+        except K.KvqError:
+            pass
     errs = {}
     for kern in kernels:
         out = gc.attention(qp, kernel=kern, num_splits=num_splits)
@@ -168,5 +175,6 @@ def test_attention_deterministic_and_split_invariant():
     b = gc.attention(qp)
     assert np.array_equal(a, b)
     for s in (1, 3, 16):
-        o = gc.attention(qp, num_splits=s, kernel=K.KERNEL_GENERIC)
-        assert attention_error(o, qf, st, case) <= ATTN_TOL
+        for kern in (K.KERNEL_GENERIC, K.KERNEL_MFMA):
+            o = gc.attention(qp, num_splits=s, kernel=kern)
+            assert attention_error(o, qf, st, case) <= ATTN_TOL

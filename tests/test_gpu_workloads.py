@@ -191,7 +191,11 @@ def test_large_attention(large):
             err = OA.max_rel_l2_per_head(got, ref)
             say(f"[{L['name']}] (b={b}, h={h}) kernel={kern} max rel-L2 {err:.2e}")
             assert err <= ATTN_TOL
-    if len(outs) > 1:   # kernels agree everywhere, not only on the samples
+    if len(outs) > 1:
+        # every head, not only the samples: the generic kernel is within ~1e-5 of
+        # the oracle, so its distance to the MFMA kernel bounds the latter's error
         o1, o2 = outs[K.KERNEL_GENERIC], outs[K.KERNEL_MFMA]
         rel = np.linalg.norm(o1 - o2, axis=-1) / np.linalg.norm(o1, axis=-1)
-        assert rel.max() <= 2 * ATTN_TOL
+        say(f"[{L['name']}] MFMA vs generic over all {rel.size} heads: max {rel.max():.2e} "
+            f"mean {rel.mean():.2e} p99 {np.percentile(rel, 99):.2e}")
+        assert rel.max() <= ATTN_TOL

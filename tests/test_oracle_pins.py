@@ -382,3 +382,12 @@ def test_window_holds_fp16_values():
     assert np.array_equal(st["k_window"], x[:, :, tq:].astype(np.float16))
     mn = x[0, 0, :32, 0].astype(np.float16).astype(np.float32).min()
     assert st["k"]["zero"][0, 0, 0, 0] == mn
+
+
+@pytest.mark.parametrize("spec", [C.Spec(C.INT_ASYM, 2, C.PER_CHANNEL, 32), C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 32),
+                                  C.Spec(C.INT_SYM, 8, C.PER_TENSOR, 0), C.Spec(C.INT_SYM, 8, C.PER_CHANNEL, 0),
+                                  C.Spec(C.FP8_E4M3, 8, 0, 0), C.Spec(C.NONE, 16, 0, 0)])
+def test_dequantize_part_rebuilds_values(spec):
+    (K, _), _ = W.random_case(8, 2, 2, 64, 32)
+    part = C.quantize_part(K, spec, np.array([0.5, 2.0], np.float32))
+    assert np.array_equal(C.dequantize_part(part, spec), part["deq"])
