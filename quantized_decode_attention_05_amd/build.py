@@ -22,7 +22,8 @@ SOURCES = {
     "kvq_api.hip": [],
     "kvq_quant.hip": ["-ffp-contract=off"],
     "kvq_attn.hip": [],
-    "kvq_attn_mfma.hip": [],
+    # keep MFMA accumulators in VGPRs (no AGPR <-> VGPR copies around the softmax rescale)
+    "kvq_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 COMMON = [

@@ -158,25 +158,60 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
 }
 
 // Pass 2: one block per (query head, sequence), one thread per channel.
-__global__ void attn_merge(Plan p, const float* ws_o, const float* ws_ml, int S, void* out) {
-  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+// M = max_s m_s and L = sum_s 2^(m_s - M) l_s by block reductions; the split
+// weights are staged in LDS so the channel loop streams the partials.
+__global__ void __launch_bounds__(128) attn_merge(Plan p, const float* ws_o, const float* ws_ml, int S,
+                                                  void* out) {
+  __shared__ float red[128];
+  __shared__ float wts[256];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int nt = blockDim.x;
   const int64_t row = (int64_t)b * p.Hq + hq;
   const float* ml = ws_ml + row * S * 2;
   float M = kNegBig;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float w = exp2f(ml[2 * s] - M);
-    L += w * ml[2 * s + 1];
-    acc += w * ws_o[(row * S + s) * p.D + c];
+  for (int s = tid; s < S; s += nt) M = fmaxf(M, ml[2 * s]);
+  red[tid] = M;
+  __syncthreads();
+  for (int w = nt / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
   }
-  const float v = acc / L;
-  const int64_t oi = row * p.D + c;
-  if (p.out_dtype == KVQ_F32) ((float*)out)[oi] = v;
-  else if (p.out_dtype == KVQ_F16) ((_Float16*)out)[oi] = (_Float16)v;
-  else {
-    const uint32_t u = __float_as_uint(v);
-    ((uint16_t*)out)[oi] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  M = red[0];
+  __syncthreads();
+  float L = 0.0f;
+  for (int s = tid; s < S; s += nt) L += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
+  red[tid] = L;
+  __syncthreads();
+  for (int w = nt / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  L = red[0];
+  // every thread walks the split chunks (the barriers must be uniform); threads
+  // c < D accumulate channel c
+  const int c = tid;
+  const bool active = c < p.D;
+  float acc = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 256) {
+    const int n = S - s0 < 256 ? S - s0 : 256;
+    __syncthreads();
+    for (int j = tid; j < n; j += nt) wts[j] = exp2f(ml[2 * (s0 + j)] - M);
+    __syncthreads();
+    if (active) {
+      const float* o = ws_o + (row * S + s0) * p.D + c;
+#pragma unroll 8
+      for (int j = 0; j < n; ++j) acc += wts[j] * o[(int64_t)j * p.D];
+    }
+  }
+  if (active) {
+    const float v = acc / L;
+    const int64_t oi = row * p.D + c;
+    if (p.out_dtype == KVQ_F32) ((float*)out)[oi] = v;
+    else if (p.out_dtype == KVQ_F16) ((_Float16*)out)[oi] = (_Float16)v;
+    else {
+      const uint32_t u = __float_as_uint(v);
+      ((uint16_t*)out)[oi] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
   }
 }
 
@@ -197,10 +232,11 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
   const int64_t unit = 64;
   const int64_t max_splits = cdiv(T, unit);
   if (splits == 0) {
-    // enough work-groups to cover the 256 CUs a few times over
+    // about two work-groups per CU (the MFMA kernel runs at two waves per
+    // SIMD), each with a long run of tokens per wavefront
     const int64_t bh = (int64_t)p.B * p.Hkv;
-    const int64_t want = cdiv(1024, bh);
-    const int64_t min_tokens = (kernel == 2) ? 256 : 128;
+    const int64_t want = cdiv(kernel == 2 ? 512 : 1024, bh);
+    const int64_t min_tokens = (kernel == 2) ? 512 : 128;
     const int64_t by_len = cdiv(T, min_tokens);
     splits = (int)(want < by_len ? want : by_len);
   }
@@ -240,7 +276,7 @@ hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena
     if (p.D == 128) hipLaunchKernelGGL(attn_generic<128>, grid, dim3(256), 0, s, p, a);
     else hipLaunchKernelGGL(attn_generic<64>, grid, dim3(256), 0, s, p, a);
   }
-  hipLaunchKernelGGL(attn_merge, dim3(p.Hq, p.B), dim3(p.D), 0, s, p, (const float*)ws_o,
+  hipLaunchKernelGGL(attn_merge, dim3(p.Hq, p.B), dim3(128), 0, s, p, (const float*)ws_o,
                      (const float*)ws_ml, ap.splits, out);
   return hipGetLastError();
 }

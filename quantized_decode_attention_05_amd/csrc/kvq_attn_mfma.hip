@@ -43,6 +43,15 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32;
 
+// Tuning knobs: quantized steps whose loads are issued together, and the
+// wavefronts per SIMD the register allocation must allow (0: compiler's choice).
+#ifndef KVQ_MFMA_STEPS_IN_FLIGHT
+#define KVQ_MFMA_STEPS_IN_FLIGHT 2
+#endif
+#ifndef KVQ_MFMA_WAVES_PER_EU
+#define KVQ_MFMA_WAVES_PER_EU 0
+#endif
+
 namespace mf {
 
 constexpr float kNegBig = -1.0e30f;
@@ -142,6 +151,36 @@ __device__ __forceinline__ void unpack_k_fp8(const u32* w, half8* A) {
   }
 }
 
+// Exact fp16 codes of a lane's 32 key channels as 16 half2 registers; channel
+// e sits in register code_reg<KF>(e), half code_half<KF>(e).
+template <int KF>
+__device__ __forceinline__ void key_codes_f16(const u32* w, u32* h) {
+  if constexpr (KF == INT2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[8 * d + i] = unmagic(((w[d] >> (2 * i)) & 0x00030003u) | kMagic);
+  } else if constexpr (KF == INT4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[4 * d + i] = unmagic(((w[d] >> (4 * i)) & 0x000F000Fu) | kMagic);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32 src = w[i >> 1];
+      const int sh = 16 * (i & 1);
+      h[i] = unmagic((((src >> sh) & 0xFFu) | (((src >> (sh + 8)) & 0xFFu) << 16)) | kMagic);
+    }
+  }
+}
+template <int KF> __device__ constexpr int code_reg(int e) {
+  return KF == INT2 ? 8 * (e >> 4) + (e & 7) : (KF == INT4 ? 4 * (e >> 3) + (e & 3) : e >> 1);
+}
+template <int KF> __device__ constexpr int code_half(int e) {
+  return KF == INT2 ? (e >> 3) & 1 : (KF == INT4 ? (e >> 2) & 1 : e & 1);
+}
+
 // Integer code of channel e (0..31) of a lane's key data.
 template <int KF>
 __device__ __forceinline__ u32 kcode(const u32* w, int e) {
@@ -224,6 +263,17 @@ __device__ __forceinline__ float wave_sum16(float x) {
   return x + __shfl_xor(x, 32, 64);
 }
 
+// Per-lane data of one 32-token step (codes and per-token value scale / zero).
+template <int KW, int VW, int NVM>
+struct StepData {
+  u32 k0[KW], k1[KW], v[VW];
+  float vs[NVM], vz[NVM];
+  __device__ void zero_meta() {
+#pragma unroll
+    for (int i = 0; i < NVM; ++i) { vs[i] = 0.0f; vz[i] = 0.0f; }
+  }
+};
+
 }  // namespace mf
 
 using namespace mf;
@@ -233,7 +283,11 @@ using namespace mf;
 // KSPLIT: rotated keys enter the matrix unit as hi + lo fp16 halves.
 // D = 128, n_rep <= 8.
 template <int KF, int VF, bool ROPE, int VG, bool KSPLIT>
-__global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
+__global__ void __launch_bounds__(256)
+#if KVQ_MFMA_WAVES_PER_EU > 0
+__attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)))
+#endif
+attn_mfma(Plan p, Args a) {
   constexpr int D = 128;
   constexpr int KB = Bits<KF>::v, VB = Bits<VF>::v;
   constexpr int KDW = KB;                 // dwords of key data per lane (32 channels)
@@ -242,7 +296,9 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
   constexpr int VGC = D / VG;             // value channels per group
 
   __shared__ float q_s[8][D];
-  __shared__ float2 fine_s[ROPE ? 32 : 1][ROPE ? 64 : 1];
+  // fine RoPE table, pair-major with the token offset XOR-swizzled by the
+  // lane row so that one row's 16 lanes (16 offsets, one pair) hit distinct banks
+  __shared__ float2 fine_s[ROPE ? 64 : 1][ROPE ? 32 : 1];
   __shared__ float red_o[kWaves][8][D];
   __shared__ float red_ml[kWaves][8][2];
 
@@ -259,7 +315,10 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
   }
   if constexpr (ROPE) {
     const float2* tab = (const float2*)(arena + p.rope);
-    for (int e = tid; e < 32 * 64; e += 256) fine_s[e >> 6][e & 63] = tab[e];
+    for (int e = tid; e < 32 * 64; e += 256) {
+      const int dlt = e >> 6, pr = e & 63;
+      fine_s[pr][dlt ^ (4 * ((pr >> 4) & 3))] = tab[e];
+    }
   }
   __syncthreads();
 
@@ -276,42 +335,55 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
   const int64_t st_beg = wave * per_wave;
   const int64_t st_end = st_beg + per_wave < nsteps ? st_beg + per_wave : nsteps;
 
-  // query columns: n < n_rep -> hi half of head n, n_rep <= n < 2 n_rep -> lo half
-  const int head = n < n_rep ? n : (n < 2 * n_rep ? n - n_rep : 0);
-  const bool is_hi = n < n_rep;
-  const bool is_col = n < 2 * n_rep;
+  // query columns: column n < n_rep is head n (hi and lo fp16 halves of the
+  // fp32 query in two operands); other columns are zero
+  const int head = n < n_rep ? n : 0;
+  const bool is_col = n < n_rep;
   const float qs = a.qscale;
 
-  half8 Bq[4];          // query operand of the current key group / window
+  half8 Bq[4], Bl[4];   // query operand (hi, lo) of the current key group / window
   float kbias = 0.0f;   // per-column logit bias from the key zero-points
   int64_t cur_grp = -1;
   int b_mode = -1;      // 0: quantized keys, 1: window keys
 
-  // Bq for per-channel factors sc (or 1); returns this lane's part of sum_c q_c z_c
+  // Bq/Bl for per-channel factors sc (or a uniform factor); returns this
+  // lane's part of sum_c q_c z_c
   auto build_b = [&](const float* sc, const float* zc, float uniform, bool natural) {
     float qz = 0.0f;
+    // this lane's 32 channel scales / zero-points, fetched with wide loads up front
+    float sv[32], zv[32];
+    if (sc) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 a4 = ((const float4*)sc)[i], b4 = ((const float4*)zc)[i];
+        sv[4 * i] = a4.x; sv[4 * i + 1] = a4.y; sv[4 * i + 2] = a4.z; sv[4 * i + 3] = a4.w;
+        zv[4 * i] = b4.x; zv[4 * i + 1] = b4.y; zv[4 * i + 2] = b4.z; zv[4 * i + 3] = b4.w;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32 r[4];
+      u32 rh[4], rl[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        float v2[2];
+        float vh[2], vl[2];
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
           const int e = 2 * e2 + hlf;
           const int cl = natural ? 8 * j + e : kslot<KF, ROPE>(j, e);
           const float qv = q_s[head][32 * g + cl] * qs;
-          const float full = qv * (sc ? sc[cl] : uniform);
+          const float full = qv * (sc ? sv[cl] : uniform);
           const float h = (float)(_Float16)full;
-          const float v = is_hi ? h : (float)(_Float16)(full - h);
-          v2[hlf] = is_col ? v : 0.0f;
-          if (zc) qz += qv * zc[cl];
+          vh[hlf] = is_col ? h : 0.0f;
+          vl[hlf] = is_col ? full - h : 0.0f;
+          if (sc) qz += qv * zv[cl];
         }
-        r[e2] = pk_f16(v2[0], v2[1]);
+        rh[e2] = pk_f16(vh[0], vh[1]);
+        rl[e2] = pk_f16(vl[0], vl[1]);
       }
-      Bq[j] = pack8(r[0], r[1], r[2], r[3]);
+      Bq[j] = pack8(rh[0], rh[1], rh[2], rh[3]);
+      Bl[j] = pack8(rl[0], rl[1], rl[2], rl[3]);
     }
-    return is_hi ? qz : 0.0f;
+    return is_col ? qz : 0.0f;
   };
 
   // softmax / output state (lane (n, g): head n for n < n_rep)
@@ -327,26 +399,39 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
   const float* kscale = (const float*)(arena + p.k.scale);
   const float* kzero = KINT ? (const float*)(arena + p.k.zero) : nullptr;
 
-  // One 32-token step: tokens [t0, t0 + 32), valid within [v_lo, v_hi).
-  // RING: the tokens come from the fp16 window instead of the quantized cache.
-  auto step = [&](auto ring_tag, int64_t t0, int64_t v_lo, int64_t v_hi) {
-    constexpr bool RING = decltype(ring_tag)::value;
-    const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
+  const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
+  const bool head_lane = n < n_rep;
 
-    // ---- issue the step's code loads ----------------------------------------------
-    constexpr int KW = RING ? 16 : KDW;
-    constexpr int VW = RING ? 32 : VDW;
-    u32 kw0[KW], kw1[KW], vw[VW];
-    if constexpr (!RING) {
-      const uint8_t* kb = arena + p.k.codes + (bh * p.Tc + t0 + tok_in0) * (D * KB / 8) + g * (4 * KDW);
-      load_dw<KDW>(kb, kw0);
-      load_dw<KDW>(kb + 4 * (D * KB / 8), kw1);
-      load_dw<VDW>(arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * (32 * D * VB / 8) + lane * (4 * VDW), vw);
-    } else {
-      load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0) % p.Rs)) * D + 32 * g) * 2, kw0);
-      load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0 + 4) % p.Rs)) * D + 32 * g) * 2, kw1);
-      load_dw<32>(arena + p.ring_v + (bh * (p.Rs / 32) + ((t0 % p.Rs) >> 5)) * (32 * D * 2) + lane * 128, vw);
+  // Code (and value scale / zero) loads of a quantized step, issued one step ahead.
+  auto load_q = [&](int64_t t0, StepData<KDW, VDW, VINT ? 8 * VG : 1>& d) {
+    const uint8_t* kb = arena + p.k.codes + (bh * p.Tc + t0 + tok_in0) * (D * KB / 8) + g * (4 * KDW);
+    load_dw<KDW>(kb, d.k0);
+    load_dw<KDW>(kb + 4 * (D * KB / 8), d.k1);
+    load_dw<VDW>(arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * (32 * D * VB / 8) + lane * (4 * VDW), d.v);
+    if constexpr (VINT) {
+      if (head_lane) {   // only lanes that own a query head use the per-token scale / zero
+        const float4* sp = (const float4*)((const float*)(arena + p.v.scale) + (bh * p.Tc + t0 + 8 * g) * VG);
+        const float4* zp = (const float4*)((const float*)(arena + p.v.zero) + (bh * p.Tc + t0 + 8 * g) * VG);
+#pragma unroll
+        for (int i = 0; i < 2 * VG; ++i) {
+          const float4 sv = sp[i], zv = zp[i];
+          d.vs[4 * i] = sv.x; d.vs[4 * i + 1] = sv.y; d.vs[4 * i + 2] = sv.z; d.vs[4 * i + 3] = sv.w;
+          d.vz[4 * i] = zv.x; d.vz[4 * i + 1] = zv.y; d.vz[4 * i + 2] = zv.z; d.vz[4 * i + 3] = zv.w;
+        }
+      }
     }
+  };
+  auto load_r = [&](int64_t t0, StepData<16, 32, 1>& d) {
+    load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0) % p.Rs)) * D + 32 * g) * 2, d.k0);
+    load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0 + 4) % p.Rs)) * D + 32 * g) * 2, d.k1);
+    load_dw<32>(arena + p.ring_v + (bh * (p.Rs / 32) + ((t0 % p.Rs) >> 5)) * (32 * D * 2) + lane * 128, d.v);
+  };
+
+  // One 32-token step: tokens [t0, t0 + 32), valid within [v_lo, v_hi).
+  // RING: tokens from the fp16 window; FULL: every token of the step is valid.
+  auto step = [&](auto ring_tag, auto full_tag, int64_t t0, int64_t v_lo, int64_t v_hi, const auto& d) {
+    constexpr bool RING = decltype(ring_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
 
     // ---- query operand of this step ---------------------------------------------
     if constexpr (!RING) {
@@ -378,6 +463,11 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
       const float* zc = RING ? nullptr : kzero + (bh * p.k.meta_rows + t0 / p.k.group) * D + 32 * g;
       const float2* crow = coarse + (t0 >> 5) * 64 + 16 * g;
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      u32 hc0[16], hc1[16];
+      if constexpr (!RING) {
+        key_codes_f16<KF>(d.k0, hc0);
+        key_codes_f16<KF>(d.k1, hc1);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // this k-step's 8 channels: scale / zero and coarse angles
@@ -393,7 +483,8 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
                               make_float2(cb.z, cb.w)};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const u32* w = u ? kw1 : kw0;
+          const u32* w = u ? d.k1 : d.k0;
+          const u32* hc = u ? hc1 : hc0;
           const int dt = tok_in0 + 4 * u;               // token offset in the step (t0 is 32-aligned)
           u32 r[4], rl[4];
 #pragma unroll
@@ -401,21 +492,25 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
             const int e = 8 * j + 2 * pr;
             float k0, k1;
             if constexpr (!RING) {
-              k0 = (float)kcode<KF>(w, e) * s8[2 * pr] + z8[2 * pr];
-              k1 = (float)kcode<KF>(w, e + 1) * s8[2 * pr + 1] + z8[2 * pr + 1];
+              const u32 c0 = hc[code_reg<KF>(e)], c1 = hc[code_reg<KF>(e + 1)];
+              k0 = __builtin_fmaf(code_half<KF>(e) ? hi_f(c0) : lo_f(c0), s8[2 * pr], z8[2 * pr]);
+              k1 = __builtin_fmaf(code_half<KF>(e + 1) ? hi_f(c1) : lo_f(c1), s8[2 * pr + 1], z8[2 * pr + 1]);
             } else {
               k0 = lo_f(w[e >> 1]);
               k1 = hi_f(w[e >> 1]);
             }
-            const float2 ff = fine_s[dt][16 * g + (e >> 1)];
+            const float2 ff = fine_s[16 * g + (e >> 1)][dt ^ (4 * g)];
             const float cs = cc[pr].x * ff.x - cc[pr].y * ff.y;
             const float sn = cc[pr].y * ff.x + cc[pr].x * ff.y;
             const float r0 = k0 * cs - k1 * sn, r1 = k0 * sn + k1 * cs;
             r[pr] = pk_f16(r0, r1);
-            if constexpr (KSPLIT) rl[pr] = pk_f16(r0 - lo_f(r[pr]), r1 - hi_f(r[pr]));
+            if constexpr (KSPLIT) rl[pr] = pk_f16(__builtin_fmaf(-1.0f, lo_f(r[pr]), r0),
+                                                  __builtin_fmaf(-1.0f, hi_f(r[pr]), r1));
           }
           floatx4& acc = u ? acc1 : acc0;
-          acc = mfma(pack8(r[0], r[1], r[2], r[3]), Bq[j], acc);
+          const half8 ah = pack8(r[0], r[1], r[2], r[3]);
+          acc = mfma(ah, Bq[j], acc);
+          acc = mfma(ah, Bl[j], acc);
           if constexpr (KSPLIT) acc = mfma(pack8(rl[0], rl[1], rl[2], rl[3]), Bq[j], acc);
         }
       }
@@ -424,7 +519,7 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
     } else {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const u32* w = u ? kw1 : kw0;
+        const u32* w = u ? d.k1 : d.k0;
         half8 A[4];
         if constexpr (RING) {
 #pragma unroll
@@ -436,50 +531,46 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
         }
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma(A[j], Bq[j], acc);
+        for (int j = 0; j < 4; ++j) {
+          acc = mfma(A[j], Bq[j], acc);
+          acc = mfma(A[j], Bl[j], acc);
+        }
         S[u] = acc;
       }
     }
 
     // ---- logits of lane (n, g): head n, tokens 8g + k -------------------------
+    // Lanes n >= n_rep compute rows that are never read; they are left unmasked.
     float x[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = S[u][i] + kbias;
-        const float other = __shfl_down(v, n_rep, 16);      // lo column of the same head
-        x[4 * u + i] = v + other;
+      for (int i = 0; i < 4; ++i) x[4 * u + i] = S[u][i] + kbias;
+    u32 valid = 0xFFu;
+    if constexpr (!FULL) {
+      valid = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t t = t0 + 8 * g + k;
+        const bool ok = t >= v_lo && t < v_hi;
+        valid |= (ok ? 1u : 0u) << k;
+        if (!ok) x[k] = kNegBig;
       }
     }
-    u32 valid = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t t = t0 + 8 * g + k;
-      const bool ok = t >= v_lo && t < v_hi && n < n_rep;
-      valid |= (ok ? 1u : 0u) << k;
-      if (!ok) x[k] = kNegBig;
-    }
 
-    // ---- online softmax ----------------------------------------------------------
+    // ---- online softmax (accumulators rescaled only when a running max rises) ----
     float mx = x[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
     mx = wave_max16(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float pk[8], psum = 0.0f;
+    if (__any(head_lane && mx > m_run)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pk[k] = ((valid >> k) & 1u) ? exp2f(x[k] - m_new) : 0.0f;
-      psum += pk[k];
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < VG; ++i) vbias[i] *= alpha;
-    {   // rescale O: lane (c, g') holds rows (heads) 4g'+i
-      float al[4];
+      for (int i = 0; i < VG; ++i) vbias[i] *= alpha;
+      float al[4];    // lane (c, g') holds rows (heads) 4g'+i
 #pragma unroll
       for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 15, 64);
 #pragma unroll
@@ -487,37 +578,42 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[t8][i] *= al[i];
     }
+    float pk[8], psum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pk[k] = exp2f(x[k] - m_run);
+      if constexpr (!FULL) pk[k] = ((valid >> k) & 1u) ? pk[k] : 0.0f;
+      psum += pk[k];
+    }
+    l_run += psum;
 
     // ---- PV -------------------------------------------------------------------------
     if constexpr (!RING && VINT) {
-      // A = p * s (hi and lo fp16 halves), z enters through the per-group bias.
-      // Only lanes that own a query head read the per-token scale / zero.
-      const float* vsp = (const float*)(arena + p.v.scale) + (bh * p.Tc + t0 + 8 * g) * VG;
-      const float* vzp = (const float*)(arena + p.v.zero) + (bh * p.Tc + t0 + 8 * g) * VG;
+      // A = p * s as hi + lo fp16 halves (lo = exact residual by FMA); z enters
+      // through the per-group bias
       half8 Ah[VG], Al[VG];
 #pragma unroll
       for (int gr = 0; gr < VG; ++gr) {
-        float sv[8], zv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { sv[k] = 0.0f; zv[k] = 0.0f; }
-        if (n < n_rep) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) { sv[k] = vsp[k * VG + gr]; zv[k] = vzp[k * VG + gr]; }
-        }
         u32 rh[4], rl[4];
         float zsum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float av[2];
+          float sv[2], pv[2];
 #pragma unroll
           for (int hlf = 0; hlf < 2; ++hlf) {
             const int k = i + 4 * hlf;
-            const bool ok = (valid >> k) & 1u;
-            av[hlf] = ok ? pk[k] * sv[k] : 0.0f;
-            zsum += ok ? pk[k] * zv[k] : 0.0f;
+            sv[hlf] = d.vs[k * VG + gr];
+            pv[hlf] = pk[k];
+            float zt = d.vz[k * VG + gr];
+            if constexpr (!FULL) {
+              const bool ok = (valid >> k) & 1u;
+              sv[hlf] = ok ? sv[hlf] : 0.0f;
+              zt = ok ? zt : 0.0f;
+            }
+            zsum = __builtin_fmaf(pv[hlf], zt, zsum);
           }
-          rh[i] = pk_f16(av[0], av[1]);
-          rl[i] = pk_f16(av[0] - lo_f(rh[i]), av[1] - hi_f(rh[i]));
+          rh[i] = pk_f16(pv[0] * sv[0], pv[1] * sv[1]);
+          rl[i] = pk_f16(__builtin_fmaf(pv[0], sv[0], -lo_f(rh[i])), __builtin_fmaf(pv[1], sv[1], -hi_f(rh[i])));
         }
         Ah[gr] = pack8(rh[0], rh[1], rh[2], rh[3]);
         Al[gr] = pack8(rl[0], rl[1], rl[2], rl[3]);
@@ -525,33 +621,62 @@ __global__ void __launch_bounds__(256) attn_mfma(Plan p, Args a) {
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const half8 bv = unpack_v<VF>(vw, i);
+        const half8 bv = unpack_v<VF>(d.v, i);
         O[i] = mfma(Ah[(16 * i) / VGC], bv, O[i]);
         O[i] = mfma(Al[(16 * i) / VGC], bv, O[i]);
       }
     } else {
       // FP8 values: A = p * v_scale; window values: A = p
-      const u32 vv = __shfl(valid, 16 * g, 64);   // validity of the B lane's tokens 8g..8g+7
       const float vsc = (!RING && VF == FP8) ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
       u32 r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = pk_f16(pk[i] * vsc, pk[i + 4] * vsc);
       const half8 Ap = pack8(r[0], r[1], r[2], r[3]);
+      u32 vv = 0xFFu;
+      if constexpr (!FULL) vv = __shfl(valid, 16 * g, 64);   // validity of the B lane's tokens
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // invalid tokens' bytes may not be finite values: zero them
         half8 bv;
-        if constexpr (RING) bv = unpack_v_f16(vw, i);
-        else bv = unpack_v<VF>(vw, i);
-        O[i] = mfma(Ap, mask_tokens(bv, vv), O[i]);
+        if constexpr (RING) bv = unpack_v_f16(d.v, i);
+        else bv = unpack_v<VF>(d.v, i);
+        // bytes of invalid tokens may not be finite values: zero them
+        if constexpr (!FULL) bv = mask_tokens(bv, vv);
+        O[i] = mfma(Ap, bv, O[i]);
       }
     }
   };
 
+  auto qstep = [&](int64_t st, const StepData<KDW, VDW, VINT ? 8 * VG : 1>& d) {
+    const int64_t t0 = lo + st * 32;
+    if (t0 + 32 <= q_end) step(std::false_type{}, std::true_type{}, t0, lo, q_end, d);
+    else step(std::false_type{}, std::false_type{}, t0, lo, q_end, d);
+  };
+
   const int64_t qs_end = st_end < nq ? st_end : nq;
-  for (int64_t st = st_beg; st < qs_end; ++st) step(std::false_type{}, lo + st * 32, lo, q_end);
-  for (int64_t st = (st_beg > nq ? st_beg : nq); st < st_end; ++st)
-    step(std::true_type{}, s_w0 + (st - nq) * 32, w_beg, hi);
+  {
+    // KVQ_MFMA_STEPS_IN_FLIGHT steps' loads are issued before the first is computed
+    constexpr int NF = KVQ_MFMA_STEPS_IN_FLIGHT;
+    StepData<KDW, VDW, VINT ? 8 * VG : 1> d[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) d[i].zero_meta();
+    int64_t st = st_beg;
+    for (; st + NF - 1 < qs_end; st += NF) {
+#pragma unroll
+      for (int i = 0; i < NF; ++i) load_q(lo + (st + i) * 32, d[i]);
+#pragma unroll
+      for (int i = 0; i < NF; ++i) qstep(st + i, d[i]);
+    }
+    for (; st < qs_end; ++st) {
+      load_q(lo + st * 32, d[0]);
+      qstep(st, d[0]);
+    }
+  }
+  for (int64_t st = (st_beg > nq ? st_beg : nq); st < st_end; ++st) {
+    StepData<16, 32, 1> d;
+    const int64_t t0 = s_w0 + (st - nq) * 32;
+    load_r(t0, d);
+    step(std::true_type{}, std::false_type{}, t0, w_beg, hi, d);
+  }
 
   // ---- combine the wavefronts of the work-group ------------------------------------
   l_run = wave_sum16(l_run);

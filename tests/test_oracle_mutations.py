@@ -13,11 +13,22 @@ import oracle.quant as Q
 from tests import test_oracle_pins as P
 
 
+def _all_assertions(e):
+    """True when e is an AssertionError, or a group of them (hypothesis raises
+    an exception group when it finds several distinct failing examples)."""
+    if isinstance(e, AssertionError):
+        return True
+    subs = getattr(e, "exceptions", None)
+    return bool(subs) and all(_all_assertions(x) for x in subs)
+
+
 def _fails(fn, *args):
     try:
         fn(*args)
-    except AssertionError:
-        return True
+    except Exception as e:  # noqa: BLE001  (only assertion failures count)
+        if _all_assertions(e):
+            return True
+        raise
     return False
 
 
