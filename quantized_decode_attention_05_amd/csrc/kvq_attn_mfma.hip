@@ -18,11 +18,15 @@
 //    Different Axes", section "Where does RoPE break this?") each lane
 //    dequantizes its 32 channels to fp32, rotates the channel pairs by
 //    position * theta_i and packs fp16 operands (dequantize -> rotate -> dot).
-//  * PV as O = P . V_tile: A = probabilities of 8 tokens per lane (times the
-//    per-token value scale of the N-tile's channel group), B = value codes
-//    read straight from the 32-token block layout, whose lane order is exactly
-//    this instruction's B-operand order; zero-points enter through per-(head,
-//    group) bias sums.
+//  * PV as O = P . V_tile: A = probabilities of 8 tokens per lane times the
+//    per-token value scale, B = value codes read straight from the 32-token
+//    block layout, whose lane order is exactly this instruction's B-operand
+//    order.  The 16 A rows are (value channel group, query head) pairs, row
+//    R = group * n_rep + head, so one A operand serves every channel group;
+//    tile i keeps the rows of its own group.  Zero-points enter through
+//    per-row bias sums.  For this the query columns repeat the heads
+//    (column n is head n mod n_rep), which costs nothing: the columns beyond
+//    n_rep would otherwise be padding.
 //  * The S^T accumulator of two 16-token tiles (token rows permuted so that
 //    lane (n, g) holds tokens 8g..8g+7) is already the PV A operand of head n:
 //    no data moves between QK^T and PV.
@@ -86,6 +90,21 @@ __device__ __forceinline__ u32 unmagic(u32 v) {
   const half2v m = {(_Float16)1024.0f, (_Float16)1024.0f};
   return h2u(__builtin_bit_cast(half2v, v) - m);
 }
+// (x & mask) | 1024-pattern, then minus 1024: two fp16 codes in one instruction
+// pair plus the subtraction.  The AND-OR is written out because the compiler
+// splits it into two instructions when both constants are literals.
+__device__ __forceinline__ u32 code_pair(u32 x, u32 mask) {
+  u32 r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(kMagic));
+  return unmagic(r);
+}
+// -1.0f that the compiler cannot fold, so that r - (float)h stays a mixed
+// fp16/fp32 FMA (v_fma_mix*) instead of a conversion plus a subtraction
+__device__ __forceinline__ float opaque_neg1() {
+  float r;
+  asm("v_mov_b32 %0, -1.0" : "=v"(r));
+  return r;
+}
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -113,7 +132,7 @@ __device__ __forceinline__ void unpack_k_magic(const u32* w, half8* A) {
     for (int j = 0; j < 4; ++j) {
       u32 r[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = unmagic(((w[j] >> (4 * i)) & 0x000F000Fu) | kMagic);
+      for (int i = 0; i < 4; ++i) r[i] = code_pair(w[j] >> (4 * i), 0x000F000Fu);
       A[j] = pack8(r[0], r[1], r[2], r[3]);
     }
   } else if constexpr (KF == INT2) {
@@ -121,7 +140,7 @@ __device__ __forceinline__ void unpack_k_magic(const u32* w, half8* A) {
     for (int d = 0; d < 2; ++d) {
       u32 r[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = unmagic(((w[d] >> (2 * i)) & 0x00030003u) | kMagic);
+      for (int i = 0; i < 8; ++i) r[i] = code_pair(w[d] >> (2 * i), 0x00030003u);
       A[2 * d] = pack8(r[0], r[1], r[2], r[3]);
       A[2 * d + 1] = pack8(r[4], r[5], r[6], r[7]);
     }
@@ -159,12 +178,12 @@ __device__ __forceinline__ void key_codes_f16(const u32* w, u32* h) {
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[8 * d + i] = unmagic(((w[d] >> (2 * i)) & 0x00030003u) | kMagic);
+      for (int i = 0; i < 8; ++i) h[8 * d + i] = code_pair(w[d] >> (2 * i), 0x00030003u);
   } else if constexpr (KF == INT4) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[4 * d + i] = unmagic(((w[d] >> (4 * i)) & 0x000F000Fu) | kMagic);
+      for (int i = 0; i < 4; ++i) h[4 * d + i] = code_pair(w[d] >> (4 * i), 0x000F000Fu);
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -196,14 +215,14 @@ template <int VF>
 __device__ __forceinline__ half8 unpack_v(const u32* w, int i) {
   if constexpr (VF == INT4) {
     const u32 x = w[i];
-    return pack8(unmagic((x & 0x000F000Fu) | kMagic), unmagic(((x >> 4) & 0x000F000Fu) | kMagic),
-                 unmagic(((x >> 8) & 0x000F000Fu) | kMagic), unmagic(((x >> 12) & 0x000F000Fu) | kMagic));
+    return pack8(code_pair(x, 0x000F000Fu), code_pair(x >> 4, 0x000F000Fu),
+                 code_pair(x >> 8, 0x000F000Fu), code_pair(x >> 12, 0x000F000Fu));
   } else if constexpr (VF == INT2) {
     // word i = 16 bits at half (i & 1) of dword i/2; token k at bit 2k
     const u32 x = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     const u32 y = (x & 0xFFu) | ((x & 0xFF00u) << 8);       // tokens 0..3 low half, 4..7 high half
-    return pack8(unmagic((y & 0x00030003u) | kMagic), unmagic(((y >> 2) & 0x00030003u) | kMagic),
-                 unmagic(((y >> 4) & 0x00030003u) | kMagic), unmagic(((y >> 6) & 0x00030003u) | kMagic));
+    return pack8(code_pair(y, 0x00030003u), code_pair(y >> 2, 0x00030003u),
+                 code_pair(y >> 4, 0x00030003u), code_pair(y >> 6, 0x00030003u));
   } else if constexpr (VF == INT8) {
     const u32 d0 = w[2 * i], d1 = w[2 * i + 1];
     u32 r[4];
@@ -262,6 +281,8 @@ __device__ __forceinline__ float wave_sum16(float x) {
   x += __shfl_xor(x, 16, 64);
   return x + __shfl_xor(x, 32, 64);
 }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Per-lane data of one 32-token step (codes and per-token value scale / zero).
 template <int KW, int VW, int NVM>
@@ -335,11 +356,14 @@ attn_mfma(Plan p, Args a) {
   const int64_t st_beg = wave * per_wave;
   const int64_t st_end = st_beg + per_wave < nsteps ? st_beg + per_wave : nsteps;
 
-  // query columns: column n < n_rep is head n (hi and lo fp16 halves of the
-  // fp32 query in two operands); other columns are zero
-  const int head = n < n_rep ? n : 0;
-  const bool is_col = n < n_rep;
+  // query columns: column n is head n mod n_rep (hi and lo fp16 halves of the
+  // fp32 query in two operands).  Lane (n, g) is A row n of PV: value group
+  // n / n_rep (rows past the last group are computed and never read).
+  const int head = n % n_rep;
+  const bool is_col = true;
+  const int vgrp = (n / n_rep) < VG ? n / n_rep : VG - 1;
   const float qs = a.qscale;
+  const float neg1 = opaque_neg1();
 
   half8 Bq[4], Bl[4];   // query operand (hi, lo) of the current key group / window
   float kbias = 0.0f;   // per-column logit bias from the key zero-points
@@ -388,9 +412,7 @@ attn_mfma(Plan p, Args a) {
 
   // softmax / output state (lane (n, g): head n for n < n_rep)
   float m_run = kNegBig, l_run = 0.0f;
-  float vbias[VG];
-#pragma unroll
-  for (int i = 0; i < VG; ++i) vbias[i] = 0.0f;
+  float vbias = 0.0f;   // sum_t p_t z_t of this lane's PV row
   floatx4 O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -400,24 +422,27 @@ attn_mfma(Plan p, Args a) {
   const float* kzero = KINT ? (const float*)(arena + p.k.zero) : nullptr;
 
   const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
-  const bool head_lane = n < n_rep;
 
   // Code (and value scale / zero) loads of a quantized step, issued one step ahead.
-  auto load_q = [&](int64_t t0, StepData<KDW, VDW, VINT ? 8 * VG : 1>& d) {
+  auto load_q = [&](int64_t t0, StepData<KDW, VDW, VINT ? 8 : 1>& d) {
     const uint8_t* kb = arena + p.k.codes + (bh * p.Tc + t0 + tok_in0) * (D * KB / 8) + g * (4 * KDW);
     load_dw<KDW>(kb, d.k0);
     load_dw<KDW>(kb + 4 * (D * KB / 8), d.k1);
     load_dw<VDW>(arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * (32 * D * VB / 8) + lane * (4 * VDW), d.v);
     if constexpr (VINT) {
-      if (head_lane) {   // only lanes that own a query head use the per-token scale / zero
-        const float4* sp = (const float4*)((const float*)(arena + p.v.scale) + (bh * p.Tc + t0 + 8 * g) * VG);
-        const float4* zp = (const float4*)((const float*)(arena + p.v.zero) + (bh * p.Tc + t0 + 8 * g) * VG);
+      // scale / zero of tokens 8g..8g+7 in this lane's value group
+      const float* sp = (const float*)(arena + p.v.scale) + (bh * p.Tc + t0 + 8 * g) * VG + vgrp;
+      const float* zp = (const float*)(arena + p.v.zero) + (bh * p.Tc + t0 + 8 * g) * VG + vgrp;
+      if constexpr (VG == 1) {
+        const float4 s0 = ((const float4*)sp)[0], s1 = ((const float4*)sp)[1];
+        const float4 z0 = ((const float4*)zp)[0], z1 = ((const float4*)zp)[1];
+        d.vs[0] = s0.x; d.vs[1] = s0.y; d.vs[2] = s0.z; d.vs[3] = s0.w;
+        d.vs[4] = s1.x; d.vs[5] = s1.y; d.vs[6] = s1.z; d.vs[7] = s1.w;
+        d.vz[0] = z0.x; d.vz[1] = z0.y; d.vz[2] = z0.z; d.vz[3] = z0.w;
+        d.vz[4] = z1.x; d.vz[5] = z1.y; d.vz[6] = z1.z; d.vz[7] = z1.w;
+      } else {
 #pragma unroll
-        for (int i = 0; i < 2 * VG; ++i) {
-          const float4 sv = sp[i], zv = zp[i];
-          d.vs[4 * i] = sv.x; d.vs[4 * i + 1] = sv.y; d.vs[4 * i + 2] = sv.z; d.vs[4 * i + 3] = sv.w;
-          d.vz[4 * i] = zv.x; d.vz[4 * i + 1] = zv.y; d.vz[4 * i + 2] = zv.z; d.vz[4 * i + 3] = zv.w;
-        }
+        for (int k = 0; k < 8; ++k) { d.vs[k] = sp[k * VG]; d.vz[k] = zp[k * VG]; }
       }
     }
   };
@@ -504,8 +529,8 @@ attn_mfma(Plan p, Args a) {
             const float sn = cc[pr].y * ff.x + cc[pr].x * ff.y;
             const float r0 = k0 * cs - k1 * sn, r1 = k0 * sn + k1 * cs;
             r[pr] = pk_f16(r0, r1);
-            if constexpr (KSPLIT) rl[pr] = pk_f16(__builtin_fmaf(-1.0f, lo_f(r[pr]), r0),
-                                                  __builtin_fmaf(-1.0f, hi_f(r[pr]), r1));
+            if constexpr (KSPLIT) rl[pr] = pk_f16(__builtin_fmaf(lo_f(r[pr]), neg1, r0),
+                                                  __builtin_fmaf(hi_f(r[pr]), neg1, r1));
           }
           floatx4& acc = u ? acc1 : acc0;
           const half8 ah = pack8(r[0], r[1], r[2], r[3]);
@@ -563,13 +588,12 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
     for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
     mx = wave_max16(mx);
-    if (__any(head_lane && mx > m_run)) {
+    if (__any(mx > m_run)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < VG; ++i) vbias[i] *= alpha;
+      vbias *= alpha;
       float al[4];    // lane (c, g') holds rows (heads) 4g'+i
 #pragma unroll
       for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 15, 64);
@@ -581,7 +605,7 @@ attn_mfma(Plan p, Args a) {
     float pk[8], psum = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      pk[k] = exp2f(x[k] - m_run);
+      pk[k] = fast_exp2(x[k] - m_run);
       if constexpr (!FULL) pk[k] = ((valid >> k) & 1u) ? pk[k] : 0.0f;
       psum += pk[k];
     }
@@ -590,40 +614,36 @@ attn_mfma(Plan p, Args a) {
     // ---- PV -------------------------------------------------------------------------
     if constexpr (!RING && VINT) {
       // A = p * s as hi + lo fp16 halves (lo = exact residual by FMA); z enters
-      // through the per-group bias
-      half8 Ah[VG], Al[VG];
+      // through the row's bias
+      u32 rh[4], rl[4];
+      float zsum = 0.0f;
 #pragma unroll
-      for (int gr = 0; gr < VG; ++gr) {
-        u32 rh[4], rl[4];
-        float zsum = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        float sv[2], pv[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sv[2], pv[2];
-#pragma unroll
-          for (int hlf = 0; hlf < 2; ++hlf) {
-            const int k = i + 4 * hlf;
-            sv[hlf] = d.vs[k * VG + gr];
-            pv[hlf] = pk[k];
-            float zt = d.vz[k * VG + gr];
-            if constexpr (!FULL) {
-              const bool ok = (valid >> k) & 1u;
-              sv[hlf] = ok ? sv[hlf] : 0.0f;
-              zt = ok ? zt : 0.0f;
-            }
-            zsum = __builtin_fmaf(pv[hlf], zt, zsum);
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int k = i + 4 * hlf;
+          sv[hlf] = d.vs[k];
+          pv[hlf] = pk[k];
+          float zt = d.vz[k];
+          if constexpr (!FULL) {
+            const bool ok = (valid >> k) & 1u;
+            sv[hlf] = ok ? sv[hlf] : 0.0f;
+            zt = ok ? zt : 0.0f;
           }
-          rh[i] = pk_f16(pv[0] * sv[0], pv[1] * sv[1]);
-          rl[i] = pk_f16(__builtin_fmaf(pv[0], sv[0], -lo_f(rh[i])), __builtin_fmaf(pv[1], sv[1], -hi_f(rh[i])));
+          zsum = __builtin_fmaf(pv[hlf], zt, zsum);
         }
-        Ah[gr] = pack8(rh[0], rh[1], rh[2], rh[3]);
-        Al[gr] = pack8(rl[0], rl[1], rl[2], rl[3]);
-        vbias[gr] += zsum;
+        rh[i] = pk_f16(pv[0] * sv[0], pv[1] * sv[1]);
+        rl[i] = pk_f16(__builtin_fmaf(pv[0], sv[0], -lo_f(rh[i])), __builtin_fmaf(pv[1], sv[1], -hi_f(rh[i])));
       }
+      const half8 Ah = pack8(rh[0], rh[1], rh[2], rh[3]);
+      const half8 Al = pack8(rl[0], rl[1], rl[2], rl[3]);
+      vbias += zsum;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const half8 bv = unpack_v<VF>(d.v, i);
-        O[i] = mfma(Ah[(16 * i) / VGC], bv, O[i]);
-        O[i] = mfma(Al[(16 * i) / VGC], bv, O[i]);
+        O[i] = mfma(Ah, bv, O[i]);
+        O[i] = mfma(Al, bv, O[i]);
       }
     } else {
       // FP8 values: A = p * v_scale; window values: A = p
@@ -646,7 +666,7 @@ attn_mfma(Plan p, Args a) {
     }
   };
 
-  auto qstep = [&](int64_t st, const StepData<KDW, VDW, VINT ? 8 * VG : 1>& d) {
+  auto qstep = [&](int64_t st, const StepData<KDW, VDW, VINT ? 8 : 1>& d) {
     const int64_t t0 = lo + st * 32;
     if (t0 + 32 <= q_end) step(std::false_type{}, std::true_type{}, t0, lo, q_end, d);
     else step(std::false_type{}, std::false_type{}, t0, lo, q_end, d);
@@ -656,7 +676,7 @@ attn_mfma(Plan p, Args a) {
   {
     // KVQ_MFMA_STEPS_IN_FLIGHT steps' loads are issued before the first is computed
     constexpr int NF = KVQ_MFMA_STEPS_IN_FLIGHT;
-    StepData<KDW, VDW, VINT ? 8 * VG : 1> d[NF];
+    StepData<KDW, VDW, VINT ? 8 : 1> d[NF];
 #pragma unroll
     for (int i = 0; i < NF; ++i) d[i].zero_meta();
     int64_t st = st_beg;
@@ -680,26 +700,25 @@ attn_mfma(Plan p, Args a) {
 
   // ---- combine the wavefronts of the work-group ------------------------------------
   l_run = wave_sum16(l_run);
-#pragma unroll
-  for (int i = 0; i < VG; ++i) vbias[i] = wave_sum16(vbias[i]);
+  vbias = wave_sum16(vbias);
   if (g == 0 && n < n_rep) {
     red_ml[wave][n][0] = m_run;
     red_ml[wave][n][1] = l_run;
   }
-  // O rows -> LDS with the value bias of the channel's group added.  Row r of
-  // this lane is head 4g + r; its per-group bias lives in lane (4g + r) mod 16.
-  float rbias[4][VG];
+  // O rows -> LDS with the row's value bias added.  Accumulator row r of this
+  // lane is A row R = 4g + r (value group R / n_rep, head R mod n_rep); tile i
+  // keeps the rows of its own group.  Row R's bias lives in lane R.
+  float rbias[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q2 = 0; q2 < VG; ++q2) rbias[r][q2] = __shfl(vbias[q2], (4 * g + r) & 15, 64);
+  for (int r = 0; r < 4; ++r) rbias[r] = __shfl(vbias, (4 * g + r) & 15, 64);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = 16 * i + n;
+    const int gi = VINT ? (16 * i) / VGC : 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int hrow = 4 * g + r;
-      if (hrow < n_rep) red_o[wave][hrow][c] = O[i][r] + (VINT ? rbias[r][(16 * i) / VGC] : 0.0f);
+      const int R = 4 * g + r;
+      if (R / n_rep == gi) red_o[wave][R - gi * n_rep][c] = O[i][r] + (VINT ? rbias[r] : 0.0f);
     }
   }
   __syncthreads();
@@ -711,7 +730,7 @@ attn_mfma(Plan p, Args a) {
     float L = 0.0f, acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(red_ml[w][r][0] - M);
+      const float f = fast_exp2(red_ml[w][r][0] - M);
       L += f * red_ml[w][r][1];
       acc += f * red_o[w][r][c];
     }
@@ -738,15 +757,15 @@ static int vfmt(const Plan& p) {
   return -1;
 }
 
+static int vgroups(const Plan& p) { return p.v.scheme == KVQ_FP8_E4M3 ? 1 : 128 / p.v.group; }
+
 bool mfma_supported(const Plan& p) {
   if (p.D != 128 || p.n_rep > 8) return false;
   const int kf = kfmt(p), vf = vfmt(p);
   if (kf < 0 || vf < 0) return false;
   if (p.pre_rope && kf == FP8) return false;
-  return true;
+  return p.n_rep * vgroups(p) <= 16;   // PV rows are (value group, head) pairs
 }
-
-static int vgroups(const Plan& p) { return p.v.scheme == KVQ_FP8_E4M3 ? 1 : 128 / p.v.group; }
 
 template <int KF, int VF, int VG>
 static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
@@ -766,7 +785,7 @@ static void launch_kv(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
       case 1: launch_kvg<KF, VF, 1>(p, grid, s, a); break;
       case 2: launch_kvg<KF, VF, 2>(p, grid, s, a); break;
       case 4: launch_kvg<KF, VF, 4>(p, grid, s, a); break;
-      default: launch_kvg<KF, VF, 8>(p, grid, s, a); break;
+      default: launch_kvg<KF, VF, 8>(p, grid, s, a); break;   // n_rep <= 2
     }
   }
 }
