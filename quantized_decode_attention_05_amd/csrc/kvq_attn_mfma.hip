@@ -47,13 +47,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32;
 
-// Tuning knobs: quantized steps whose loads are issued together, and the
-// wavefronts per SIMD the register allocation must allow (0: compiler's choice).
-#ifndef KVQ_MFMA_STEPS_IN_FLIGHT
-#define KVQ_MFMA_STEPS_IN_FLIGHT 2
+// Tuning knobs: the wavefronts per SIMD the register allocation must allow
+// (0: compiler's choice) and the LDS stages per wavefront (0: by stage size).
+#ifndef KVQ_MFMA_STAGES
+#define KVQ_MFMA_STAGES 0
 #endif
 #ifndef KVQ_MFMA_WAVES_PER_EU
-#define KVQ_MFMA_WAVES_PER_EU 0
+#define KVQ_MFMA_WAVES_PER_EU 2
 #endif
 
 namespace mf {
@@ -73,6 +73,7 @@ struct Args {
   int64_t T, Tq, chunk;
   int32_t S;
   float qscale;
+  float neg1;   // -1.0f, passed in so that r - (float)h stays one mixed fp16/fp32 FMA
 };
 
 __device__ __forceinline__ half8 pack8(u32 a, u32 b, u32 c, u32 d) {
@@ -92,24 +93,48 @@ __device__ __forceinline__ u32 unmagic(u32 v) {
 }
 // (x & mask) | 1024-pattern, then minus 1024: two fp16 codes in one instruction
 // pair plus the subtraction.  The AND-OR is written out because the compiler
-// splits it into two instructions when both constants are literals.
+// splits it into two instructions when both constants are literals.  Its
+// result always passes through the compiler-generated subtraction before a
+// matrix instruction reads it: the compiler's hazard checks do not look inside
+// inline assembly, and a matrix instruction needs wait states after a vector
+// instruction writes one of its source registers.
 __device__ __forceinline__ u32 code_pair(u32 x, u32 mask) {
   u32 r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(kMagic));
   return unmagic(r);
 }
-// -1.0f that the compiler cannot fold, so that r - (float)h stays a mixed
-// fp16/fp32 FMA (v_fma_mix*) instead of a conversion plus a subtraction
-__device__ __forceinline__ float opaque_neg1() {
-  float r;
-  asm("v_mov_b32 %0, -1.0" : "=v"(r));
-  return r;
+// ---- direct global -> LDS streaming ------------------------------------------------
+// Each lane moves 16 bytes from its own global address to LDS byte
+// lds_base + 16 * lane (lds_base wave-uniform, in M0).  Issued as inline
+// assembly so that the compiler's wait-count bookkeeping, which would make
+// every later LDS read wait for all outstanding loads, does not see them; the
+// kernel waits for each stage itself with s_waitcnt vmcnt.  Nothing else in
+// the streaming loop issues vector-memory loads, so the counts are exact.
+__device__ __forceinline__ void dma16(u32 lds_base, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds_base), "v"(gptr) : "memory", "m0");
 }
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ u32 lds_addr(const void* p) {
+  return (u32)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float lo_f(u32 x) { return (float)__builtin_bit_cast(half2v, x)[0]; }
 __device__ __forceinline__ float hi_f(u32 x) { return (float)__builtin_bit_cast(half2v, x)[1]; }
+
+// fp16 residuals (r0 - h.lo, r1 - h.hi) of two fp32 values whose fp16
+// roundings are packed in h (neg1 = -1.0f, opaque to the compiler so the
+// subtraction stays a mixed-precision FMA with an fp16 source).
+__device__ __forceinline__ u32 f16_residual2(u32 h, float r0, float r1, float neg1) {
+  const _Float16 a = (_Float16)__builtin_fmaf(lo_f(h), neg1, r0);
+  const _Float16 b = (_Float16)__builtin_fmaf(hi_f(h), neg1, r1);
+  const half2v v = {a, b};
+  return h2u(v);
+}
 
 // Position of the e-th fp16 of k-step j inside a lane's 32 key channels, for
 // the register order each code width unpacks into.
@@ -316,11 +341,24 @@ attn_mfma(Plan p, Args a) {
   constexpr bool KINT = KF != FP8, VINT = VF != FP8;
   constexpr int VGC = D / VG;             // value channels per group
 
+  // Per-wavefront LDS ring of NB stages; a stage holds one 32-token step:
+  // key rows, the value block, value scale/zero, the key group's scale/zero
+  // rows and (pre-RoPE keys) the step's coarse cos/sin row.
+  constexpr int KROW = D * KB / 8;
+  constexpr int SZ_K = 32 * KROW, SZ_V = 32 * D * VB / 8;
+  constexpr int SZ_VM = VINT ? 2 * 32 * VG * 4 : 0, SZ_KM = KINT ? 2 * D * 4 : 0, SZ_KT = ROPE ? 64 * 8 : 0;
+  constexpr int OFF_V = SZ_K, OFF_VM = OFF_V + SZ_V, OFF_KM = OFF_VM + SZ_VM, OFF_KT = OFF_KM + SZ_KM;
+  constexpr int SLOT = OFF_KT + SZ_KT;
+  constexpr int NB = KVQ_MFMA_STAGES > 0 ? KVQ_MFMA_STAGES : (SLOT <= 6144 ? 3 : 2);
+  constexpr int N_DMA = SZ_K / 1024 + SZ_V / 1024 + (SZ_VM + 1023) / 1024 + (KINT ? 1 : 0) + (ROPE ? 1 : 0);
+  static_assert(SZ_K % 1024 == 0 && SZ_V % 1024 == 0 && NB * SLOT >= 8 * D * 4, "stage layout");
+
   __shared__ float q_s[8][D];
   // fine RoPE table, pair-major with the token offset XOR-swizzled by the
   // lane row so that one row's 16 lanes (16 offsets, one pair) hit distinct banks
   __shared__ float2 fine_s[ROPE ? 64 : 1][ROPE ? 32 : 1];
-  __shared__ float red_o[kWaves][8][D];
+  // the rings; after the streaming loop a wavefront's ring holds its O rows
+  __shared__ __attribute__((aligned(16))) uint8_t ring_s[kWaves][NB * SLOT];
   __shared__ float red_ml[kWaves][8][2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -363,7 +401,6 @@ attn_mfma(Plan p, Args a) {
   const bool is_col = true;
   const int vgrp = (n / n_rep) < VG ? n / n_rep : VG - 1;
   const float qs = a.qscale;
-  const float neg1 = opaque_neg1();
 
   half8 Bq[4], Bl[4];   // query operand (hi, lo) of the current key group / window
   float kbias = 0.0f;   // per-column logit bias from the key zero-points
@@ -417,22 +454,57 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const float2* coarse = ROPE ? (const float2*)(arena + p.rope) + 32 * 64 : nullptr;
-  const float* kscale = (const float*)(arena + p.k.scale);
-  const float* kzero = KINT ? (const float*)(arena + p.k.zero) : nullptr;
+  const float k_fp8 = KF == FP8 ? ((const float*)(arena + p.k.scale))[kvh] : 1.0f;
+  const float v_fp8 = VF == FP8 ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
+  uint8_t* const ring = ring_s[wave];
 
   const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
 
-  // Code (and value scale / zero) loads of a quantized step, issued one step ahead.
-  auto load_q = [&](int64_t t0, StepData<KDW, VDW, VINT ? 8 : 1>& d) {
-    const uint8_t* kb = arena + p.k.codes + (bh * p.Tc + t0 + tok_in0) * (D * KB / 8) + g * (4 * KDW);
-    load_dw<KDW>(kb, d.k0);
-    load_dw<KDW>(kb + 4 * (D * KB / 8), d.k1);
-    load_dw<VDW>(arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * (32 * D * VB / 8) + lane * (4 * VDW), d.v);
+  // Stage of a quantized step: issue its loads straight into LDS slot sl.
+  auto issue = [&](int64_t t0, int sl) {
+    uint8_t* const st_l = ring + sl * SLOT;
+    const uint8_t* kg = arena + p.k.codes + (bh * p.Tc + t0) * KROW;
+#pragma unroll
+    for (int c = 0; c < SZ_K / 1024; ++c)
+      dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + 1024 * c)), kg + 1024 * c + 16 * lane);
+    const uint8_t* vg = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V;
+#pragma unroll
+    for (int c = 0; c < SZ_V / 1024; ++c)
+      dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_V + 1024 * c)), vg + 1024 * c + 16 * lane);
     if constexpr (VINT) {
-      // scale / zero of tokens 8g..8g+7 in this lane's value group
-      const float* sp = (const float*)(arena + p.v.scale) + (bh * p.Tc + t0 + 8 * g) * VG + vgrp;
-      const float* zp = (const float*)(arena + p.v.zero) + (bh * p.Tc + t0 + 8 * g) * VG + vgrp;
+      // 16-byte granules: 8*VG of scales, then 8*VG of zero-points
+      const uint8_t* vs = arena + p.v.scale + (bh * p.Tc + t0) * VG * 4;
+      const uint8_t* vz = arena + p.v.zero + (bh * p.Tc + t0) * VG * 4;
+#pragma unroll
+      for (int c = 0; c < (SZ_VM + 1023) / 1024; ++c) {
+        const int e = 64 * c + lane;
+        if (e < 16 * VG)
+          dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_VM + 1024 * c)),
+                e < 8 * VG ? vs + 16 * e : vz + 16 * (e - 8 * VG));
+      }
+    }
+    if constexpr (KINT) {
+      // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key group
+      const int64_t mrow = (bh * p.k.meta_rows + t0 / p.k.group) * D * 4;
+      dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_KM)),
+            lane < 32 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 32));
+    }
+    if constexpr (ROPE) {
+      if (lane < 32)
+        dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_KT)),
+              arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane);
+    }
+  };
+  // Registers of a quantized step from its LDS slot.
+  auto read_slot = [&](int sl, StepData<KDW, VDW, VINT ? 8 : 1>& d) {
+    const uint8_t* st_l = ring + sl * SLOT;
+    const uint8_t* kr = st_l + tok_in0 * KROW + g * (4 * KDW);
+    load_dw<KDW>(kr, d.k0);
+    load_dw<KDW>(kr + 4 * KROW, d.k1);
+    load_dw<VDW>(st_l + OFF_V + lane * (4 * VDW), d.v);
+    if constexpr (VINT) {
+      const float* sp = (const float*)(st_l + OFF_VM) + 8 * g * VG + vgrp;
+      const float* zp = sp + 32 * VG;
       if constexpr (VG == 1) {
         const float4 s0 = ((const float4*)sp)[0], s1 = ((const float4*)sp)[1];
         const float4 z0 = ((const float4*)zp)[0], z1 = ((const float4*)zp)[1];
@@ -446,6 +518,7 @@ attn_mfma(Plan p, Args a) {
       }
     }
   };
+  int cur_slot = 0;   // slot of the quantized step being computed
   auto load_r = [&](int64_t t0, StepData<16, 32, 1>& d) {
     load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0) % p.Rs)) * D + 32 * g) * 2, d.k0);
     load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0 + 4) % p.Rs)) * D + 32 * g) * 2, d.k1);
@@ -463,15 +536,14 @@ attn_mfma(Plan p, Args a) {
       if constexpr (KINT && !ROPE) {
         const int64_t grp = t0 / p.k.group;
         if (b_mode != 0 || grp != cur_grp) {
-          const float* sc = kscale + (bh * p.k.meta_rows + grp) * D + 32 * g;
-          const float* zc = kzero + (bh * p.k.meta_rows + grp) * D + 32 * g;
+          const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM) + 32 * g;
+          const float* zc = sc + D;
           kbias = wave_sum16(build_b(sc, zc, 1.0f, false));
           cur_grp = grp;
           b_mode = 0;
         }
       } else if (b_mode != 0) {
-        const float ks = (KF == FP8) ? kscale[kvh] : 1.0f;
-        build_b(nullptr, nullptr, ks, true);
+        build_b(nullptr, nullptr, k_fp8, true);
         kbias = 0.0f;
         b_mode = 0;
       }
@@ -484,9 +556,10 @@ attn_mfma(Plan p, Args a) {
     // ---- S^T = K . Q^T for the two 16-token tiles ----------------------------
     floatx4 S[2];
     if constexpr (ROPE) {
-      const float* sc = RING ? nullptr : kscale + (bh * p.k.meta_rows + t0 / p.k.group) * D + 32 * g;
-      const float* zc = RING ? nullptr : kzero + (bh * p.k.meta_rows + t0 / p.k.group) * D + 32 * g;
-      const float2* crow = coarse + (t0 >> 5) * 64 + 16 * g;
+      const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM) + 32 * g;
+      const float* zc = sc + D;
+      const float2* crow = RING ? (const float2*)(arena + p.rope) + (32 + (t0 >> 5)) * 64 + 16 * g
+                                : (const float2*)(ring + cur_slot * SLOT + OFF_KT) + 16 * g;
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       u32 hc0[16], hc1[16];
       if constexpr (!RING) {
@@ -529,8 +602,7 @@ attn_mfma(Plan p, Args a) {
             const float sn = cc[pr].y * ff.x + cc[pr].x * ff.y;
             const float r0 = k0 * cs - k1 * sn, r1 = k0 * sn + k1 * cs;
             r[pr] = pk_f16(r0, r1);
-            if constexpr (KSPLIT) rl[pr] = pk_f16(__builtin_fmaf(lo_f(r[pr]), neg1, r0),
-                                                  __builtin_fmaf(hi_f(r[pr]), neg1, r1));
+            if constexpr (KSPLIT) rl[pr] = f16_residual2(r[pr], r0, r1, a.neg1);
           }
           floatx4& acc = u ? acc1 : acc0;
           const half8 ah = pack8(r[0], r[1], r[2], r[3]);
@@ -647,7 +719,7 @@ attn_mfma(Plan p, Args a) {
       }
     } else {
       // FP8 values: A = p * v_scale; window values: A = p
-      const float vsc = (!RING && VF == FP8) ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
+      const float vsc = (!RING && VF == FP8) ? v_fp8 : 1.0f;
       u32 r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = pk_f16(pk[i] * vsc, pk[i + 4] * vsc);
@@ -674,21 +746,24 @@ attn_mfma(Plan p, Args a) {
 
   const int64_t qs_end = st_end < nq ? st_end : nq;
   {
-    // KVQ_MFMA_STEPS_IN_FLIGHT steps' loads are issued before the first is computed
-    constexpr int NF = KVQ_MFMA_STEPS_IN_FLIGHT;
-    StepData<KDW, VDW, VINT ? 8 : 1> d[NF];
+    // Streaming loop: NB - 1 stages in flight; a stage is consumed (waited
+    // for, read into registers), the next stage is issued into the slot freed
+    // by the previous step, then the step is computed.
+    const int64_t qs_beg = st_beg < qs_end ? st_beg : qs_end;
 #pragma unroll
-    for (int i = 0; i < NF; ++i) d[i].zero_meta();
-    int64_t st = st_beg;
-    for (; st + NF - 1 < qs_end; st += NF) {
-#pragma unroll
-      for (int i = 0; i < NF; ++i) load_q(lo + (st + i) * 32, d[i]);
-#pragma unroll
-      for (int i = 0; i < NF; ++i) qstep(st + i, d[i]);
-    }
-    for (; st < qs_end; ++st) {
-      load_q(lo + st * 32, d[0]);
-      qstep(st, d[0]);
+    for (int i = 0; i < NB - 1; ++i)
+      if (qs_beg + i < qs_end) issue(lo + (qs_beg + i) * 32, i);
+    int sl = 0;
+    for (int64_t st = qs_beg; st < qs_end; ++st) {
+      if (st + NB - 2 < qs_end) wait_vmem<N_DMA * (NB - 2)>();
+      else wait_vmem<0>();
+      StepData<KDW, VDW, VINT ? 8 : 1> d;
+      read_slot(sl, d);
+      cur_slot = sl;
+      const int nsl = sl == 0 ? NB - 1 : sl - 1;
+      if (st + NB - 1 < qs_end) issue(lo + (st + NB - 1) * 32, nsl);
+      qstep(st, d);
+      sl = sl == NB - 1 ? 0 : sl + 1;
     }
   }
   for (int64_t st = (st_beg > nq ? st_beg : nq); st < st_end; ++st) {
@@ -705,6 +780,7 @@ attn_mfma(Plan p, Args a) {
     red_ml[wave][n][0] = m_run;
     red_ml[wave][n][1] = l_run;
   }
+  float (*const red_o_w)[D] = (float (*)[D])ring;   // this wavefront's O rows
   // O rows -> LDS with the row's value bias added.  Accumulator row r of this
   // lane is A row R = 4g + r (value group R / n_rep, head R mod n_rep); tile i
   // keeps the rows of its own group.  Row R's bias lives in lane R.
@@ -718,7 +794,7 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int R = 4 * g + r;
-      if (R / n_rep == gi) red_o[wave][R - gi * n_rep][c] = O[i][r] + (VINT ? rbias[r] : 0.0f);
+      if (R / n_rep == gi) red_o_w[R - gi * n_rep][c] = O[i][r] + (VINT ? rbias[r] : 0.0f);
     }
   }
   __syncthreads();
@@ -732,7 +808,7 @@ attn_mfma(Plan p, Args a) {
     for (int w = 0; w < kWaves; ++w) {
       const float f = fast_exp2(red_ml[w][r][0] - M);
       L += f * red_ml[w][r][1];
-      acc += f * red_o[w][r][c];
+      acc += f * ((const float (*)[D])ring_s[w])[r][c];
     }
     const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + r;
     a.ws_o[(hq * a.S + split) * D + c] = acc;
@@ -803,7 +879,7 @@ static void launch_k(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
 hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
                                  float sm_scale, void* ws, hipStream_t s) {
   Args a{(const uint8_t*)arena, q, (float*)((uint8_t*)ws + ap.ws_o), (float*)((uint8_t*)ws + ap.ws_ml),
-         ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e};
+         ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e, -1.0f};
   dim3 grid(ap.splits, p.Hkv, p.B);
   switch (kfmt(p)) {
     case INT2: launch_k<INT2>(p, grid, s, a); break;
