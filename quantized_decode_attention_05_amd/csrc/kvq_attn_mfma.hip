@@ -116,9 +116,6 @@ __device__ __forceinline__ void dma16(u32 lds_base, const void* gptr) {
 template <int N> __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
-__device__ __forceinline__ u32 lds_addr(const void* p) {
-  return (u32)(size_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -361,7 +358,8 @@ attn_mfma(Plan p, Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring_s[kWaves][NB * SLOT];
   __shared__ float red_ml[kWaves][8][2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int n_rep = p.n_rep;
@@ -404,7 +402,7 @@ attn_mfma(Plan p, Args a) {
 
   half8 Bq[4], Bl[4];   // query operand (hi, lo) of the current key group / window
   float kbias = 0.0f;   // per-column logit bias from the key zero-points
-  int64_t cur_grp = -1;
+  bool new_kgrp = true;  // the step being computed starts a key group (or is the first)
   int b_mode = -1;      // 0: quantized keys, 1: window keys
 
   // Bq/Bl for per-channel factors sc (or a uniform factor); returns this
@@ -457,20 +455,19 @@ attn_mfma(Plan p, Args a) {
   const float k_fp8 = KF == FP8 ? ((const float*)(arena + p.k.scale))[kvh] : 1.0f;
   const float v_fp8 = VF == FP8 ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
   uint8_t* const ring = ring_s[wave];
+  const u32 ring_lds = (u32)(size_t)(__attribute__((address_space(3))) uint8_t*)&ring_s[0][0] + wave * (NB * SLOT);
 
   const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
 
   // Stage of a quantized step: issue its loads straight into LDS slot sl.
-  auto issue = [&](int64_t t0, int sl) {
-    uint8_t* const st_l = ring + sl * SLOT;
-    const uint8_t* kg = arena + p.k.codes + (bh * p.Tc + t0) * KROW;
+  auto issue = [&](int64_t t0, int64_t kgrp, int sl) {
+    const u32 sb = __builtin_amdgcn_readfirstlane(ring_lds + sl * SLOT);
+    const uint8_t* kg = arena + p.k.codes + (bh * p.Tc + t0) * KROW + 16 * lane;
 #pragma unroll
-    for (int c = 0; c < SZ_K / 1024; ++c)
-      dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + 1024 * c)), kg + 1024 * c + 16 * lane);
-    const uint8_t* vg = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V;
+    for (int c = 0; c < SZ_K / 1024; ++c) dma16(sb + 1024 * c, kg + 1024 * c);
+    const uint8_t* vg = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V + 16 * lane;
 #pragma unroll
-    for (int c = 0; c < SZ_V / 1024; ++c)
-      dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_V + 1024 * c)), vg + 1024 * c + 16 * lane);
+    for (int c = 0; c < SZ_V / 1024; ++c) dma16(sb + OFF_V + 1024 * c, vg + 1024 * c);
     if constexpr (VINT) {
       // 16-byte granules: 8*VG of scales, then 8*VG of zero-points
       const uint8_t* vs = arena + p.v.scale + (bh * p.Tc + t0) * VG * 4;
@@ -478,21 +475,16 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
       for (int c = 0; c < (SZ_VM + 1023) / 1024; ++c) {
         const int e = 64 * c + lane;
-        if (e < 16 * VG)
-          dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_VM + 1024 * c)),
-                e < 8 * VG ? vs + 16 * e : vz + 16 * (e - 8 * VG));
+        if (e < 16 * VG) dma16(sb + OFF_VM + 1024 * c, e < 8 * VG ? vs + 16 * e : vz + 16 * (e - 8 * VG));
       }
     }
     if constexpr (KINT) {
       // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key group
-      const int64_t mrow = (bh * p.k.meta_rows + t0 / p.k.group) * D * 4;
-      dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_KM)),
-            lane < 32 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 32));
+      const int64_t mrow = (bh * p.k.meta_rows + kgrp) * D * 4;
+      dma16(sb + OFF_KM, lane < 32 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 32));
     }
     if constexpr (ROPE) {
-      if (lane < 32)
-        dma16(__builtin_amdgcn_readfirstlane(lds_addr(st_l + OFF_KT)),
-              arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane);
+      if (lane < 32) dma16(sb + OFF_KT, arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane);
     }
   };
   // Registers of a quantized step from its LDS slot.
@@ -534,12 +526,10 @@ attn_mfma(Plan p, Args a) {
     // ---- query operand of this step ---------------------------------------------
     if constexpr (!RING) {
       if constexpr (KINT && !ROPE) {
-        const int64_t grp = t0 / p.k.group;
-        if (b_mode != 0 || grp != cur_grp) {
+        if (b_mode != 0 || new_kgrp) {
           const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM) + 32 * g;
           const float* zc = sc + D;
           kbias = wave_sum16(build_b(sc, zc, 1.0f, false));
-          cur_grp = grp;
           b_mode = 0;
         }
       } else if (b_mode != 0) {
@@ -749,10 +739,22 @@ attn_mfma(Plan p, Args a) {
     // Streaming loop: NB - 1 stages in flight; a stage is consumed (waited
     // for, read into registers), the next stage is issued into the slot freed
     // by the previous step, then the step is computed.
+    // Key groups are tracked incrementally (one division up front): the
+    // issue side (i_grp, i_rem) and the compute side (c_rem) each advance by
+    // one 32-token step per iteration.
     const int64_t qs_beg = st_beg < qs_end ? st_beg : qs_end;
+    const int64_t kG = KINT ? p.k.group : 32;
+    int64_t i_grp = (lo + qs_beg * 32) / kG;
+    int64_t i_rem = (lo + qs_beg * 32) - i_grp * kG;
+    int64_t c_rem = i_rem;
+    const int64_t iss_end = lo + qs_end * 32;   // this wavefront's quantized steps only
+    auto next_issue = [&](int sl_) {
+      if (i_grp * kG + i_rem < iss_end) issue(i_grp * kG + i_rem, i_grp, sl_);
+      i_rem += 32;
+      if (i_rem == kG) { i_rem = 0; ++i_grp; }
+    };
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i)
-      if (qs_beg + i < qs_end) issue(lo + (qs_beg + i) * 32, i);
+    for (int i = 0; i < NB - 1; ++i) next_issue(i);
     int sl = 0;
     for (int64_t st = qs_beg; st < qs_end; ++st) {
       if (st + NB - 2 < qs_end) wait_vmem<N_DMA * (NB - 2)>();
@@ -760,9 +762,12 @@ attn_mfma(Plan p, Args a) {
       StepData<KDW, VDW, VINT ? 8 : 1> d;
       read_slot(sl, d);
       cur_slot = sl;
-      const int nsl = sl == 0 ? NB - 1 : sl - 1;
-      if (st + NB - 1 < qs_end) issue(lo + (st + NB - 1) * 32, nsl);
+      next_issue(sl == 0 ? NB - 1 : sl - 1);
+      new_kgrp = new_kgrp || c_rem == 0;
       qstep(st, d);
+      new_kgrp = false;
+      c_rem += 32;
+      if (c_rem == kG) c_rem = 0;
       sl = sl == NB - 1 ? 0 : sl + 1;
     }
   }
