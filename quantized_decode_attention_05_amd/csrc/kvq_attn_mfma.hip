@@ -192,27 +192,17 @@ __device__ __forceinline__ void unpack_k_fp8(const u32* w, half8* A) {
   }
 }
 
-// Exact fp16 codes of a lane's 32 key channels as 16 half2 registers; channel
-// e sits in register code_reg<KF>(e), half code_half<KF>(e).
+// Exact fp16 codes of a lane's 32 key channels come as 16 half2 registers;
+// channel e sits in register code_reg<KF>(e), half code_half<KF>(e).  This
+// decodes register idx alone, where it is first used.
 template <int KF>
-__device__ __forceinline__ void key_codes_f16(const u32* w, u32* h) {
-  if constexpr (KF == INT2) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[8 * d + i] = code_pair(w[d] >> (2 * i), 0x00030003u);
-  } else if constexpr (KF == INT4) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[4 * d + i] = code_pair(w[d] >> (4 * i), 0x000F000Fu);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32 src = w[i >> 1];
-      const int sh = 16 * (i & 1);
-      h[i] = unmagic((((src >> sh) & 0xFFu) | (((src >> (sh + 8)) & 0xFFu) << 16)) | kMagic);
-    }
+__device__ __forceinline__ u32 key_code_reg(const u32* w, int idx) {
+  if constexpr (KF == INT2) return code_pair(w[idx >> 3] >> (2 * (idx & 7)), 0x00030003u);
+  else if constexpr (KF == INT4) return code_pair(w[idx >> 2] >> (4 * (idx & 3)), 0x000F000Fu);
+  else {
+    const u32 src = w[idx >> 1];
+    const int sh = 16 * (idx & 1);
+    return unmagic((((src >> sh) & 0xFFu) | (((src >> (sh + 8)) & 0xFFu) << 16)) | kMagic);
   }
 }
 template <int KF> __device__ constexpr int code_reg(int e) {
@@ -407,7 +397,7 @@ attn_mfma(Plan p, Args a) {
 
   // Bq/Bl for per-channel factors sc (or a uniform factor); returns this
   // lane's part of sum_c q_c z_c
-  auto build_b = [&](const float* sc, const float* zc, float uniform, bool natural) {
+  auto build_b = [&](const float* sc, const float* zc, float uniform, bool natural) __attribute__((always_inline)) {
     float qz = 0.0f;
     // this lane's 32 channel scales / zero-points, fetched with wide loads up front
     float sv[32], zv[32];
@@ -460,35 +450,62 @@ attn_mfma(Plan p, Args a) {
   const int tok_in0 = 8 * (n >> 2) + (n & 3);   // A row n -> token of tile 0 (+4 for tile 1)
 
   // Stage of a quantized step: issue its loads straight into LDS slot sl.
-  auto issue = [&](int64_t t0, int64_t kgrp, int sl) {
-    const u32 sb = __builtin_amdgcn_readfirstlane(ring_lds + sl * SLOT);
-    const uint8_t* kg = arena + p.k.codes + (bh * p.Tc + t0) * KROW + 16 * lane;
-#pragma unroll
-    for (int c = 0; c < SZ_K / 1024; ++c) dma16(sb + 1024 * c, kg + 1024 * c);
-    const uint8_t* vg = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V + 16 * lane;
-#pragma unroll
-    for (int c = 0; c < SZ_V / 1024; ++c) dma16(sb + OFF_V + 1024 * c, vg + 1024 * c);
+  // Each lane keeps one global pointer per stream, set at the wavefront's
+  // first quantized step and advanced by constant strides (the key-metadata
+  // pointer by one row when a key group ends).
+  const uint8_t *pk = nullptr, *pv = nullptr, *pvm0 = nullptr, *pvm1 = nullptr, *pkm = nullptr, *prp = nullptr;
+  auto init_ptrs = [&](int64_t t0, int64_t kgrp) __attribute__((always_inline)) {
+    pk = arena + p.k.codes + (bh * p.Tc + t0) * KROW + 16 * lane;
+    pv = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V + 16 * lane;
     if constexpr (VINT) {
       // 16-byte granules: 8*VG of scales, then 8*VG of zero-points
       const uint8_t* vs = arena + p.v.scale + (bh * p.Tc + t0) * VG * 4;
       const uint8_t* vz = arena + p.v.zero + (bh * p.Tc + t0) * VG * 4;
-#pragma unroll
-      for (int c = 0; c < (SZ_VM + 1023) / 1024; ++c) {
-        const int e = 64 * c + lane;
-        if (e < 16 * VG) dma16(sb + OFF_VM + 1024 * c, e < 8 * VG ? vs + 16 * e : vz + 16 * (e - 8 * VG));
+      if constexpr (VG == 8) {
+        pvm0 = vs + 16 * lane;
+        pvm1 = vz + 16 * lane;
+      } else {
+        pvm0 = lane < 8 * VG ? vs + 16 * lane : vz + 16 * (lane - 8 * VG);
       }
     }
     if constexpr (KINT) {
       // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key group
       const int64_t mrow = (bh * p.k.meta_rows + kgrp) * D * 4;
-      dma16(sb + OFF_KM, lane < 32 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 32));
+      pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 32);
     }
+    if constexpr (ROPE) prp = arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane;
+  };
+  auto issue = [&](int sl) __attribute__((always_inline)) {
+    const u32 sb = __builtin_amdgcn_readfirstlane(ring_lds + sl * SLOT);
+#pragma unroll
+    for (int c = 0; c < SZ_K / 1024; ++c) dma16(sb + 1024 * c, pk + 1024 * c);
+#pragma unroll
+    for (int c = 0; c < SZ_V / 1024; ++c) dma16(sb + OFF_V + 1024 * c, pv + 1024 * c);
+    if constexpr (VINT) {
+      if constexpr (VG == 8) {
+        dma16(sb + OFF_VM, pvm0);
+        dma16(sb + OFF_VM + 1024, pvm1);
+      } else if (lane < 16 * VG) {
+        dma16(sb + OFF_VM, pvm0);
+      }
+    }
+    if constexpr (KINT) dma16(sb + OFF_KM, pkm);
     if constexpr (ROPE) {
-      if (lane < 32) dma16(sb + OFF_KT, arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane);
+      if (lane < 32) dma16(sb + OFF_KT, prp);
     }
   };
+  auto advance_ptrs = [&](bool group_ends) __attribute__((always_inline)) {
+    pk += SZ_K;
+    pv += SZ_V;
+    if constexpr (VINT) {
+      pvm0 += 32 * VG * 4;
+      if constexpr (VG == 8) pvm1 += 32 * VG * 4;
+    }
+    if constexpr (KINT) { if (group_ends) pkm += D * 4; }
+    if constexpr (ROPE) prp += 64 * 8;
+  };
   // Registers of a quantized step from its LDS slot.
-  auto read_slot = [&](int sl, StepData<KDW, VDW, VINT ? 8 : 1>& d) {
+  auto read_slot = [&](int sl, StepData<KDW, VDW, VINT ? 8 : 1>& d) __attribute__((always_inline)) {
     const uint8_t* st_l = ring + sl * SLOT;
     const uint8_t* kr = st_l + tok_in0 * KROW + g * (4 * KDW);
     load_dw<KDW>(kr, d.k0);
@@ -511,7 +528,7 @@ attn_mfma(Plan p, Args a) {
     }
   };
   int cur_slot = 0;   // slot of the quantized step being computed
-  auto load_r = [&](int64_t t0, StepData<16, 32, 1>& d) {
+  auto load_r = [&](int64_t t0, StepData<16, 32, 1>& d) __attribute__((always_inline)) {
     load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0) % p.Rs)) * D + 32 * g) * 2, d.k0);
     load_dw<16>(arena + p.ring_k + ((bh * p.Rs + ((t0 + tok_in0 + 4) % p.Rs)) * D + 32 * g) * 2, d.k1);
     load_dw<32>(arena + p.ring_v + (bh * (p.Rs / 32) + ((t0 % p.Rs) >> 5)) * (32 * D * 2) + lane * 128, d.v);
@@ -519,7 +536,7 @@ attn_mfma(Plan p, Args a) {
 
   // One 32-token step: tokens [t0, t0 + 32), valid within [v_lo, v_hi).
   // RING: tokens from the fp16 window; FULL: every token of the step is valid.
-  auto step = [&](auto ring_tag, auto full_tag, int64_t t0, int64_t v_lo, int64_t v_hi, const auto& d) {
+  auto step = [&](auto ring_tag, auto full_tag, int64_t t0, int64_t v_lo, int64_t v_hi, const auto& d) __attribute__((always_inline)) {
     constexpr bool RING = decltype(ring_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
 
@@ -551,11 +568,6 @@ attn_mfma(Plan p, Args a) {
       const float2* crow = RING ? (const float2*)(arena + p.rope) + (32 + (t0 >> 5)) * 64 + 16 * g
                                 : (const float2*)(ring + cur_slot * SLOT + OFF_KT) + 16 * g;
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      u32 hc0[16], hc1[16];
-      if constexpr (!RING) {
-        key_codes_f16<KF>(d.k0, hc0);
-        key_codes_f16<KF>(d.k1, hc1);
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // this k-step's 8 channels: scale / zero and coarse angles
@@ -572,7 +584,6 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const u32* w = u ? d.k1 : d.k0;
-          const u32* hc = u ? hc1 : hc0;
           const int dt = tok_in0 + 4 * u;               // token offset in the step (t0 is 32-aligned)
           u32 r[4], rl[4];
 #pragma unroll
@@ -580,7 +591,7 @@ attn_mfma(Plan p, Args a) {
             const int e = 8 * j + 2 * pr;
             float k0, k1;
             if constexpr (!RING) {
-              const u32 c0 = hc[code_reg<KF>(e)], c1 = hc[code_reg<KF>(e + 1)];
+              const u32 c0 = key_code_reg<KF>(w, code_reg<KF>(e)), c1 = key_code_reg<KF>(w, code_reg<KF>(e + 1));
               k0 = __builtin_fmaf(code_half<KF>(e) ? hi_f(c0) : lo_f(c0), s8[2 * pr], z8[2 * pr]);
               k1 = __builtin_fmaf(code_half<KF>(e + 1) ? hi_f(c1) : lo_f(c1), s8[2 * pr + 1], z8[2 * pr + 1]);
             } else {
@@ -600,6 +611,9 @@ attn_mfma(Plan p, Args a) {
           acc = mfma(ah, Bl[j], acc);
           if constexpr (KSPLIT) acc = mfma(pack8(rl[0], rl[1], rl[2], rl[3]), Bq[j], acc);
         }
+        // keep the scheduler from hoisting every k-step's LDS reads at once
+        // (register pressure): one k-step's operands are live at a time
+        __builtin_amdgcn_sched_barrier(0);
       }
       S[0] = acc0;
       S[1] = acc1;
@@ -728,7 +742,7 @@ attn_mfma(Plan p, Args a) {
     }
   };
 
-  auto qstep = [&](int64_t st, const StepData<KDW, VDW, VINT ? 8 : 1>& d) {
+  auto qstep = [&](int64_t st, const StepData<KDW, VDW, VINT ? 8 : 1>& d) __attribute__((always_inline)) {
     const int64_t t0 = lo + st * 32;
     if (t0 + 32 <= q_end) step(std::false_type{}, std::true_type{}, t0, lo, q_end, d);
     else step(std::false_type{}, std::false_type{}, t0, lo, q_end, d);
@@ -748,10 +762,13 @@ attn_mfma(Plan p, Args a) {
     int64_t i_rem = (lo + qs_beg * 32) - i_grp * kG;
     int64_t c_rem = i_rem;
     const int64_t iss_end = lo + qs_end * 32;   // this wavefront's quantized steps only
-    auto next_issue = [&](int sl_) {
-      if (i_grp * kG + i_rem < iss_end) issue(i_grp * kG + i_rem, i_grp, sl_);
+    init_ptrs(i_grp * kG + i_rem, i_grp);
+    auto next_issue = [&](int sl_) __attribute__((always_inline)) {
+      if (i_grp * kG + i_rem < iss_end) issue(sl_);
       i_rem += 32;
-      if (i_rem == kG) { i_rem = 0; ++i_grp; }
+      const bool ends = i_rem == kG;
+      if (ends) { i_rem = 0; ++i_grp; }
+      advance_ptrs(ends);
     };
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) next_issue(i);
