@@ -157,55 +157,56 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
   }
 }
 
-// Pass 2: one block per (query head, sequence), one thread per channel.
-// M = max_s m_s and L = sum_s 2^(m_s - M) l_s by block reductions; the split
-// weights are staged in LDS so the channel loop streams the partials.
-__global__ void __launch_bounds__(128) attn_merge(Plan p, const float* ws_o, const float* ws_ml, int S,
+// Pass 2: one work-group of four wavefronts per (query head, sequence).  Each
+// wavefront reduces M = max_s m_s and L = sum_s 2^(m_s - M) l_s over all
+// splits with cross-lane shuffles (no barriers); wavefront w then accumulates
+// the splits s = w (mod 4) for every channel (two per lane when D = 128), with
+// several splits' loads in flight, and the four partial sums meet in LDS.
+__device__ __forceinline__ float merge_wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float merge_wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__global__ void __launch_bounds__(256) attn_merge(Plan p, const float* ws_o, const float* ws_ml, int S,
                                                   void* out) {
-  __shared__ float red[128];
-  __shared__ float wts[256];
+  __shared__ float part[4][128];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int nt = blockDim.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int64_t row = (int64_t)b * p.Hq + hq;
   const float* ml = ws_ml + row * S * 2;
   float M = kNegBig;
-  for (int s = tid; s < S; s += nt) M = fmaxf(M, ml[2 * s]);
-  red[tid] = M;
-  __syncthreads();
-  for (int w = nt / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = merge_wave_max(M);
   float L = 0.0f;
-  for (int s = tid; s < S; s += nt) L += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
-  red[tid] = L;
-  __syncthreads();
-  for (int w = nt / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  L = red[0];
-  // every thread walks the split chunks (the barriers must be uniform); threads
-  // c < D accumulate channel c
-  const int c = tid;
-  const bool active = c < p.D;
-  float acc = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += 256) {
-    const int n = S - s0 < 256 ? S - s0 : 256;
-    __syncthreads();
-    for (int j = tid; j < n; j += nt) wts[j] = exp2f(ml[2 * (s0 + j)] - M);
-    __syncthreads();
-    if (active) {
-      const float* o = ws_o + (row * S + s0) * p.D + c;
-#pragma unroll 8
-      for (int j = 0; j < n; ++j) acc += wts[j] * o[(int64_t)j * p.D];
+  for (int s = lane; s < S; s += 64) L += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
+  L = merge_wave_sum(L);
+  const float* o = ws_o + row * S * p.D;
+  float a0 = 0.0f, a1 = 0.0f;
+  if (p.D == 128) {
+#pragma unroll 4
+    for (int s = w; s < S; s += 4) {
+      const float wt = exp2f(ml[2 * s] - M);
+      const float2 v = ((const float2*)(o + (int64_t)s * 128))[lane];
+      a0 += wt * v.x;
+      a1 += wt * v.y;
     }
+    part[w][2 * lane] = a0;
+    part[w][2 * lane + 1] = a1;
+  } else {   // D = 64: one channel per lane
+#pragma unroll 4
+    for (int s = w; s < S; s += 4) a0 += exp2f(ml[2 * s] - M) * o[(int64_t)s * 64 + lane];
+    part[w][lane] = a0;
   }
-  if (active) {
-    const float v = acc / L;
-    const int64_t oi = row * p.D + c;
+  __syncthreads();
+  if (tid < p.D) {
+    const float v = (part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]) / L;
+    const int64_t oi = row * p.D + tid;
     if (p.out_dtype == KVQ_F32) ((float*)out)[oi] = v;
     else if (p.out_dtype == KVQ_F16) ((_Float16*)out)[oi] = (_Float16)v;
     else {
@@ -276,7 +277,7 @@ hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena
     if (p.D == 128) hipLaunchKernelGGL(attn_generic<128>, grid, dim3(256), 0, s, p, a);
     else hipLaunchKernelGGL(attn_generic<64>, grid, dim3(256), 0, s, p, a);
   }
-  hipLaunchKernelGGL(attn_merge, dim3(p.Hq, p.B), dim3(128), 0, s, p, (const float*)ws_o,
+  hipLaunchKernelGGL(attn_merge, dim3(p.Hq, p.B), dim3(256), 0, s, p, (const float*)ws_o,
                      (const float*)ws_ml, ap.splits, out);
   return hipGetLastError();
 }

@@ -144,6 +144,21 @@ __device__ __forceinline__ int kslot(int j, int e) {
 
 template <int F> struct Bits { static constexpr int v = (F == FP8) ? 8 : F; };
 
+// LDS position of 16-byte granule q (channels 4q..4q+3) of a key scale or
+// zero-point row.  The four lane groups g read granules 8g + i at the same
+// time (broadcast over the 16 lanes of a group); XOR-ing bits 1-2 with g puts
+// the four in different bank groups.  An involution, so the loads that fill
+// the row use it too.
+__device__ __forceinline__ int km_pos(int q) { return q ^ (((q >> 3) & 3) << 1); }
+
+// LDS position of the 16-byte granule of token t (its four group scales, or
+// zero-points) when values have four channel groups: lane group g reads tokens
+// 8g + k at the same time; rotating each run of 8 by t/8 spreads the four over
+// bank groups.  vm_src is the inverse (which token's granule a filling lane
+// fetches).
+__device__ __forceinline__ int vm_pos(int t) { return (t & ~7) | ((t + (t >> 3)) & 7); }
+__device__ __forceinline__ int vm_src(int l) { return (l & ~7) | ((l - (l >> 3)) & 7); }
+
 // ---- key operand unpacking -------------------------------------------------------
 
 // Codes (1024 + x) of one lane's 32 channels in kslot order, from KB dwords.
@@ -404,7 +419,7 @@ attn_mfma(Plan p, Args a) {
     if (sc) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float4 a4 = ((const float4*)sc)[i], b4 = ((const float4*)zc)[i];
+        const float4 a4 = ((const float4*)sc)[km_pos(8 * g + i)], b4 = ((const float4*)zc)[km_pos(8 * g + i)];
         sv[4 * i] = a4.x; sv[4 * i + 1] = a4.y; sv[4 * i + 2] = a4.z; sv[4 * i + 3] = a4.w;
         zv[4 * i] = b4.x; zv[4 * i + 1] = b4.y; zv[4 * i + 2] = b4.z; zv[4 * i + 3] = b4.w;
       }
@@ -465,13 +480,15 @@ attn_mfma(Plan p, Args a) {
         pvm0 = vs + 16 * lane;
         pvm1 = vz + 16 * lane;
       } else {
-        pvm0 = lane < 8 * VG ? vs + 16 * lane : vz + 16 * (lane - 8 * VG);
+        if constexpr (VG == 4) pvm0 = lane < 32 ? vs + 16 * vm_src(lane) : vz + 16 * vm_src(lane - 32);
+        else pvm0 = lane < 8 * VG ? vs + 16 * lane : vz + 16 * (lane - 8 * VG);
       }
     }
     if constexpr (KINT) {
       // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key group
       const int64_t mrow = (bh * p.k.meta_rows + kgrp) * D * 4;
-      pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 32);
+      pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * km_pos(lane)
+                      : arena + p.k.zero + mrow + 16 * km_pos(lane - 32);
     }
     if constexpr (ROPE) prp = arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane;
   };
@@ -523,7 +540,16 @@ attn_mfma(Plan p, Args a) {
         d.vz[4] = z1.x; d.vz[5] = z1.y; d.vz[6] = z1.z; d.vz[7] = z1.w;
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) { d.vs[k] = sp[k * VG]; d.vz[k] = zp[k * VG]; }
+        for (int k = 0; k < 8; ++k) {
+          if constexpr (VG == 4) {
+            const float* vm = (const float*)(st_l + OFF_VM) + 4 * vm_pos(8 * g + k) + vgrp;
+            d.vs[k] = vm[0];
+            d.vz[k] = vm[128];
+          } else {
+            d.vs[k] = sp[k * VG];
+            d.vz[k] = zp[k * VG];
+          }
+        }
       }
     }
   };
@@ -544,7 +570,7 @@ attn_mfma(Plan p, Args a) {
     if constexpr (!RING) {
       if constexpr (KINT && !ROPE) {
         if (b_mode != 0 || new_kgrp) {
-          const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM) + 32 * g;
+          const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM);   // granules at km_pos
           const float* zc = sc + D;
           kbias = wave_sum16(build_b(sc, zc, 1.0f, false));
           b_mode = 0;
@@ -563,7 +589,7 @@ attn_mfma(Plan p, Args a) {
     // ---- S^T = K . Q^T for the two 16-token tiles ----------------------------
     floatx4 S[2];
     if constexpr (ROPE) {
-      const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM) + 32 * g;
+      const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM);   // granules at km_pos
       const float* zc = sc + D;
       const float2* crow = RING ? (const float2*)(arena + p.rope) + (32 + (t0 >> 5)) * 64 + 16 * g
                                 : (const float2*)(ring + cur_slot * SLOT + OFF_KT) + 16 * g;
@@ -573,8 +599,9 @@ attn_mfma(Plan p, Args a) {
         // this k-step's 8 channels: scale / zero and coarse angles
         float s8[8], z8[8];
         if constexpr (!RING) {
-          const float4 sa = ((const float4*)sc)[2 * j], sb = ((const float4*)sc)[2 * j + 1];
-          const float4 za = ((const float4*)zc)[2 * j], zb = ((const float4*)zc)[2 * j + 1];
+          const int qa = km_pos(8 * g + 2 * j), qb = km_pos(8 * g + 2 * j + 1);
+          const float4 sa = ((const float4*)sc)[qa], sb = ((const float4*)sc)[qb];
+          const float4 za = ((const float4*)zc)[qa], zb = ((const float4*)zc)[qb];
           s8[0] = sa.x; s8[1] = sa.y; s8[2] = sa.z; s8[3] = sa.w; s8[4] = sb.x; s8[5] = sb.y; s8[6] = sb.z; s8[7] = sb.w;
           z8[0] = za.x; z8[1] = za.y; z8[2] = za.z; z8[3] = za.w; z8[4] = zb.x; z8[5] = zb.y; z8[6] = zb.z; z8[7] = zb.w;
         }
