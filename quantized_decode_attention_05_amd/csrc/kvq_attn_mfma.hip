@@ -151,6 +151,12 @@ template <int F> struct Bits { static constexpr int v = (F == FP8) ? 8 : F; };
 // the row use it too.
 __device__ __forceinline__ int km_pos(int q) { return q ^ (((q >> 3) & 3) << 1); }
 
+// LDS positions of a channel pair's coefficients (pre-RoPE keys): the 16-byte
+// (u, v) entry and the 8-byte w entry of pair p, which lane group p / 16
+// reads; XOR-ing with the group spreads the four groups over bank groups.
+__device__ __forceinline__ int pc_pos(int p) { return p ^ (((p >> 4) & 3) << 1); }
+__device__ __forceinline__ int pcw_pos(int p) { return 2 * km_pos(p >> 1) + (p & 1); }
+
 // LDS position of the 16-byte granule of token t (its four group scales, or
 // zero-points) when values have four channel groups: lane group g reads tokens
 // 8g + k at the same time; rotating each run of 8 by t/8 spreads the four over
@@ -589,25 +595,24 @@ attn_mfma(Plan p, Args a) {
     // ---- S^T = K . Q^T for the two 16-token tiles ----------------------------
     floatx4 S[2];
     if constexpr (ROPE) {
-      const float* sc = (const float*)(ring + cur_slot * SLOT + OFF_KM);   // granules at km_pos
-      const float* zc = sc + D;
-      const float2* crow = RING ? (const float2*)(arena + p.rope) + (32 + (t0 >> 5)) * 64 + 16 * g
-                                : (const float2*)(ring + cur_slot * SLOT + OFF_KT) + 16 * g;
+      const float2* crow = (const float2*)(arena + p.rope) + (32 + (t0 >> 5)) * 64 + 16 * g;
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // this k-step's 8 channels: scale / zero and coarse angles
-        float s8[8], z8[8];
-        if constexpr (!RING) {
-          const int qa = km_pos(8 * g + 2 * j), qb = km_pos(8 * g + 2 * j + 1);
-          const float4 sa = ((const float4*)sc)[qa], sb = ((const float4*)sc)[qb];
-          const float4 za = ((const float4*)zc)[qa], zb = ((const float4*)zc)[qb];
-          s8[0] = sa.x; s8[1] = sa.y; s8[2] = sa.z; s8[3] = sa.w; s8[4] = sb.x; s8[5] = sb.y; s8[6] = sb.z; s8[7] = sb.w;
-          z8[0] = za.x; z8[1] = za.y; z8[2] = za.z; z8[3] = za.w; z8[4] = zb.x; z8[5] = zb.y; z8[6] = zb.z; z8[7] = zb.w;
+        // quantized steps: this k-step's four pair coefficients; window steps:
+        // the coarse angles of its four pairs
+        float4 uv[4];
+        float2 wv[4], cc[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const int pp = 16 * g + 4 * j + pr;
+          if constexpr (!RING) {
+            uv[pr] = ((const float4*)(ring + cur_slot * SLOT + OFF_KM))[pc_pos(pp)];
+            wv[pr] = ((const float2*)(ring + cur_slot * SLOT + OFF_KT))[pcw_pos(pp)];
+          } else {
+            cc[pr] = crow[4 * j + pr];
+          }
         }
-        const float4 ca = ((const float4*)crow)[2 * j], cb = ((const float4*)crow)[2 * j + 1];
-        const float2 cc[4] = {make_float2(ca.x, ca.y), make_float2(ca.z, ca.w), make_float2(cb.x, cb.y),
-                              make_float2(cb.z, cb.w)};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const u32* w = u ? d.k1 : d.k0;
@@ -616,19 +621,24 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
           for (int pr = 0; pr < 4; ++pr) {
             const int e = 8 * j + 2 * pr;
-            float k0, k1;
-            if constexpr (!RING) {
-              const u32 c0 = key_code_reg<KF>(w, code_reg<KF>(e)), c1 = key_code_reg<KF>(w, code_reg<KF>(e + 1));
-              k0 = __builtin_fmaf(code_half<KF>(e) ? hi_f(c0) : lo_f(c0), s8[2 * pr], z8[2 * pr]);
-              k1 = __builtin_fmaf(code_half<KF>(e + 1) ? hi_f(c1) : lo_f(c1), s8[2 * pr + 1], z8[2 * pr + 1]);
-            } else {
-              k0 = lo_f(w[e >> 1]);
-              k1 = hi_f(w[e >> 1]);
-            }
             const float2 ff = fine_s[16 * g + (e >> 1)][dt ^ (4 * g)];
-            const float cs = cc[pr].x * ff.x - cc[pr].y * ff.y;
-            const float sn = cc[pr].y * ff.x + cc[pr].x * ff.y;
-            const float r0 = k0 * cs - k1 * sn, r1 = k0 * sn + k1 * cs;
+            float r0, r1;
+            if constexpr (!RING) {
+              // coarse-rotated pair from its codes, then the fine rotation
+              const u32 c0 = key_code_reg<KF>(w, code_reg<KF>(e)), c1 = key_code_reg<KF>(w, code_reg<KF>(e + 1));
+              const float cx = code_half<KF>(e) ? hi_f(c0) : lo_f(c0);
+              const float cy = code_half<KF>(e + 1) ? hi_f(c1) : lo_f(c1);
+              const float px = __builtin_fmaf(cx, uv[pr].x, __builtin_fmaf(cy, uv[pr].z, wv[pr].x));
+              const float py = __builtin_fmaf(cx, uv[pr].y, __builtin_fmaf(cy, uv[pr].w, wv[pr].y));
+              r0 = px * ff.x - py * ff.y;
+              r1 = px * ff.y + py * ff.x;
+            } else {
+              const float k0 = lo_f(w[e >> 1]), k1 = hi_f(w[e >> 1]);
+              const float cs = cc[pr].x * ff.x - cc[pr].y * ff.y;
+              const float sn = cc[pr].y * ff.x + cc[pr].x * ff.y;
+              r0 = k0 * cs - k1 * sn;
+              r1 = k0 * sn + k1 * cs;
+            }
             r[pr] = pk_f16(r0, r1);
             if constexpr (KSPLIT) rl[pr] = f16_residual2(r[pr], r0, r1, a.neg1);
           }
@@ -806,6 +816,24 @@ attn_mfma(Plan p, Args a) {
       StepData<KDW, VDW, VINT ? 8 : 1> d;
       read_slot(sl, d);
       cur_slot = sl;
+      if constexpr (ROPE) {
+        // Lane i: channel pair i.  A pre-RoPE key pair of this step is
+        // (x, y) = (sx cx + zx, sy cy + zy); rotating it by the step's coarse
+        // angle (C, S) gives cx u + cy v + w with u = sx (C, S),
+        // v = sy (-S, C), w = (C zx - S zy, S zx + C zy).  Each (token, pair)
+        // then needs four FMAs and the fine rotation by its offset in the step.
+        // The coefficients replace the key-metadata and coarse rows in the
+        // slot: (u, v) over the 1 KB scale/zero rows, w over the coarse row.
+        uint8_t* st_l = ring + sl * SLOT;
+        const float2 cs2 = ((const float2*)(st_l + OFF_KT))[lane];
+        const int mo = 16 * km_pos(lane >> 1) + 8 * (lane & 1);
+        const float2 s2 = *(const float2*)(st_l + OFF_KM + mo);
+        const float2 z2 = *(const float2*)(st_l + OFF_KM + 4 * D + mo);
+        asm volatile("" ::: "memory");   // every lane's reads before any lane's writes
+        ((float4*)(st_l + OFF_KM))[pc_pos(lane)] = make_float4(s2.x * cs2.x, s2.x * cs2.y, -s2.y * cs2.y, s2.y * cs2.x);
+        ((float2*)(st_l + OFF_KT))[pcw_pos(lane)] =
+            make_float2(cs2.x * z2.x - cs2.y * z2.y, cs2.y * z2.x + cs2.x * z2.y);
+      }
       next_issue(sl == 0 ? NB - 1 : sl - 1);
       new_kgrp = new_kgrp || c_rem == 0;
       qstep(st, d);
