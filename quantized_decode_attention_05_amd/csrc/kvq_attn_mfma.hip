@@ -12,8 +12,9 @@
 //    exact in fp16; with per-channel keys the per-channel scale folds into the
 //    query columns and the zero-point into a per-head bias:
 //      logit = sum_c (q_c s_c) x_c + sum_c q_c z_c.
-//    A code becomes fp16 by ORing its bits into the mantissa of 1024 and
-//    subtracting 1024 (exact), so the accumulation never carries an offset.
+//    2- and 4-bit codes become fp16 through the fp4 / fp8 conversion
+//    instructions (exact, two codes each); 8-bit codes by ORing their bits
+//    into the mantissa of 1024 and subtracting 1024 (exact).
 //  * With pre-RoPE keys ("KV Cache Quantization: Why Keys and Values Need
 //    Different Axes", section "Where does RoPE break this?") each lane
 //    dequantizes its 32 channels to fp32, rotates the channel pairs by
@@ -133,13 +134,36 @@ __device__ __forceinline__ u32 f16_residual2(u32 h, float r0, float r1, float ne
   return h2u(v);
 }
 
+// ---- 2- and 4-bit codes through the conversion instructions ----------------------
+// A 2-bit code c in the low bits of a 4-bit field is the E2M1 value c / 2, and
+// a 4-bit code in the low bits of a byte is the E4M3 value c / 512 (the
+// subnormals and the first binade are evenly spaced), so the scaled fp4 -> fp16
+// and fp8 -> fp16 conversions return codes exactly, two per instruction.  A
+// dword masked with 0x33333333 (INT2) or 0x0F0F0F0F (INT4) keeps codes 0 and 2
+// of every run of four; shifted right by one code width first, codes 1 and 3.
+// So register r of a lane's 32 codes holds codes (4 (r >> 1) + (r & 1), + 2),
+// and fp16 number f of the registers in order is code nib_pos(f).
+__device__ constexpr int nib_pos(int f) { return 4 * (f >> 2) + ((f >> 1) & 1) + 2 * (f & 1); }
+
+__device__ __forceinline__ u32 fp4_pair(u32 x, int byte) {   // byte: compile-time after unrolling
+  switch (byte & 3) {
+    case 0: return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 0));
+    case 1: return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 1));
+    case 2: return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 2));
+    default: return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 3));
+  }
+}
+__device__ __forceinline__ u32 fp8_pair(u32 x, int word) {
+  return h2u(word & 1 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, true)
+                      : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, false));
+}
+
 // Position of the e-th fp16 of k-step j inside a lane's 32 key channels, for
 // the register order each code width unpacks into.
 template <int KF, bool ROPE>
 __device__ __forceinline__ int kslot(int j, int e) {
   if (ROPE || KF == INT8 || KF == FP8) return 8 * j + e;                  // natural
-  if (KF == INT4) return 8 * j + (e >> 1) + 4 * (e & 1);                   // (c, c+4) pairs
-  return 16 * (j >> 1) + 4 * (j & 1) + (e >> 1) + 8 * (e & 1);             // INT2: (c, c+8) pairs
+  return 8 * j + nib_pos(e);                                              // INT2 / INT4
 }
 
 template <int F> struct Bits { static constexpr int v = (F == FP8) ? 8 : F; };
@@ -167,26 +191,16 @@ __device__ __forceinline__ int vm_src(int l) { return (l & ~7) | ((l - (l >> 3))
 
 // ---- key operand unpacking -------------------------------------------------------
 
-// Codes (1024 + x) of one lane's 32 channels in kslot order, from KB dwords.
+// Exact fp16 codes of one lane's 32 key channels in kslot order, from KB dwords.
 template <int KF>
-__device__ __forceinline__ void unpack_k_magic(const u32* w, half8* A) {
-  if constexpr (KF == INT4) {
+__device__ __forceinline__ u32 key_code_reg(const u32* w, int r);
+template <int KF>
+__device__ __forceinline__ void unpack_k_codes(const u32* w, half8* A) {
+  if constexpr (KF == INT2 || KF == INT4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32 r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = code_pair(w[j] >> (4 * i), 0x000F000Fu);
-      A[j] = pack8(r[0], r[1], r[2], r[3]);
-    }
-  } else if constexpr (KF == INT2) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      u32 r[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = code_pair(w[d] >> (2 * i), 0x00030003u);
-      A[2 * d] = pack8(r[0], r[1], r[2], r[3]);
-      A[2 * d + 1] = pack8(r[4], r[5], r[6], r[7]);
-    }
+    for (int j = 0; j < 4; ++j)
+      A[j] = pack8(key_code_reg<KF>(w, 4 * j), key_code_reg<KF>(w, 4 * j + 1),
+                   key_code_reg<KF>(w, 4 * j + 2), key_code_reg<KF>(w, 4 * j + 3));
   } else {  // INT8: natural pairs (c, c+1)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -215,47 +229,44 @@ __device__ __forceinline__ void unpack_k_fp8(const u32* w, half8* A) {
 
 // Exact fp16 codes of a lane's 32 key channels come as 16 half2 registers;
 // channel e sits in register code_reg<KF>(e), half code_half<KF>(e).  This
-// decodes register idx alone, where it is first used.
+// decodes register r alone, where it is first used.
 template <int KF>
-__device__ __forceinline__ u32 key_code_reg(const u32* w, int idx) {
-  if constexpr (KF == INT2) return code_pair(w[idx >> 3] >> (2 * (idx & 7)), 0x00030003u);
-  else if constexpr (KF == INT4) return code_pair(w[idx >> 2] >> (4 * (idx & 3)), 0x000F000Fu);
-  else {
-    const u32 src = w[idx >> 1];
-    const int sh = 16 * (idx & 1);
+__device__ __forceinline__ u32 key_code_reg(const u32* w, int r) {
+  if constexpr (KF == INT2) {
+    const u32 x = w[r >> 3];
+    return fp4_pair(r & 1 ? (x >> 2) & 0x33333333u : x & 0x33333333u, r >> 1);
+  } else if constexpr (KF == INT4) {
+    const u32 x = w[r >> 2];
+    return fp8_pair(r & 1 ? (x >> 4) & 0x0F0F0F0Fu : x & 0x0F0F0F0Fu, r >> 1);
+  } else {
+    const u32 src = w[r >> 1];
+    const int sh = 16 * (r & 1);
     return unmagic((((src >> sh) & 0xFFu) | (((src >> (sh + 8)) & 0xFFu) << 16)) | kMagic);
   }
 }
 template <int KF> __device__ constexpr int code_reg(int e) {
-  return KF == INT2 ? 8 * (e >> 4) + (e & 7) : (KF == INT4 ? 4 * (e >> 3) + (e & 3) : e >> 1);
+  return (KF == INT2 || KF == INT4) ? 2 * (e >> 2) + (e & 1) : e >> 1;
 }
 template <int KF> __device__ constexpr int code_half(int e) {
-  return KF == INT2 ? (e >> 3) & 1 : (KF == INT4 ? (e >> 2) & 1 : e & 1);
-}
-
-// Integer code of channel e (0..31) of a lane's key data.
-template <int KF>
-__device__ __forceinline__ u32 kcode(const u32* w, int e) {
-  constexpr int B = Bits<KF>::v;
-  const int bit = e * B;
-  return (w[bit >> 5] >> (bit & 31)) & ((1u << B) - 1u);
+  return (KF == INT2 || KF == INT4) ? (e >> 1) & 1 : e & 1;
 }
 
 // ---- value operand unpacking -----------------------------------------------------
 
-// Tile i of a lane's value chunk as the B operand (token pairs (r, r+4)).
+// Tile i of a lane's value chunk as the B operand.  INT2 / INT4: fp16 number f
+// is token nib_pos(f); INT8 / FP8: token pairs (r, r+4) (vtok gives the order).
 template <int VF>
 __device__ __forceinline__ half8 unpack_v(const u32* w, int i) {
   if constexpr (VF == INT4) {
-    const u32 x = w[i];
-    return pack8(code_pair(x, 0x000F000Fu), code_pair(x >> 4, 0x000F000Fu),
-                 code_pair(x >> 8, 0x000F000Fu), code_pair(x >> 12, 0x000F000Fu));
+    const u32 x = w[i];                                                      // token k at bits 4k
+    const u32 ev = x & 0x0F0F0F0Fu, od = (x >> 4) & 0x0F0F0F0Fu;
+    return pack8(fp8_pair(ev, 0), fp8_pair(od, 0), fp8_pair(ev, 1), fp8_pair(od, 1));
   } else if constexpr (VF == INT2) {
     // word i = 16 bits at half (i & 1) of dword i/2; token k at bit 2k
-    const u32 x = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    const u32 y = (x & 0xFFu) | ((x & 0xFF00u) << 8);       // tokens 0..3 low half, 4..7 high half
-    return pack8(code_pair(y, 0x00030003u), code_pair(y >> 2, 0x00030003u),
-                 code_pair(y >> 4, 0x00030003u), code_pair(y >> 6, 0x00030003u));
+    const u32 x = w[i >> 1];
+    const u32 ev = x & 0x33333333u, od = (x >> 2) & 0x33333333u;
+    const int b = 2 * (i & 1);
+    return pack8(fp4_pair(ev, b), fp4_pair(od, b), fp4_pair(ev, b + 1), fp4_pair(od, b + 1));
   } else if constexpr (VF == INT8) {
     const u32 d0 = w[2 * i], d1 = w[2 * i + 1];
     u32 r[4];
@@ -271,6 +282,11 @@ __device__ __forceinline__ half8 unpack_v(const u32* w, int i) {
                  h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 1.0f, false)),
                  h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 1.0f, true)));
   }
+}
+
+// Token of fp16 number f of a value tile's B operand.
+template <int VF> __device__ constexpr int vtok(int f) {
+  return (VF == INT2 || VF == INT4) ? nib_pos(f) : (f >> 1) + 4 * (f & 1);
 }
 
 // fp16 window values: word i = 8 fp16 (tokens 0..7) in dwords 4i..4i+3.
@@ -665,7 +681,7 @@ attn_mfma(Plan p, Args a) {
         } else if constexpr (KF == FP8) {
           unpack_k_fp8(w, A);
         } else {
-          unpack_k_magic<KF>(w, A);
+          unpack_k_codes<KF>(w, A);
         }
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -735,7 +751,7 @@ attn_mfma(Plan p, Args a) {
         float sv[2], pv[2];
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
-          const int k = i + 4 * hlf;
+          const int k = vtok<VF>(2 * i + hlf);
           sv[hlf] = d.vs[k];
           pv[hlf] = pk[k];
           float zt = d.vz[k];
