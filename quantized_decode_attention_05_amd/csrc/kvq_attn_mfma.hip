@@ -162,8 +162,24 @@ __device__ __forceinline__ u32 fp8_pair(u32 x, int word) {
 // the register order each code width unpacks into.
 template <int KF, bool ROPE>
 __device__ __forceinline__ int kslot(int j, int e) {
+  if (ROPE && KF == INT2) return 16 * (j >> 1) + 4 * (j & 1) + (e >> 1) + 8 * (e & 1);   // (c, c+8)
   if (ROPE || KF == INT8 || KF == FP8) return 8 * j + e;                  // natural
   return 8 * j + nib_pos(e);                                              // INT2 / INT4
+}
+
+// Pre-RoPE INT2 keys only feed fp32 FMAs, so a code need not become an exact
+// integer: register i (0..7) of a code dword holds codes i and i + 8 as the fp16
+// values 1 + c 2^(p_i - 10), the code ORed into the mantissa of 1.0 at bit p_i
+// after at most one shift of the dword (two shifts per dword in all).  The
+// per-pair coefficients absorb the factor 2^(10 - p_i) and the offset; with
+// p_i >= 4 the offset is at most 64 code steps, so the fp32 FMAs lose nothing
+// that matters against the fp16 rounding of the rotated key.
+__device__ constexpr int int2_pos(int i) { return i < 2 ? 4 + 2 * i : (i < 5 ? 2 * i : 2 * i - 6); }
+__device__ __forceinline__ u32 int2_pos_reg(u32 x, int i) {
+  const u32 y = i < 2 ? x << 4 : (i < 5 ? x : x >> 6);
+  u32 r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(y), "v"(0x00030003u << int2_pos(i)), "v"(0x3C003C00u));
+  return r;
 }
 
 template <int F> struct Bits { static constexpr int v = (F == FP8) ? 8 : F; };
@@ -395,7 +411,7 @@ attn_mfma(Plan p, Args a) {
 
   for (int e = tid; e < n_rep * D; e += 256) {
     const int r = e / D, c = e % D;
-    q_s[r][c] = load_in(a.q, ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c, p.in_dtype);
+    q_s[r][c] = load_in(a.q, ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c, p.in_dtype) * a.qscale;
   }
   if constexpr (ROPE) {
     const float2* tab = (const float2*)(arena + p.rope);
@@ -423,9 +439,7 @@ attn_mfma(Plan p, Args a) {
   // fp32 query in two operands).  Lane (n, g) is A row n of PV: value group
   // n / n_rep (rows past the last group are computed and never read).
   const int head = n % n_rep;
-  const bool is_col = true;
   const int vgrp = (n / n_rep) < VG ? n / n_rep : VG - 1;
-  const float qs = a.qscale;
 
   half8 Bq[4], Bl[4];   // query operand (hi, lo) of the current key group / window
   float kbias = 0.0f;   // per-column logit bias from the key zero-points
@@ -451,25 +465,22 @@ attn_mfma(Plan p, Args a) {
       u32 rh[4], rl[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        float vh[2], vl[2];
+        float full[2];
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
           const int e = 2 * e2 + hlf;
           const int cl = natural ? 8 * j + e : kslot<KF, ROPE>(j, e);
-          const float qv = q_s[head][32 * g + cl] * qs;
-          const float full = qv * (sc ? sv[cl] : uniform);
-          const float h = (float)(_Float16)full;
-          vh[hlf] = is_col ? h : 0.0f;
-          vl[hlf] = is_col ? full - h : 0.0f;
-          if (sc) qz += qv * zv[cl];
+          const float qv = q_s[head][32 * g + cl];   // already times the logit scale
+          full[hlf] = qv * (sc ? sv[cl] : uniform);
+          if (sc) qz = __builtin_fmaf(qv, zv[cl], qz);
         }
-        rh[e2] = pk_f16(vh[0], vh[1]);
-        rl[e2] = pk_f16(vl[0], vl[1]);
+        rh[e2] = pk_f16(full[0], full[1]);
+        rl[e2] = f16_residual2(rh[e2], full[0], full[1], a.neg1);
       }
       Bq[j] = pack8(rh[0], rh[1], rh[2], rh[3]);
       Bl[j] = pack8(rl[0], rl[1], rl[2], rl[3]);
     }
-    return is_col ? qz : 0.0f;
+    return qz;
   };
 
   // softmax / output state (lane (n, g): head n for n < n_rep)
@@ -598,7 +609,7 @@ attn_mfma(Plan p, Args a) {
           b_mode = 0;
         }
       } else if (b_mode != 0) {
-        build_b(nullptr, nullptr, k_fp8, true);
+        build_b(nullptr, nullptr, k_fp8, !(ROPE && KF == INT2));
         kbias = 0.0f;
         b_mode = 0;
       }
@@ -615,35 +626,49 @@ attn_mfma(Plan p, Args a) {
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // quantized steps: this k-step's four pair coefficients; window steps:
-        // the coarse angles of its four pairs
+        // Pairs of this k-step (first channel cp[pr], lane-local): natural
+        // (8j + 2pr), or for INT2 codes the channels b, b+2, b+8, b+10 with
+        // b = 16 (j >> 1) + 4 (j & 1), whose rotated values pack as (c, c+8).
+        constexpr bool C8 = KF == INT2 && !RING;
+        int cp[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr)
+          cp[pr] = C8 ? 16 * (j >> 1) + 4 * (j & 1) + 2 * (pr & 1) + 8 * (pr >> 1) : 8 * j + 2 * pr;
+        // quantized steps: the pairs' coefficients; window steps: their coarse angles
         float4 uv[4];
         float2 wv[4], cc[4];
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-          const int pp = 16 * g + 4 * j + pr;
+          const int pp = 16 * g + (cp[pr] >> 1);
           if constexpr (!RING) {
             uv[pr] = ((const float4*)(ring + cur_slot * SLOT + OFF_KM))[pc_pos(pp)];
             wv[pr] = ((const float2*)(ring + cur_slot * SLOT + OFF_KT))[pcw_pos(pp)];
           } else {
-            cc[pr] = crow[4 * j + pr];
+            cc[pr] = crow[cp[pr] >> 1];
           }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const u32* w = u ? d.k1 : d.k0;
           const int dt = tok_in0 + 4 * u;               // token offset in the step (t0 is 32-aligned)
-          u32 r[4], rl[4];
+          float rx[4], ry[4];
 #pragma unroll
           for (int pr = 0; pr < 4; ++pr) {
-            const int e = 8 * j + 2 * pr;
+            const int e = cp[pr];
             const float2 ff = fine_s[16 * g + (e >> 1)][dt ^ (4 * g)];
             float r0, r1;
             if constexpr (!RING) {
               // coarse-rotated pair from its codes, then the fine rotation
-              const u32 c0 = key_code_reg<KF>(w, code_reg<KF>(e)), c1 = key_code_reg<KF>(w, code_reg<KF>(e + 1));
-              const float cx = code_half<KF>(e) ? hi_f(c0) : lo_f(c0);
-              const float cy = code_half<KF>(e + 1) ? hi_f(c1) : lo_f(c1);
+              float cx, cy;
+              if constexpr (C8) {
+                const u32 h0 = int2_pos_reg(w[e >> 4], e & 7), h1 = int2_pos_reg(w[e >> 4], (e & 7) + 1);
+                cx = (e >> 3) & 1 ? hi_f(h0) : lo_f(h0);
+                cy = (e >> 3) & 1 ? hi_f(h1) : lo_f(h1);
+              } else {
+                const u32 c0 = key_code_reg<KF>(w, code_reg<KF>(e)), c1 = key_code_reg<KF>(w, code_reg<KF>(e + 1));
+                cx = code_half<KF>(e) ? hi_f(c0) : lo_f(c0);
+                cy = code_half<KF>(e + 1) ? hi_f(c1) : lo_f(c1);
+              }
               const float px = __builtin_fmaf(cx, uv[pr].x, __builtin_fmaf(cy, uv[pr].z, wv[pr].x));
               const float py = __builtin_fmaf(cx, uv[pr].y, __builtin_fmaf(cy, uv[pr].w, wv[pr].y));
               r0 = px * ff.x - py * ff.y;
@@ -655,8 +680,27 @@ attn_mfma(Plan p, Args a) {
               r0 = k0 * cs - k1 * sn;
               r1 = k0 * sn + k1 * cs;
             }
-            r[pr] = pk_f16(r0, r1);
-            if constexpr (KSPLIT) rl[pr] = f16_residual2(r[pr], r0, r1, a.neg1);
+            rx[pr] = r0;
+            ry[pr] = r1;
+          }
+          // operand registers: natural (pair pr in register pr) or (c, c+8)
+          float lo_v[4], hi_v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (C8) {
+              const int pa = q >> 1;                     // pairs pa (low halves) and pa + 2 (high halves)
+              lo_v[q] = q & 1 ? ry[pa] : rx[pa];
+              hi_v[q] = q & 1 ? ry[pa + 2] : rx[pa + 2];
+            } else {
+              lo_v[q] = rx[q];
+              hi_v[q] = ry[q];
+            }
+          }
+          u32 r[4], rl[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            r[q] = pk_f16(lo_v[q], hi_v[q]);
+            if constexpr (KSPLIT) rl[q] = f16_residual2(r[q], lo_v[q], hi_v[q], a.neg1);
           }
           floatx4& acc = u ? acc1 : acc0;
           const half8 ah = pack8(r[0], r[1], r[2], r[3]);
@@ -699,7 +743,7 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * u + i] = S[u][i] + kbias;
+      for (int i = 0; i < 4; ++i) x[4 * u + i] = ROPE ? S[u][i] : S[u][i] + kbias;   // pre-RoPE: zero-points sit in the pair coefficients
     u32 valid = 0xFFu;
     if constexpr (!FULL) {
       valid = 0;
@@ -802,6 +846,8 @@ attn_mfma(Plan p, Args a) {
   };
 
   const int64_t qs_end = st_end < nq ? st_end : nq;
+  // pre-RoPE INT2 keys: position factors 2^(10 - p) of channel pair `lane` (channels 2 lane, 2 lane + 1)
+  const float2 pf = make_float2((float)(1 << (10 - int2_pos(2 * (lane & 3)))), (float)(1 << (10 - int2_pos(2 * (lane & 3) + 1))));
   {
     // Streaming loop: NB - 1 stages in flight; a stage is consumed (waited
     // for, read into registers), the next stage is issued into the slot freed
@@ -843,9 +889,16 @@ attn_mfma(Plan p, Args a) {
         uint8_t* st_l = ring + sl * SLOT;
         const float2 cs2 = ((const float2*)(st_l + OFF_KT))[lane];
         const int mo = 16 * km_pos(lane >> 1) + 8 * (lane & 1);
-        const float2 s2 = *(const float2*)(st_l + OFF_KM + mo);
-        const float2 z2 = *(const float2*)(st_l + OFF_KM + 4 * D + mo);
+        float2 s2 = *(const float2*)(st_l + OFF_KM + mo);
+        float2 z2 = *(const float2*)(st_l + OFF_KM + 4 * D + mo);
         asm volatile("" ::: "memory");   // every lane's reads before any lane's writes
+        if constexpr (KF == INT2) {
+          // codes arrive as 1 + c 2^(p - 10): x = s c + z = (s f) h + (z - s f), f = 2^(10 - p)
+          s2.x *= pf.x;
+          s2.y *= pf.y;
+          z2.x -= s2.x;
+          z2.y -= s2.y;
+        }
         ((float4*)(st_l + OFF_KM))[pc_pos(lane)] = make_float4(s2.x * cs2.x, s2.x * cs2.y, -s2.y * cs2.y, s2.y * cs2.x);
         ((float2*)(st_l + OFF_KT))[pcw_pos(lane)] =
             make_float2(cs2.x * z2.x - cs2.y * z2.y, cs2.y * z2.x + cs2.x * z2.y);
