@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels.  Torch tensors are used
 for device memory and streams: the wrappers pass ``data_ptr()`` and the
 current HIP stream.  Importing this module fails loudly when the library has
-not been built (``python -m quantized_decode_attention_05_amd.build``).
+not been built (``python quantized_decode_attention_05_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      f"`python -m quantized_decode_attention_05_amd.build`")
+                      f"`python quantized_decode_attention_05_amd/build.py`")
 _lib = C.CDLL(LIB_PATH)
 
 # ---- constants (mirror include/kvq.h) ------------------------------------------

@@ -1,6 +1,7 @@
 """Build libkvq.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m quantized_decode_attention_05_amd.build [--jobs N]
+Usage: python quantized_decode_attention_05_amd/build.py [--jobs N]
+(or __graft_entry__.build(); importing it through the package needs the built library)
 """
 from __future__ import annotations
 
