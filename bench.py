@@ -261,7 +261,7 @@ def main():
         vn = torch.from_numpy(W.full_new_tokens(name, "v").view(np.int16)).view(torch.bfloat16).to(dev)
     arena = torch.empty(K.kvq_arena_bytes(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(K.kvq_workspace_bytes(cfg, cap, a.kernel, a.splits), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(K.kvq_workspace_bytes(cfg, cap, a.kernel, a.splits), dtype=torch.uint8, device=dev)
     sm = 1.0 / math.sqrt(D)
     print(f"[bench] prefill T={T0}", file=sys.stderr, flush=True)
     K.kvq_quantize_append(cfg, arena, 0, kp, vp, flags=K.CALIBRATE if calibrate else 0)

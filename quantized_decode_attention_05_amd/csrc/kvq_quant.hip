@@ -130,41 +130,37 @@ __global__ void __launch_bounds__(256) reduce_tensor(Plan p, Src s, int64_t t_le
 
 // ---- encode kernels ------------------------------------------------------------
 
-// K rows: one thread per (token, dword of the row).
-__global__ void encode_k_rows(Plan p, Src s, int64_t t_lo, int64_t t_len) {
+// K rows: one work item per (token, dword of the row).
+__device__ __forceinline__ void encode_k_item(const Plan& p, const Src& s, int64_t t_lo, int64_t t_len,
+                                              int64_t i) {
   const int dw_per_row = p.k_row_bytes / 4;
   const int per = 32 / p.k.bits;                 // channels per dword
-  const int64_t total = (int64_t)p.B * p.Hkv * t_len * dw_per_row;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int j = (int)(i % dw_per_row);
-    int64_t r = i / dw_per_row;
-    const int64_t t = t_lo + r % t_len;
-    r /= t_len;
-    const int h = (int)(r % p.Hkv), b = (int)(r / p.Hkv);
-    uint32_t word = 0;
-    for (int u = 0; u < per; ++u) {
-      const int c = j * per + u;
-      const float x = src_val<SIDE_K>(p, s, b, h, t, c);
-      const uint32_t code = encode_elem(p, p.k, s.arena, b, h, t, c, x);
-      word |= (p.k.bits == 32 ? code : (code & ((1u << p.k.bits) - 1))) << (u * p.k.bits);
-    }
-    const int64_t bh = (int64_t)b * p.Hkv + h;
-    uint32_t* row = (uint32_t*)((uint8_t*)s.arena + p.k.codes + (bh * p.Tc + t) * p.k_row_bytes);
-    row[j] = word;
+  const int j = (int)(i % dw_per_row);
+  int64_t r = i / dw_per_row;
+  const int64_t t = t_lo + r % t_len;
+  r /= t_len;
+  const int h = (int)(r % p.Hkv), b = (int)(r / p.Hkv);
+  uint32_t word = 0;
+  for (int u = 0; u < per; ++u) {
+    const int c = j * per + u;
+    const float x = src_val<SIDE_K>(p, s, b, h, t, c);
+    const uint32_t code = encode_elem(p, p.k, s.arena, b, h, t, c, x);
+    word |= (p.k.bits == 32 ? code : (code & ((1u << p.k.bits) - 1))) << (u * p.k.bits);
   }
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  uint32_t* row = (uint32_t*)((uint8_t*)s.arena + p.k.codes + (bh * p.Tc + t) * p.k_row_bytes);
+  row[j] = word;
 }
 
-// V blocks: one thread per word (8 tokens x 1 channel).  Words only partly
+// V blocks: one work item per word (8 tokens x 1 channel).  Words only partly
 // inside [t_lo, t_lo + t_len) keep their other codes (read-modify-write).
-__global__ void encode_v_blocks(Plan p, Src s, int64_t t_lo, int64_t t_len) {
+__device__ __forceinline__ void encode_v_item(const Plan& p, const Src& s, int64_t t_lo, int64_t t_len,
+                                              int64_t i) {
   const int bits = p.v.bits;
   const int words_per_block = 64 * (p.D / 16);
   const int64_t blk_lo = t_lo / kVBlock, blk_hi = (t_lo + t_len - 1) / kVBlock + 1;
   const int64_t nblk = blk_hi - blk_lo;
-  const int64_t total = (int64_t)p.B * p.Hkv * nblk * words_per_block;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  {
     const int w = (int)(i % words_per_block);
     int64_t r = i / words_per_block;
     const int64_t blk = blk_lo + r % nblk;
@@ -202,43 +198,42 @@ __global__ void encode_v_blocks(Plan p, Src s, int64_t t_lo, int64_t t_len) {
   }
 }
 
-// fp16 window: token t -> slot t mod Rs of ring K (rows) and ring V (blocks).
-__global__ void write_ring(Plan p, Src s, int64_t w_lo, int64_t w_len) {
-  const int64_t total = (int64_t)p.B * p.Hkv * w_len * p.D;
-  const int rblock = kVBlock * p.D * 2;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+// K rows and V blocks of tokens [t_lo, t_lo + t_len) in one launch: items
+// [0, nk) are K-row dwords, [nk, nk + nv) V-block words (disjoint bytes).
+__global__ void encode_kv(Plan p, Src sk, Src sv, int64_t t_lo, int64_t t_len, int64_t nk, int64_t nv) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nk + nv;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(i % p.D);
-    int64_t r = i / p.D;
-    const int64_t t = w_lo + r % w_len;
-    r /= w_len;
-    const int h = (int)(r % p.Hkv), b = (int)(r / p.Hkv);
-    const int64_t bh = (int64_t)b * p.Hkv + h;
-    const int64_t slot = t % p.Rs;
-    const int64_t src = (bh * s.n + (t - s.t0)) * p.D + c;
-    const _Float16 kx = (_Float16)load_in(s.in, src, p.in_dtype);
-    ((_Float16*)(s.arena + p.ring_k))[(bh * p.Rs + slot) * p.D + c] = kx;
-    (void)kx;
+    if (i < nk) encode_k_item(p, sk, t_lo, t_len, i);
+    else encode_v_item(p, sv, t_lo, t_len, i - nk);
   }
 }
 
-__global__ void write_ring_v(Plan p, const uint8_t* arena_c, const void* vin, int64_t t0, int n,
-                             int64_t w_lo, int64_t w_len) {
-  uint8_t* arena = (uint8_t*)arena_c;
-  const int64_t total = (int64_t)p.B * p.Hkv * w_len * p.D;
+// fp16 window: token t -> slot t mod Rs of ring K (rows) and ring V (blocks),
+// both in one launch: items [0, n) write keys, [n, 2n) values.
+__global__ void write_ring_kv(Plan p, Src sk, const void* vin, int64_t w_lo, int64_t w_len) {
+  uint8_t* arena = (uint8_t*)sk.arena;
+  const int64_t n = (int64_t)p.B * p.Hkv * w_len * p.D;
   const int rblock = kVBlock * p.D * 2;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < 2 * n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(i % p.D);
-    int64_t r = i / p.D;
+    const bool is_v = i >= n;
+    const int64_t e = is_v ? i - n : i;
+    const int c = (int)(e % p.D);
+    int64_t r = e / p.D;
     const int64_t t = w_lo + r % w_len;
     r /= w_len;
     const int h = (int)(r % p.Hkv), b = (int)(r / p.Hkv);
     const int64_t bh = (int64_t)b * p.Hkv + h;
     const int64_t slot = t % p.Rs;
-    const _Float16 vx = (_Float16)load_in(vin, (bh * n + (t - t0)) * p.D + c, p.in_dtype);
-    uint8_t* base = arena + p.ring_v + (uint64_t)bh * (p.Rs / kVBlock) * rblock;
-    ((_Float16*)(base + vblock_word_byte(slot, c, p.D, 16, rblock)))[slot & 7] = vx;
+    const int64_t src = (bh * sk.n + (t - sk.t0)) * p.D + c;
+    if (!is_v) {
+      const _Float16 kx = (_Float16)load_in(sk.in, src, p.in_dtype);
+      ((_Float16*)(arena + p.ring_k))[(bh * p.Rs + slot) * p.D + c] = kx;
+    } else {
+      const _Float16 vx = (_Float16)load_in(vin, src, p.in_dtype);
+      uint8_t* base = arena + p.ring_v + (uint64_t)bh * (p.Rs / kVBlock) * rblock;
+      ((_Float16*)(base + vblock_word_byte(slot, c, p.D, 16, rblock)))[slot & 7] = vx;
+    }
   }
 }
 
@@ -389,10 +384,9 @@ hipError_t launch_quantize_range(const Plan& p, void* arena, int64_t t0, int n_n
   launch_reduce<SIDE_V>(p, sv, q_lo, q_hi, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t kw = (int64_t)p.B * p.Hkv * len * (p.k_row_bytes / 4);
-  hipLaunchKernelGGL(encode_k_rows, dim3(grid_for(kw, 256)), dim3(256), 0, s, p, sk, q_lo, len);
   const int64_t nblk = (q_hi - 1) / kVBlock - q_lo / kVBlock + 1;
   const int64_t vw = (int64_t)p.B * p.Hkv * nblk * 64 * (p.D / 16);
-  hipLaunchKernelGGL(encode_v_blocks, dim3(grid_for(vw, 256)), dim3(256), 0, s, p, sv, q_lo, len);
+  hipLaunchKernelGGL(encode_kv, dim3(grid_for(kw + vw, 256)), dim3(256), 0, s, p, sk, sv, q_lo, len, kw, vw);
   return hipGetLastError();
 }
 
@@ -401,9 +395,7 @@ hipError_t launch_ring_write(const Plan& p, void* arena, int64_t t0, int n_new, 
   Src sk{(const uint8_t*)arena, k_new, t0, n_new};
   const int64_t w_len = t0 + n_new - w_lo;
   const int64_t total = (int64_t)p.B * p.Hkv * w_len * p.D;
-  hipLaunchKernelGGL(write_ring, dim3(grid_for(total, 256)), dim3(256), 0, s, p, sk, w_lo, w_len);
-  hipLaunchKernelGGL(write_ring_v, dim3(grid_for(total, 256)), dim3(256), 0, s, p,
-                     (const uint8_t*)arena, v_new, t0, n_new, w_lo, w_len);
+  hipLaunchKernelGGL(write_ring_kv, dim3(grid_for(2 * total, 256)), dim3(256), 0, s, p, sk, v_new, w_lo, w_len);
   return hipGetLastError();
 }
 

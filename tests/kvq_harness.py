@@ -83,8 +83,10 @@ class GpuCache:
         T = self.T if T is None else T
         c = self.case
         q = to_dev(q_payload, c.dtype)
-        out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda")
-        ws = torch.empty(K.kvq_workspace_bytes(self.cfg, T, kernel, num_splits), dtype=torch.uint8,
+        # poisoned, so an output the kernels never write cannot pass on a
+        # stale buffer the allocator hands back
+        out = torch.full((c.B, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(K.kvq_workspace_bytes(self.cfg, T, kernel, num_splits), dtype=torch.uint8,
                          device="cuda")
         sm = 1.0 / math.sqrt(c.D) if sm_scale is None else sm_scale
         K.kvq_decode_attention(self.cfg, self.arena, T, q, out, sm, ws, kernel, num_splits)
@@ -94,8 +96,8 @@ class GpuCache:
     def dequantize(self, T=None, bh_sel=None):
         T = self.T if T is None else T
         c = self.case
-        ko = torch.empty((c.B, c.Hkv, T, c.D), dtype=torch.float32, device="cuda")
-        vo = torch.empty_like(ko)
+        ko = torch.full((c.B, c.Hkv, T, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        vo = torch.full_like(ko, float("nan"))
         K.kvq_dequantize(self.cfg, self.arena, T, ko, vo)
         torch.cuda.synchronize()
         if bh_sel is not None:

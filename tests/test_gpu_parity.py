@@ -178,3 +178,33 @@ def test_attention_deterministic_and_split_invariant():
         for kern in (K.KERNEL_GENERIC, K.KERNEL_MFMA):
             o = gc.attention(qp, num_splits=s, kernel=kern)
             assert attention_error(o, qf, st, case) <= ATTN_TOL
+
+
+def test_one_workspace_many_calls():
+    """One workspace serves successive calls with different split counts: each
+    call has to write every output (out is poisoned with NaN first), agree with
+    the oracle, and give the same result for the same split count."""
+    import math
+    import torch
+    case = Case(B=3, Hq=24, Hkv=3, D=128, dtype="bf16", k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128)
+    T = 2400
+    gc, st, _ = run_case(case, T, [T], seed=23, kernels=[K.KERNEL_GENERIC])
+    (qf, qp) = W.random_queries(23, case.B, case.Hq, case.D, dtype="bf16")
+    from tests.kvq_harness import to_dev
+    q = to_dev(qp, case.dtype)
+    nbytes = max(K.kvq_workspace_bytes(gc.cfg, T, K.KERNEL_MFMA, s) for s in (1, 2, 3, 7, 16, 37))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
+    first = None
+    for s in (2, 1, 3, 7, 16, 37, 2, 2):
+        out.fill_(float("nan"))
+        K.kvq_decode_attention(gc.cfg, gc.arena, T, q, out, 1.0 / math.sqrt(case.D), ws, K.KERNEL_MFMA, s)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.isfinite(o).all(), f"splits={s}: outputs not written"
+        assert attention_error(o, qf, st, case) <= ATTN_TOL, s
+        if s == 2:
+            if first is None:
+                first = o
+            else:
+                assert np.array_equal(o, first), "same split count, different result"
