@@ -20,8 +20,9 @@ What it computes, per (sequence, kv head) unless stated:
   per-tensor = one group per (sequence, kv head); per-channel = one group per
   channel over G consecutive tokens from position 0 (G = 0: all tokens);
   per-token = one group per token over Gc consecutive channels (Gc = 0: all).
-* FP8: one scale per kv head, absmax / 448 over the first call's tokens of all
-  sequences (calibrated) or a caller-supplied / unit scale.
+* FP8 E4M3: one scale per kv head, absmax / 448 over the first call's tokens
+  of all sequences (calibrated) or a caller-supplied / unit scale.
+* FP8 E5M2: no scales (unit scale per kv head).
 
 It also writes the documented byte layout of codes (K rows, V 32-token
 blocks, fp16 ring) so tests can compare the library's cache bytes directly.
@@ -34,7 +35,7 @@ import numpy as np
 
 from . import quant as Q
 
-NONE, INT_ASYM, INT_SYM, FP8_E4M3 = 0, 1, 2, 3
+NONE, INT_ASYM, INT_SYM, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_CHANNEL, PER_TOKEN = 0, 1, 2
 VBLOCK = 32          # tokens per V code block
 RING_ALIGN = 32      # ring slots are a multiple of this
@@ -120,6 +121,10 @@ def quantize_part(x: np.ndarray, spec: Spec, fp8_scale=None):
         s = np.asarray(fp8_scale, dtype=np.float32).reshape(1, H, 1, 1)
         codes = Q.fp8_quantize(x, s)
         return dict(codes=codes, scale=s.reshape(H), zero=None, deq=Q.fp8_dequantize(codes, s))
+    if spec.scheme == FP8_E5M2:
+        # no scales: the value itself is encoded (unit scale per kv head)
+        codes = Q.e5m2_encode(x)
+        return dict(codes=codes, scale=np.ones(H, dtype=np.float32), zero=None, deq=Q.e5m2_decode(codes))
 
     if spec.axis == PER_TENSOR:
         xg = x.reshape(B, H, 1, T * D)
@@ -197,7 +202,7 @@ def quantize_cache(cfg: Cfg, K: np.ndarray, V: np.ndarray, T: int,
 def code_bits(spec: Spec) -> int:
     if spec.scheme == NONE:
         return spec.bits
-    if spec.scheme in (FP8_E4M3, INT_SYM):
+    if spec.scheme in (FP8_E4M3, FP8_E5M2, INT_SYM):
         return 8
     return spec.bits
 
@@ -314,6 +319,8 @@ def dequantize_part(part: dict, spec: Spec) -> np.ndarray:
         return codes.astype(np.float32)
     if spec.scheme == FP8_E4M3:
         return Q.fp8_dequantize(codes, part["scale"].reshape(1, H, 1, 1))
+    if spec.scheme == FP8_E5M2:
+        return Q.e5m2_decode(codes)
     s, z = part["scale"], part["zero"]
     if spec.axis == PER_TENSOR:
         sb = s.reshape(B, H, 1, 1)

@@ -20,6 +20,10 @@ ties to even):
 * FP8 E4M3 (same page, section "Why do per-tensor scales waste bits on the K
   cache?": 3 mantissa bits, saturation at +-448): encoded here by an explicit
   nearest-point search over the 254 finite code points, ties to the even code.
+* FP8 E5M2 (same section: 2 mantissa bits, saturation at +-57344; the section
+  "How do I turn it on in vLLM without wrecking long context?" adds that it
+  needs no scales): OCP E5M2, bias 15, the same nearest-point search over its
+  246 finite code points, applied to the value itself (unit scale).
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ import numpy as np
 F32 = np.float32
 EPS = F32(1e-8)          # floor on (max - min) of the min-max listing; reused for absmax
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 
 def stage(x: np.ndarray, through_fp16: bool) -> np.ndarray:
@@ -149,3 +154,52 @@ def fp8_quantize(x: np.ndarray, scale) -> np.ndarray:
 
 def fp8_dequantize(codes: np.ndarray, scale) -> np.ndarray:
     return (e4m3_decode(codes) * np.asarray(scale, dtype=F32)).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# FP8 E5M2 (OCP: bias 15, exponent field 31 = infinities and NaNs)
+# ----------------------------------------------------------------------------
+
+def e5m2_value_of_code(code) -> np.ndarray:
+    """Closed-form value of E5M2 code bytes (float64; +-inf for 0x7C / 0xFC,
+    NaN for 0x7D-0x7F / 0xFD-0xFF)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    mag = np.where(e == 0, (m / 4.0) * 2.0 ** -14, (1.0 + m / 4.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def _e5m2_grid():
+    codes = np.arange(0x7C, dtype=np.int64)             # 0x00 .. 0x7B (0x7C is +inf)
+    vals = e5m2_value_of_code(codes)
+    assert np.all(np.diff(vals) > 0)
+    return codes, vals
+
+
+_GRID5_CODES, _GRID5_VALS = _e5m2_grid()
+
+
+def e5m2_encode(y: np.ndarray) -> np.ndarray:
+    """Encode fp32 values to E5M2 bytes: saturate to +-57344, then round to
+    the nearest representable magnitude with ties to the even code; the sign
+    bit is kept (-0.0 -> 0x80).  Inputs are assumed finite."""
+    y = np.asarray(y, dtype=F32)
+    a = np.minimum(np.abs(y).astype(np.float64), E5M2_MAX)
+    hi = np.searchsorted(_GRID5_VALS, a, side="left")
+    hi = np.clip(hi, 0, len(_GRID5_VALS) - 1)
+    lo = np.clip(hi - 1, 0, len(_GRID5_VALS) - 1)
+    d_hi = _GRID5_VALS[hi] - a
+    d_lo = a - _GRID5_VALS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & ((_GRID5_CODES[lo] & 1) == 0))
+    mag_code = np.where(pick_lo, _GRID5_CODES[lo], _GRID5_CODES[hi])
+    mag_code = np.where(a == _GRID5_VALS[hi], _GRID5_CODES[hi], mag_code)
+    sign = np.signbit(y).astype(np.int64) << 7
+    return (mag_code | sign).astype(np.uint8)
+
+
+def e5m2_decode(codes: np.ndarray) -> np.ndarray:
+    """E5M2 bytes -> float32 (exact)."""
+    return e5m2_value_of_code(codes).astype(F32)

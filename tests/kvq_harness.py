@@ -118,7 +118,7 @@ class GpuCache:
 
 def _meta_shape(spec, B, H, D, Tc, Tq):
     scheme, bits, axis, group = spec
-    if scheme == OC.FP8_E4M3:
+    if scheme in (OC.FP8_E4M3, OC.FP8_E5M2):
         return None
     if axis == OC.PER_TENSOR:
         return (B, H, 1, 1), (B, H, 1, 1)
@@ -162,7 +162,7 @@ def compare_sections(gc: GpuCache, st: dict, bh_sel=None):
 
     for side, spec in (("k", c.k), ("v", c.v)):
         part = st[side]
-        if spec[0] == OC.FP8_E4M3:
+        if spec[0] in (OC.FP8_E4M3, OC.FP8_E5M2):
             off = getattr(lay, side + "_scale")
             s = arena[off: off + 4 * H].cpu().numpy().view(np.float32)
             if bh_sel is not None:

@@ -152,3 +152,20 @@ def test_residual_bugs_are_caught(monkeypatch, bug):
     else:
         monkeypatch.setattr(C, "has_window", lambda cfg: False)
         assert _fails(P.test_window_holds_fp16_values)
+
+
+def test_e5m2_missing_saturation_is_caught(monkeypatch):
+    orig = Q.e5m2_encode
+
+    def nosat(y):
+        y = np.asarray(y, dtype=np.float32)
+        c = orig(y)
+        return np.where(np.abs(y) > 57344, c | 0x7C, c).astype(np.uint8)   # overflow to infinity
+    monkeypatch.setattr(Q, "e5m2_encode", nosat)
+    assert _fails(P.test_e5m2_page_facts)
+
+
+def test_e5m2_wrong_bias_is_caught(monkeypatch):
+    orig = Q.e5m2_value_of_code
+    monkeypatch.setattr(Q, "e5m2_value_of_code", lambda c: orig(c) * 2.0)   # bias 14
+    assert _fails(P.test_e5m2_grid_matches_library_decode)

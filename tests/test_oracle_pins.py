@@ -214,6 +214,68 @@ def test_e4m3_encode_matches_library_cast_after_clamp():
     assert sp == [0x80, 0x00, 0x02]
 
 
+# ---------------------------------------------------------------------------
+# FP8 E5M2: closed-form grid, page facts, library cross-check
+# ---------------------------------------------------------------------------
+
+def test_e5m2_grid_matches_library_decode():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = Q.e5m2_value_of_code(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(nan, np.isnan(mine))
+    assert nan.sum() == 6
+    fin = ~nan
+    assert np.array_equal(mine[fin], lib[fin])          # includes +-inf at 0x7C / 0xFC
+
+
+def test_e5m2_page_facts():
+    g = _gold("e5m2_format_facts.json")["facts"]
+    vals = Q.e5m2_value_of_code(np.arange(0x7C))
+    assert vals.max() == g["e5m2_max_finite"]
+    mant = g["e5m2_mantissa_bits"]
+    # relative rounding error <= 2^-(mantissa bits + 1) in the normal range
+    rng = np.random.default_rng(3)
+    y = np.exp(rng.uniform(np.log(2.0 ** -14), np.log(57344.0), 20000)).astype(np.float32)
+    rel = np.abs(Q.e5m2_decode(Q.e5m2_encode(y)) - y) / y
+    assert rel.max() <= 2.0 ** -(mant + 1) + 1e-9
+    assert rel.max() > 0.1
+    # saturation instead of infinity beyond the range
+    big = np.array([57344, 60000, 61439, 61440, 1e9, -1e9], dtype=np.float32)
+    assert Q.e5m2_encode(big).tolist() == [0x7B] * 4 + [0x7B, 0xFB]
+    # one byte of E5M2 is the high byte of the fp16 with the same value
+    fin = np.arange(0x7C, dtype=np.uint16)
+    as_f16 = (fin << np.uint16(8)).view(np.float16).astype(np.float64)
+    assert np.array_equal(as_f16, Q.e5m2_value_of_code(fin))
+
+
+def test_e5m2_encode_matches_library_cast_after_clamp():
+    rng = np.random.default_rng(4)
+    grid = Q.e5m2_value_of_code(np.arange(0x7C))
+    y = np.concatenate([
+        rng.standard_normal(50000).astype(np.float32) * 40,
+        rng.standard_normal(20000).astype(np.float32) * 1e-4,
+        rng.standard_normal(20000).astype(np.float32) * 2e4,
+        grid.astype(np.float32),
+        ((grid[:-1] + grid[1:]) / 2).astype(np.float32),   # exact ties
+        np.array([0.0, -0.0, 2.0 ** -17, 3 * 2.0 ** -18, 2.0 ** -16], dtype=np.float32),
+    ])
+    y = np.concatenate([y, -y])
+    mine = Q.e5m2_encode(y)
+    lib = torch.from_numpy(np.clip(y, -57344, 57344)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(mine, lib)
+    sp = Q.e5m2_encode(np.array([-0.0, 2.0 ** -17, 3 * 2.0 ** -17], dtype=np.float32)).tolist()
+    assert sp == [0x80, 0x00, 0x02]
+
+
+def test_e5m2_cache_has_unit_scale():
+    x = np.array([[[[1.0, -70000.0, 3.3]]]], dtype=np.float32)
+    part = C.quantize_part(x, C.Spec(C.FP8_E5M2, 8, 0, 0))
+    assert part["scale"].tolist() == [1.0]
+    assert part["codes"].ravel().tolist() == [0x3C, 0xFB, 0x43]   # 3.3 -> 1.75 * 2^1
+    assert part["deq"].ravel().tolist() == [1.0, -57344.0, 3.5]
+
+
 def test_fp8_scale_calibration():
     assert float(Q.fp8_scale_from_absmax(np.float32(448.0))) == 1.0
     assert float(Q.fp8_scale_from_absmax(np.float32(0.0))) == 1.0
