@@ -30,11 +30,13 @@ HBM_PEAK_GBS = 8000.0
 # cache format of each workload: (k spec, v spec, residual, pre-RoPE, calibrate)
 FORMATS = {
     "c3_fp8_e4m3_gqa_8k": ((3, 8, 0, 0), (3, 8, 0, 0), 0, False, True),
+    "c3_fp8_e5m2_gqa_8k": ((4, 8, 0, 0), (4, 8, 0, 0), 0, False, False),
     "c4_int4_llama70b_128k": ((1, 4, 1, 128), (1, 4, 2, 0), 128, False, False),
     "c5_int2_kivi_prerope_32k": ((1, 2, 1, 32), (1, 2, 2, 32), 32, True, False),
 }
 DESCR = {
     "c3_fp8_e4m3_gqa_8k": "FP8 E4M3 K/V, per-kv-head calibrated scales",
+    "c3_fp8_e5m2_gqa_8k": "FP8 E5M2 K/V, no scales",
     "c4_int4_llama70b_128k": "INT4 K per-channel G128 + INT4 V per-token, fp16 window 128",
     "c5_int2_kivi_prerope_32k": "INT2 K per-channel G32 (pre-RoPE) + INT2 V per-token G32, fp16 window 32",
 }
@@ -65,7 +67,7 @@ def algorithmic_bytes(w, fmt, T):
                 per += 4 * nmeta
     per += (T - Tq) * D * 2 * 2
     total = per * B * Hkv
-    fp8_scales = 8 * Hkv if kspec[0] == 3 else 0
+    fp8_scales = 8 * Hkv if kspec[0] in (3, 4) else 0
     return total + fp8_scales + B * Hq * D * 2 + B * Hq * D * 4, Tq
 
 
@@ -330,7 +332,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int2+fp32" if kspec[1] == 2 else ("fp8+fp32" if kspec[0] == 3 else "int4+fp32"),
+        "dtype": "int2+fp32" if kspec[1] == 2 else ({3: "fp8e4m3+fp32", 4: "fp8e5m2+fp32"}.get(kspec[0], "int4+fp32")),
         "data": "synthetic (seeded Gaussian K/V with fixed outlier key channels, bf16)",
         "config": {
             "workload": name, "format": DESCR[name], "batch": B, "q_heads": Hq, "kv_heads": Hkv,

@@ -70,7 +70,12 @@ enum kvq_scheme {
   KVQ_NONE     = 0,  /* unquantized: bits 16 -> fp16 storage, 32 -> fp32          */
   KVQ_INT_ASYM = 1,  /* asymmetric min-max: bits 2, 4 or 8, codes in [0, 2^b-1]    */
   KVQ_INT_SYM  = 2,  /* symmetric absmax INT8: bits 8, codes in [-127, 127]        */
-  KVQ_FP8_E4M3 = 3   /* OCP E4M3FN bytes with one fp32 scale per kv head           */
+  KVQ_FP8_E4M3 = 3,  /* OCP E4M3FN bytes with one fp32 scale per kv head           */
+  KVQ_FP8_E5M2 = 4   /* OCP E5M2 bytes, no scales (stored scale fixed at 1.0);      */
+                     /* saturates at +-57344 ("FP8 KV Cache Quantization: Why Keys */
+                     /* Break Before Values", sections "Why do per-tensor scales  */
+                     /* waste bits on the K cache?" and "How do I turn it on in   */
+                     /* vLLM without wrecking long context?")                     */
 };
 enum kvq_axis {      /* grouping axis of INT schemes (ignored for NONE / FP8)      */
   KVQ_PER_TENSOR  = 0, /* one (scale, zero) per (sequence, kv head)                */
@@ -114,7 +119,7 @@ typedef struct kvq_config {
  *                                of byte c*bK/8, low bits first; INT_SYM is
  *                                two's complement; NONE stores fp16/fp32 LE.
  *  k_scale  fp32 PER_TENSOR [B][H]; PER_CHANNEL [B][H][Tc/G or 1][D];
- *                PER_TOKEN [B][H][Tc][D/Gc]; FP8 [H].
+ *                PER_TOKEN [B][H][Tc][D/Gc]; FP8 [H] (1.0 for E5M2).
  *  k_zero   fp32, same shape as k_scale (INT_ASYM only; the group minimum).
  *  v_codes  [B][H][Tc/32][32*D*bV/8]  32-token blocks: token t = 32*blk +
  *                8*g + k and channel c = 16*i + n go to word i of lane
@@ -164,11 +169,14 @@ int64_t kvq_quantized_tokens(const kvq_config* cfg, int64_t T);
  * Append n_new tokens at positions [t0, t0 + n_new) of every sequence.
  *   k_new, v_new: device [B][Hkv][n_new][D] in cfg->in_dtype (values as
  *                 computed by the model: pre-RoPE keys when cfg->pre_rope_k).
- *   k_scale, v_scale: FP8 only; device fp32 [Hkv] scales to store at t0 == 0,
- *                 or NULL.  With KVQ_CALIBRATE (t0 == 0 only) the scales are
- *                 absmax/448 per kv head over this call's tokens of all
- *                 sequences; with neither, 1.0.  Later calls reuse the stored
- *                 scales and saturate values beyond +-448*scale.
+ *   k_scale, v_scale: FP8 E4M3 only; device fp32 [Hkv] scales to store at
+ *                 t0 == 0, or NULL.  With KVQ_CALIBRATE (t0 == 0 only) the
+ *                 scales are absmax/448 per kv head over this call's tokens of
+ *                 all sequences; with neither, 1.0.  Later calls reuse the
+ *                 stored scales and saturate values beyond +-448*scale.  An
+ *                 E5M2 side takes no scale (KVQ_ERR_INVALID_ARG if one is
+ *                 passed for it), ignores KVQ_CALIBRATE, stores 1.0 and
+ *                 saturates beyond +-57344.
  * A cache is started by a call with t0 == 0, which also writes the RoPE tables.
  * Tokens that leave the fp16 window are quantized in blocks of Gt ("folds");
  * the result equals quantizing the same tokens in one call.

@@ -27,7 +27,7 @@ _lib = C.CDLL(LIB_PATH)
 KVQ_OK = 0
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_CAPACITY",
           -4: "KVQ_ERR_ALIGN", -5: "KVQ_ERR_NULL", -6: "KVQ_ERR_WORKSPACE", -7: "KVQ_ERR_HIP"}
-NONE, INT_ASYM, INT_SYM, FP8_E4M3 = 0, 1, 2, 3
+NONE, INT_ASYM, INT_SYM, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_CHANNEL, PER_TOKEN = 0, 1, 2
 F32, F16, BF16 = 0, 1, 2
 CALIBRATE = 1

@@ -22,6 +22,7 @@ static int check_spec(const kvq_tensor_spec& s, int D) {
       if (s.bits != 16 && s.bits != 32) return KVQ_ERR_INVALID_ARG;
       return KVQ_OK;
     case KVQ_FP8_E4M3:
+    case KVQ_FP8_E5M2:
       if (s.bits != 8) return KVQ_ERR_INVALID_ARG;
       return KVQ_OK;
     case KVQ_INT_SYM:
@@ -64,7 +65,7 @@ static void side_meta(const kvq_tensor_spec& s, int D, int64_t Tc, int Hkv, Side
   f->group = s.group;
   f->meta_cols = 0;
   f->meta_rows = 0;
-  if (s.scheme == KVQ_FP8_E4M3) {
+  if (is_fp8(s.scheme)) {
     f->meta_rows = 1;
     f->meta_cols = 1;
   } else if (is_int(s.scheme)) {
@@ -122,7 +123,7 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   const uint64_t NA = UINT64_MAX;
   p->k.codes = take(BH * p->Tc * p->k_row_bytes);
   auto meta_bytes = [&](const SideFmt& f) -> uint64_t {
-    if (f.scheme == KVQ_FP8_E4M3) return (uint64_t)p->Hkv * 4;
+    if (is_fp8(f.scheme)) return (uint64_t)p->Hkv * 4;
     return BH * f.meta_rows * f.meta_cols * 4;
   };
   p->k.scale = (p->k.scheme == KVQ_NONE) ? NA : take(meta_bytes(p->k));
@@ -134,7 +135,7 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   p->ring_v = p->window ? take(BH * p->Rs * D * 2) : NA;
   p->rope_rows = p->Tc / kVBlock + 1;
   p->rope = p->pre_rope ? take((uint64_t)(kVBlock + p->rope_rows) * (D / 2) * 2 * 4) : NA;
-  const bool fp8 = p->k.scheme == KVQ_FP8_E4M3 || p->v.scheme == KVQ_FP8_E4M3;
+  const bool fp8 = is_fp8(p->k.scheme) || is_fp8(p->v.scheme);
   p->fp8_calib = fp8 ? take((uint64_t)2 * p->Hkv * 4) : NA;
   p->total = off;
   return KVQ_OK;
@@ -229,9 +230,12 @@ int kvq_quantize_append(const kvq_config* cfg, void* arena, int64_t t0, int32_t 
   if (flags & ~KVQ_CALIBRATE) return KVQ_ERR_INVALID_ARG;
   if (t0 < 0 || n_new < 0) return KVQ_ERR_INVALID_ARG;
   if (t0 + n_new > p.max_tokens) return KVQ_ERR_CAPACITY;
-  const bool fp8 = p.k.scheme == KVQ_FP8_E4M3 || p.v.scheme == KVQ_FP8_E4M3;
+  const bool fp8 = is_fp8(p.k.scheme) || is_fp8(p.v.scheme);
   if ((flags & KVQ_CALIBRATE) && (!fp8 || t0 != 0)) return KVQ_ERR_INVALID_ARG;
   if ((k_scale || v_scale) && (!fp8 || t0 != 0 || (flags & KVQ_CALIBRATE))) return KVQ_ERR_INVALID_ARG;
+  // E5M2 takes no scale
+  if ((k_scale && p.k.scheme != KVQ_FP8_E4M3) || (v_scale && p.v.scheme != KVQ_FP8_E4M3))
+    return KVQ_ERR_INVALID_ARG;
   if (p.one_shot && t0 != 0) return KVQ_ERR_UNSUPPORTED;
   if (n_new == 0) return KVQ_OK;
   if (!arena || !k_new || !v_new) return KVQ_ERR_NULL;

@@ -64,7 +64,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr u32 kMagic = 0x64006400u;    // fp16 1024 in both halves
 
-enum Fmt { INT2 = 2, INT4 = 4, INT8 = 8, FP8 = 9 };
+enum Fmt { INT2 = 2, INT4 = 4, INT8 = 8, FP8 = 9, BF8 = 10 };   // FP8: E4M3, BF8: E5M2
+__host__ __device__ constexpr bool is_f8(int f) { return f == FP8 || f == BF8; }
 
 struct Args {
   const uint8_t* arena;
@@ -182,7 +183,7 @@ __device__ __forceinline__ u32 int2_pos_reg(u32 x, int i) {
   return r;
 }
 
-template <int F> struct Bits { static constexpr int v = (F == FP8) ? 8 : F; };
+template <int F> struct Bits { static constexpr int v = is_f8(F) ? 8 : F; };
 
 // LDS position of 16-byte granule q (channels 4q..4q+3) of a key scale or
 // zero-point row.  The four lane groups g read granules 8g + i at the same
@@ -232,15 +233,23 @@ __device__ __forceinline__ void unpack_k_codes(const u32* w, half8* A) {
   }
 }
 
-// Exact fp16 values of 32 E4M3 codes (natural order).
-__device__ __forceinline__ void unpack_k_fp8(const u32* w, half8* A) {
+// Exact fp16 values of the two 8-bit codes in bytes (0, 1) (hi: (2, 3)) of x.
+// E4M3 through the conversion instruction; an E5M2 byte is the high byte of
+// the fp16 with the same value, so one byte permute places two of them.
+template <int F>
+__device__ __forceinline__ u32 f8_pair(u32 x, bool hi) {
+  if constexpr (F == BF8) return __builtin_amdgcn_perm(x, x, hi ? 0x030C020Cu : 0x010C000Cu);
+  else return h2u(hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+}
+
+// Exact fp16 values of 32 E4M3 / E5M2 codes (natural order).
+template <int F>
+__device__ __forceinline__ void unpack_k_f8(const u32* w, half8* A) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    A[j] = pack8(h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j], 1.0f, false)),
-                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j], 1.0f, true)),
-                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j + 1], 1.0f, false)),
-                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * j + 1], 1.0f, true)));
-  }
+  for (int j = 0; j < 4; ++j)
+    A[j] = pack8(f8_pair<F>(w[2 * j], false), f8_pair<F>(w[2 * j], true),
+                 f8_pair<F>(w[2 * j + 1], false), f8_pair<F>(w[2 * j + 1], true));
 }
 
 // Exact fp16 codes of a lane's 32 key channels come as 16 half2 registers;
@@ -289,14 +298,11 @@ __device__ __forceinline__ half8 unpack_v(const u32* w, int i) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) r[k] = unmagic((((d0 >> (8 * k)) & 0xFFu) | (((d1 >> (8 * k)) & 0xFFu) << 16)) | kMagic);
     return pack8(r[0], r[1], r[2], r[3]);
-  } else {  // FP8
+  } else {  // FP8 (E4M3 or E5M2)
     const u32 d0 = w[2 * i], d1 = w[2 * i + 1];
     const u32 y0 = (d0 & 0xFFu) | ((d1 & 0xFFu) << 8) | ((d0 & 0xFF00u) << 8) | ((d1 & 0xFF00u) << 16);
     const u32 y1 = ((d0 >> 16) & 0xFFu) | ((d1 >> 8) & 0xFF00u) | ((d0 >> 8) & 0xFF0000u) | (d1 & 0xFF000000u);
-    return pack8(h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 1.0f, false)),
-                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 1.0f, true)),
-                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 1.0f, false)),
-                 h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 1.0f, true)));
+    return pack8(f8_pair<VF>(y0, false), f8_pair<VF>(y0, true), f8_pair<VF>(y1, false), f8_pair<VF>(y1, true));
   }
 }
 
@@ -378,7 +384,7 @@ attn_mfma(Plan p, Args a) {
   constexpr int KB = Bits<KF>::v, VB = Bits<VF>::v;
   constexpr int KDW = KB;                 // dwords of key data per lane (32 channels)
   constexpr int VDW = 2 * VB;             // dwords of value data per lane per 32-token block
-  constexpr bool KINT = KF != FP8, VINT = VF != FP8;
+  constexpr bool KINT = !is_f8(KF), VINT = !is_f8(VF);
   constexpr int VGC = D / VG;             // value channels per group
 
   // Per-wavefront LDS ring of NB stages; a stage holds one 32-token step:
@@ -490,8 +496,8 @@ attn_mfma(Plan p, Args a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const float k_fp8 = KF == FP8 ? ((const float*)(arena + p.k.scale))[kvh] : 1.0f;
-  const float v_fp8 = VF == FP8 ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
+  const float k_fp8 = is_f8(KF) ? ((const float*)(arena + p.k.scale))[kvh] : 1.0f;
+  const float v_fp8 = is_f8(VF) ? ((const float*)(arena + p.v.scale))[kvh] : 1.0f;
   uint8_t* const ring = ring_s[wave];
   const u32 ring_lds = (u32)(size_t)(__attribute__((address_space(3))) uint8_t*)&ring_s[0][0] + wave * (NB * SLOT);
 
@@ -722,8 +728,8 @@ attn_mfma(Plan p, Args a) {
         if constexpr (RING) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) A[j] = pack8(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
-        } else if constexpr (KF == FP8) {
-          unpack_k_fp8(w, A);
+        } else if constexpr (is_f8(KF)) {
+          unpack_k_f8<KF>(w, A);
         } else {
           unpack_k_codes<KF>(w, A);
         }
@@ -820,7 +826,7 @@ attn_mfma(Plan p, Args a) {
       }
     } else {
       // FP8 values: A = p * v_scale; window values: A = p
-      const float vsc = (!RING && VF == FP8) ? v_fp8 : 1.0f;
+      const float vsc = (!RING && is_f8(VF)) ? v_fp8 : 1.0f;
       u32 r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = pk_f16(pk[i] * vsc, pk[i + 4] * vsc);
@@ -969,30 +975,34 @@ attn_mfma(Plan p, Args a) {
 
 static int kfmt(const Plan& p) {
   if (p.k.scheme == KVQ_FP8_E4M3) return FP8;
+  if (p.k.scheme == KVQ_FP8_E5M2) return BF8;
   if (p.k.scheme == KVQ_INT_ASYM && p.k.axis == KVQ_PER_CHANNEL && p.k.group > 0 && p.k.group % 32 == 0)
     return p.k.bits;
   return -1;
 }
 static int vfmt(const Plan& p) {
   if (p.v.scheme == KVQ_FP8_E4M3) return FP8;
+  if (p.v.scheme == KVQ_FP8_E5M2) return BF8;
   if (p.v.scheme == KVQ_INT_ASYM && p.v.axis == KVQ_PER_TOKEN && p.v.group >= 16) return p.v.bits;
   return -1;
 }
 
-static int vgroups(const Plan& p) { return p.v.scheme == KVQ_FP8_E4M3 ? 1 : 128 / p.v.group; }
+static int vgroups(const Plan& p) { return is_fp8(p.v.scheme) ? 1 : 128 / p.v.group; }
 
 bool mfma_supported(const Plan& p) {
   if (p.D != 128 || p.n_rep > 8) return false;
   const int kf = kfmt(p), vf = vfmt(p);
   if (kf < 0 || vf < 0) return false;
-  if (p.pre_rope && kf == FP8) return false;
+  if (p.pre_rope && is_f8(kf)) return false;
+  // E5M2 pairs only with FP8 values / keys (other mixes run the generic kernel)
+  if ((kf == BF8 || vf == BF8) && !(is_f8(kf) && is_f8(vf))) return false;
   return p.n_rep * vgroups(p) <= 16;   // PV rows are (value group, head) pairs
 }
 
 template <int KF, int VF, int VG>
 static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
   if (p.pre_rope) {
-    if constexpr (KF != FP8) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true>), grid, dim3(256), 0, s, p, a);
+    if constexpr (!is_f8(KF)) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true>), grid, dim3(256), 0, s, p, a);
   } else {
     hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false>), grid, dim3(256), 0, s, p, a);
   }
@@ -1000,7 +1010,7 @@ static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
 
 template <int KF, int VF>
 static void launch_kv(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
-  if constexpr (VF == FP8) {
+  if constexpr (is_f8(VF)) {
     launch_kvg<KF, VF, 1>(p, grid, s, a);
   } else {
     switch (vgroups(p)) {
@@ -1014,11 +1024,19 @@ static void launch_kv(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
 
 template <int KF>
 static void launch_k(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
-  switch (vfmt(p)) {
-    case INT2: launch_kv<KF, INT2>(p, grid, s, a); break;
-    case INT4: launch_kv<KF, INT4>(p, grid, s, a); break;
-    case INT8: launch_kv<KF, INT8>(p, grid, s, a); break;
-    default: launch_kv<KF, FP8>(p, grid, s, a); break;
+  if constexpr (KF == BF8) {            // E5M2 keys: FP8-class values only
+    if (vfmt(p) == BF8) launch_kv<KF, BF8>(p, grid, s, a);
+    else launch_kv<KF, FP8>(p, grid, s, a);
+  } else {
+    switch (vfmt(p)) {
+      case INT2: launch_kv<KF, INT2>(p, grid, s, a); break;
+      case INT4: launch_kv<KF, INT4>(p, grid, s, a); break;
+      case INT8: launch_kv<KF, INT8>(p, grid, s, a); break;
+      case BF8:
+        if constexpr (KF == FP8) launch_kv<KF, BF8>(p, grid, s, a);
+        break;
+      default: launch_kv<KF, FP8>(p, grid, s, a); break;
+    }
   }
 }
 
@@ -1031,6 +1049,7 @@ hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* 
     case INT2: launch_k<INT2>(p, grid, s, a); break;
     case INT4: launch_k<INT4>(p, grid, s, a); break;
     case INT8: launch_k<INT8>(p, grid, s, a); break;
+    case BF8: launch_k<BF8>(p, grid, s, a); break;
     default: launch_k<FP8>(p, grid, s, a); break;
   }
   return hipGetLastError();

@@ -40,7 +40,7 @@ __device__ __forceinline__ float src_val(const Plan& p, const Src& s, int b, int
 __device__ __forceinline__ int64_t meta_index(const Plan& p, const SideFmt& f, int b, int h,
                                               int64_t t, int c) {
   const int64_t bh = (int64_t)b * p.Hkv + h;
-  if (f.scheme == KVQ_FP8_E4M3) return h;
+  if (is_fp8(f.scheme)) return h;
   if (f.axis == KVQ_PER_TENSOR) return bh;
   if (f.axis == KVQ_PER_CHANNEL) {
     const int64_t g = f.group ? t / f.group : 0;
@@ -68,6 +68,23 @@ __device__ __forceinline__ uint32_t sym_code(float x, float s) {
   float r = __builtin_rintf(x / s);
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+// E5M2 encode with saturation: nearest representable, ties to even (the
+// code's parity is its last mantissa bit's).
+__device__ __forceinline__ uint32_t e5m2_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), kE5M2Max);
+  uint32_t code;
+  if (a < 6.103515625e-05f) {                // below 2^-14: quantum 2^-16
+    code = (uint32_t)__builtin_rintf(a * 65536.0f);   // 0..4 (4 is the smallest normal)
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
+    uint32_t m = (uint32_t)__builtin_rintf(ldexpf(a, 2 - e));   // 4..8
+    if (m == 8) { m = 4; e += 1; }
+    code = ((uint32_t)(e + 15) << 2) | (m - 4);
+  }
+  return code | sign;
 }
 
 // E4M3FN encode with saturation: nearest representable, ties to even.
@@ -120,6 +137,7 @@ __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* aren
   const int64_t mi = meta_index(p, f, b, h, t, c);
   const float s = ((const float*)(arena + f.scale))[mi];
   if (f.scheme == KVQ_FP8_E4M3) return e4m3_decode(code) * s;
+  if (f.scheme == KVQ_FP8_E5M2) return e5m2_decode(code) * s;
   if (f.scheme == KVQ_INT_SYM) return (float)(int8_t)(uint8_t)code * s;
   const float z = ((const float*)(arena + f.zero))[mi];
   const float prod = (float)code * s;

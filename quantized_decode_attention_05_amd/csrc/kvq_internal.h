@@ -11,6 +11,12 @@ namespace kvq {
 constexpr int kVBlock = 32;      // tokens per V code block
 constexpr int kRingAlign = 32;   // ring slots are a multiple of this
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+
+// FP8 schemes: bytes with one fp32 scale per kv head (1.0 for E5M2)
+__host__ __device__ inline bool is_fp8(int scheme) {
+  return scheme == KVQ_FP8_E4M3 || scheme == KVQ_FP8_E5M2;
+}
 
 // One side (K or V) of the cache.
 struct SideFmt {
@@ -65,6 +71,14 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i, int dtype) {
 
 // fp32 -> fp16 (round to nearest even) -> fp32
 __device__ __forceinline__ float stage_f16(float x) { return (float)(_Float16)x; }
+
+// Value of an E5M2 code byte (finite codes; infinities and NaNs never produced).
+__device__ __forceinline__ float e5m2_decode(uint32_t c) {
+  uint32_t e = (c >> 2) & 0x1F, m = c & 3;
+  float mag = (e == 0) ? (float)m * 1.52587890625e-05f                  // m * 2^-16
+                       : __uint_as_float(((e + 112u) << 23) | (m << 21)); // (1+m/4) 2^(e-15)
+  return (c & 0x80) ? -mag : mag;
+}
 
 // Value of an E4M3FN code byte (finite codes; NaN codes never produced).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {

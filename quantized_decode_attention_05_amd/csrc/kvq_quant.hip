@@ -31,6 +31,7 @@ __device__ __forceinline__ uint32_t encode_elem(const Plan& p, const SideFmt& f,
   const int64_t mi = meta_index(p, f, b, h, t, c);
   const float s = ((const float*)(arena + f.scale))[mi];
   if (f.scheme == KVQ_FP8_E4M3) return e4m3_encode(x / s);
+  if (f.scheme == KVQ_FP8_E5M2) return e5m2_encode(x / s);   // s = 1
   if (f.scheme == KVQ_INT_SYM) return sym_code(x, s);
   const float z = ((const float*)(arena + f.zero))[mi];
   return asym_code(x, s, z, f.bits);
@@ -276,10 +277,12 @@ __global__ void fp8_finalize(Plan p, uint8_t* arena, const uint32_t* amax, const
   if (h >= p.Hkv) return;
   for (int side = 0; side < 2; ++side) {
     const SideFmt& f = side ? p.v : p.k;
-    if (f.scheme != KVQ_FP8_E4M3) continue;
+    if (!is_fp8(f.scheme)) continue;
     const float* given = side ? vs : ks;
-    float s = 1.0f;
-    if (mode == 1) {
+    float s = 1.0f;                       // E5M2 takes no scale
+    if (f.scheme != KVQ_FP8_E4M3) {
+      s = 1.0f;
+    } else if (mode == 1) {
       const float a = __uint_as_float(amax[side * p.Hkv + h]);
       s = (a == 0.0f) ? 1.0f : a / kE4M3Max;
     } else if (given) {

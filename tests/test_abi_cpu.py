@@ -89,6 +89,12 @@ def test_append_validation_paths():
     assert _append(fp8, t0=8, flags=K.CALIBRATE) == -1           # calibrate only at t0 == 0
     assert _append(fp8, t0=8, ks=0x400000) == -1                 # scales only at t0 == 0
     assert _append(fp8, ks=0x400000, flags=K.CALIBRATE) == -1
+    e5 = _cfg(k=(K.FP8_E5M2, 8, 0, 0), v=(K.FP8_E5M2, 8, 0, 0), residual=0)
+    assert _append(e5, ks=0x400000) == -1                        # E5M2 takes no scale
+    assert _append(e5, vs=0x400000) == -1
+    mix = _cfg(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E5M2, 8, 0, 0), residual=0)
+    assert _append(mix, vs=0x400000) == -1
+    assert _append(_cfg(k=(K.FP8_E5M2, 4, 0, 0)), t0=0) == -1    # FP8 is 8 bits
     whole = _cfg(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 0), v=(K.INT_ASYM, 4, K.PER_TOKEN, 0), residual=0)
     assert _append(whole, t0=16) == -2                           # would rescale history
     tens = _cfg(k=(K.INT_SYM, 8, K.PER_TENSOR, 0), v=(K.NONE, 16, 0, 0), residual=0)

@@ -14,7 +14,7 @@ from tests.kvq_harness import (ATTN_TOL, Case, GpuCache, attention_error, compar
 
 pytestmark = pytest.mark.gpu
 
-A, S, F8, NO = K.INT_ASYM, K.INT_SYM, K.FP8_E4M3, K.NONE
+A, S, F8, E5, NO = K.INT_ASYM, K.INT_SYM, K.FP8_E4M3, K.FP8_E5M2, K.NONE
 CH, TOK, TEN = K.PER_CHANNEL, K.PER_TOKEN, K.PER_TENSOR
 
 # (name, case, T, append schedule, kernels)
@@ -27,6 +27,9 @@ FORMATS = [
     ("int4tok32_int2tok_R64", dict(k=(A, 4, TOK, 32), v=(A, 2, TOK, 64), R=64)),
     ("fp8_fp8", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0)),
     ("fp8_fp8_R32", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=32)),
+    ("e5m2_e5m2", dict(k=(E5, 8, 0, 0), v=(E5, 8, 0, 0), R=0)),
+    ("e4m3_e5m2_R32", dict(k=(F8, 8, 0, 0), v=(E5, 8, 0, 0), R=32)),
+    ("int4ch128_e5m2_R128", dict(k=(A, 4, CH, 128), v=(E5, 8, 0, 0), R=128)),
     ("sym8tok_sym8tok", dict(k=(S, 8, TOK, 0), v=(S, 8, TOK, 32), R=0)),
     ("none16_int4tok", dict(k=(NO, 16, 0, 0), v=(A, 4, TOK, 0), R=0)),
     ("int2ch32_none32", dict(k=(A, 2, CH, 32), v=(NO, 32, 0, 0), R=32)),
@@ -165,6 +168,29 @@ def test_e4m3_decode_all_codes():
     kd, _ = gc.dequantize(2)
     from oracle import quant as OQ
     assert np.array_equal(kd[0, 0, :, :127], OQ.e4m3_decode(rows))
+
+
+def test_e5m2_decode_all_codes_and_saturation():
+    """Every finite E5M2 byte dequantizes to its closed-form value, and values
+    beyond +-57344 saturate (no scale is stored but 1.0)."""
+    import torch
+    from oracle import quant as OQ
+    case = Case(B=1, Hq=1, Hkv=1, D=128, dtype="f32", k=(E5, 8, 0, 0), v=(E5, 8, 0, 0))
+    gc = GpuCache(case, cap=64)
+    (Kf, _), (Vf, _) = W.random_case(6, 1, 1, 8, 128, dtype="f32")
+    Kf = Kf.copy()
+    Kf[0, 0, 2:4] *= 1e5                             # beyond the range
+    gc.append(Kf[:, :, :4], Vf[:, :, :4], 0)
+    st = OC.quantize_cache(case.oracle_cfg(), Kf, Vf, 4)
+    compare_sections(gc, st)
+    compare_dequant(gc, st)
+    assert np.any((st["k"]["codes"][0, 0, 2:4] & 0x7F) == 0x7B)
+    codes = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], dtype=np.uint8)   # 248 finite
+    rows = np.zeros((2, 128), np.uint8)
+    rows.reshape(-1)[:codes.size] = codes
+    gc.arena[gc.layout.k_codes: gc.layout.k_codes + 256] = torch.from_numpy(rows.reshape(-1)).cuda()
+    kd, _ = gc.dequantize(2)
+    assert np.array_equal(kd[0, 0], OQ.e5m2_decode(rows))
 
 
 def test_attention_deterministic_and_split_invariant():

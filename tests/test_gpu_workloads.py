@@ -23,7 +23,7 @@ from tests.kvq_harness import (ATTN_TOL, Case, GpuCache, compare_dequant, compar
 
 pytestmark = pytest.mark.gpu
 
-A, S, F8, NO = K.INT_ASYM, K.INT_SYM, K.FP8_E4M3, K.NONE
+A, S, F8, E5, NO = K.INT_ASYM, K.INT_SYM, K.FP8_E4M3, K.FP8_E5M2, K.NONE
 CH, TOK, TEN = K.PER_CHANNEL, K.PER_TOKEN, K.PER_TENSOR
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -105,6 +105,7 @@ def test_c2_int4_single_head(kaxis):
 
 LARGE = {
     "c3_fp8_e4m3_gqa_8k": dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0),
+    "c3_fp8_e5m2_gqa_8k": dict(k=(E5, 8, 0, 0), v=(E5, 8, 0, 0), R=0),
     "c4_int4_llama70b_128k": dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128),
     "c5_int2_kivi_prerope_32k": dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True),
 }

@@ -67,6 +67,11 @@ WORKLOADS = {
         B=16, Hq=32, Hkv=8, D=128, T=8192, n_new=1, dtype="bf16", seed=3,
         n_outliers=4, outlier_scale=30.0,
     ),
+    # the same inputs cached as FP8 E5M2 (no scales; the FP8 page's scale-free variant)
+    "c3_fp8_e5m2_gqa_8k": dict(
+        B=16, Hq=32, Hkv=8, D=128, T=8192, n_new=1, dtype="bf16", seed=3,
+        n_outliers=4, outlier_scale=30.0,
+    ),
     # Llama-3.1-70B shaped layer: INT4 K per-channel G128 + INT4 V per-token, R=128
     "c4_int4_llama70b_128k": dict(
         B=1, Hq=64, Hkv=8, D=128, T=131072, n_new=0, dtype="bf16", seed=4,
