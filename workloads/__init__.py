@@ -194,6 +194,31 @@ def random_case(seed: int, B: int, Hkv: int, T: int, D: int, n_outliers: int = 3
     return _as_dtype(K, dtype), _as_dtype(V, dtype)
 
 
+def sink_case(seed: int, B: int, Hq: int, Hkv: int, T: int, D: int, sink_channel: int = 5,
+              sink_value: float = 1300.0, q_sink: float = 0.1, outlier_scale: float = 5.0,
+              dtype: str = "bf16"):
+    """K, V [B, Hkv, T, D] and q [B, Hq, D] with a planted attention-sink key.
+
+    Keys and values are N(0, 1) with three outlier channels (x outlier_scale)
+    per kv head, as in ``random_case``; token 0 of every (sequence, kv head)
+    is an attention sink whose key has ``sink_value`` in ``sink_channel``,
+    beyond E4M3's +-448 at unit scale (the FP8 page's section "Why do
+    per-tensor scales waste bits on the K cache?": sinks carry keys with
+    outsized norms).  Every query has +``q_sink`` in that channel, so the sink
+    takes most of the attention mass; the outlier channels avoid it.
+    Returns ((K, K payload), (V, V payload), (q, q payload))."""
+    rng = np.random.default_rng((seed, 79))
+    K = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    V = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    for h in range(Hkv):
+        ch = rng.choice([c for c in range(D) if c != sink_channel], size=3, replace=False)
+        K[:, h][..., ch] *= np.float32(outlier_scale)
+    K[:, :, 0, sink_channel] = np.float32(sink_value)
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32)
+    q[:, :, sink_channel] = np.float32(q_sink)
+    return _as_dtype(K, dtype), _as_dtype(V, dtype), _as_dtype(q, dtype)
+
+
 def random_queries(seed: int, B: int, Hq: int, D: int, dtype: str = "f32"):
     rng = np.random.default_rng((seed, 78))
     return _as_dtype(rng.standard_normal((B, Hq, D), dtype=np.float32), dtype)
