@@ -219,6 +219,30 @@ def sink_case(seed: int, B: int, Hq: int, Hkv: int, T: int, D: int, sink_channel
     return _as_dtype(K, dtype), _as_dtype(V, dtype), _as_dtype(q, dtype)
 
 
+def rope_study_case(seed: int, B: int, Hq: int, Hkv: int, T: int, D: int,
+                    outliers=(3, 17, 44, 91), magnitude: float = 20.0, consistent: bool = True):
+    """fp32 K, V [B, Hkv, T, D] and q [B, Hq, D] (N(0, 1)) with outlier key
+    channels for the pre- vs post-RoPE study ("KV Cache Quantization: Why Keys
+    and Values Need Different Axes", section "Where does RoPE break this?").
+
+    consistent=True: each outlier channel is +-magnitude + N(0, 1) with a sign
+    fixed per (kv head, channel): "the same channel is always huge".
+    consistent=False: the outlier channels are N(0, 1) * magnitude, the
+    random-sign scaling of the page's own listing."""
+    rng = np.random.default_rng((seed, 80, int(consistent)))
+    K = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    V = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    for h in range(Hkv):
+        for c in outliers:
+            if consistent:
+                sgn = np.float32(1.0 if rng.random() < 0.5 else -1.0)
+                K[:, h, :, c] = sgn * np.float32(magnitude) + K[:, h, :, c]
+            else:
+                K[:, h, :, c] *= np.float32(magnitude)
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32)
+    return K, V, q
+
+
 def random_queries(seed: int, B: int, Hq: int, D: int, dtype: str = "f32"):
     rng = np.random.default_rng((seed, 78))
     return _as_dtype(rng.standard_normal((B, Hq, D), dtype=np.float32), dtype)
