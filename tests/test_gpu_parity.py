@@ -234,3 +234,28 @@ def test_one_workspace_many_calls():
                 first = o
             else:
                 assert np.array_equal(o, first), "same split count, different result"
+
+
+@pytest.mark.parametrize("kern", [K.KERNEL_GENERIC, K.KERNEL_MFMA])
+def test_output_dtypes_round_the_fp32_result(kern):
+    """fp16 and bf16 outputs are the fp32 result rounded to nearest even (the
+    merge converts once, at the end)."""
+    import math
+    import torch
+    from tests.kvq_harness import to_dev
+    case = Case(B=2, Hq=8, Hkv=2, D=128, dtype="bf16", k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32,
+                pre_rope=True)
+    gc, st, _ = run_case(case, 700, [700], seed=29, kernels=[K.KERNEL_GENERIC])
+    (qf, qp) = W.random_queries(29, case.B, case.Hq, case.D, dtype="bf16")
+    q = to_dev(qp, case.dtype)
+    sm = 1.0 / math.sqrt(case.D)
+    ws = torch.zeros(K.kvq_workspace_bytes(gc.cfg, 700, kern), dtype=torch.uint8, device="cuda")
+    ref = torch.full((case.B, case.Hq, case.D), float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq_decode_attention(gc.cfg, gc.arena, 700, q, ref, sm, ws, kern)
+    for code, tdt in ((K.F16, torch.float16), (K.BF16, torch.bfloat16)):
+        cfg = type(gc.cfg).from_buffer_copy(gc.cfg)
+        cfg.out_dtype = code
+        out = torch.full((case.B, case.Hq, case.D), float("nan"), dtype=tdt, device="cuda")
+        K.kvq_decode_attention(cfg, gc.arena, 700, q, out, sm, ws, kern)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref.to(tdt)), (kern, tdt)
