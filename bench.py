@@ -34,6 +34,14 @@ FORMATS = {
     "c4_int4_llama70b_128k": ((1, 4, 1, 128), (1, 4, 2, 0), 128, False, False),
     "c5_int2_kivi_prerope_32k": ((1, 2, 1, 32), (1, 2, 2, 32), 32, True, False),
 }
+# what bounds each workload's attention launch, from the measurements recorded
+# with the profiles (SQ busy counters, context / batch sweeps, ablations)
+LIMITER = {
+    "c3_fp8_e4m3_gqa_8k": "hbm streaming (~6.7 TB/s marginal) plus ~8.6 us fixed per-launch cost",
+    "c3_fp8_e5m2_gqa_8k": "hbm streaming plus fixed per-launch cost, as the E4M3 cache",
+    "c4_int4_llama70b_128k": "~15 us fixed per-launch cost (two kernels, start-up) over ~6.3 TB/s marginal streaming",
+    "c5_int2_kivi_prerope_32k": "vector-ALU issue (~90% busy): pre-RoPE dequantize, rotation and fp16 split per key pair",
+}
 DESCR = {
     "c3_fp8_e4m3_gqa_8k": "FP8 E4M3 K/V, per-kv-head calibrated scales",
     "c3_fp8_e5m2_gqa_8k": "FP8 E5M2 K/V, no scales",
@@ -373,6 +381,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
             "kernel": "decode attention launch: pass 1 (split-K) + merge, HIP-event timed",
+            "limiter": LIMITER[name],
         },
     }
     if warm_us is not None:
