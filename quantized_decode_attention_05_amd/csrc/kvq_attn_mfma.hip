@@ -372,9 +372,10 @@ using namespace mf;
 
 // One decode-attention pass-1 work-group.  KF/VF: key/value code format;
 // ROPE: keys cached before RoPE; VG: value channel groups (INT values);
+// PV2: 32 PV rows (8 heads x 4 value groups) in two A operands of 16 rows;
 // KSPLIT: rotated keys enter the matrix unit as hi + lo fp16 halves.
 // D = 128, n_rep <= 8.
-template <int KF, int VF, bool ROPE, int VG, bool KSPLIT>
+template <int KF, int VF, bool ROPE, int VG, bool KSPLIT, bool PV2>
 __global__ void __launch_bounds__(256)
 #if KVQ_MFMA_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)))
@@ -446,6 +447,8 @@ attn_mfma(Plan p, Args a) {
   // n / n_rep (rows past the last group are computed and never read).
   const int head = n % n_rep;
   const int vgrp = (n / n_rep) < VG ? n / n_rep : VG - 1;
+  // PV2 (n_rep = 8, VG = 4): the second A operand's row n is value group vgrp + 2
+  static_assert(!PV2 || VG == 4, "two PV row halves need four value groups");
 
   half8 Bq[4], Bl[4];   // query operand (hi, lo) of the current key group / window
   float kbias = 0.0f;   // per-column logit bias from the key zero-points
@@ -492,6 +495,7 @@ attn_mfma(Plan p, Args a) {
   // softmax / output state (lane (n, g): head n for n < n_rep)
   float m_run = kNegBig, l_run = 0.0f;
   float vbias = 0.0f;   // sum_t p_t z_t of this lane's PV row
+  float vbias1 = 0.0f;  // the same for the lane's row of the second half (PV2)
   floatx4 O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -773,6 +777,7 @@ attn_mfma(Plan p, Args a) {
       m_run = m_new;
       l_run *= alpha;
       vbias *= alpha;
+      if constexpr (PV2) vbias1 *= alpha;
       float al[4];    // lane (c, g') holds rows (heads) 4g'+i
 #pragma unroll
       for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 15, 64);
@@ -794,35 +799,56 @@ attn_mfma(Plan p, Args a) {
     if constexpr (!RING && VINT) {
       // A = p * s as hi + lo fp16 halves (lo = exact residual by FMA); z enters
       // through the row's bias
-      u32 rh[4], rl[4];
-      float zsum = 0.0f;
+      auto build_a = [&](const float* vs, const float* vz, half8& Ah, half8& Al) __attribute__((always_inline)) {
+        u32 rh[4], rl[4];
+        float zsum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sv[2], pv[2];
+        for (int i = 0; i < 4; ++i) {
+          float sv[2], pv[2];
 #pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const int k = vtok<VF>(2 * i + hlf);
-          sv[hlf] = d.vs[k];
-          pv[hlf] = pk[k];
-          float zt = d.vz[k];
-          if constexpr (!FULL) {
-            const bool ok = (valid >> k) & 1u;
-            sv[hlf] = ok ? sv[hlf] : 0.0f;
-            zt = ok ? zt : 0.0f;
+          for (int hlf = 0; hlf < 2; ++hlf) {
+            const int k = vtok<VF>(2 * i + hlf);
+            sv[hlf] = vs[k];
+            pv[hlf] = pk[k];
+            float zt = vz[k];
+            if constexpr (!FULL) {
+              const bool ok = (valid >> k) & 1u;
+              sv[hlf] = ok ? sv[hlf] : 0.0f;
+              zt = ok ? zt : 0.0f;
+            }
+            zsum = __builtin_fmaf(pv[hlf], zt, zsum);
           }
-          zsum = __builtin_fmaf(pv[hlf], zt, zsum);
+          rh[i] = pk_f16(pv[0] * sv[0], pv[1] * sv[1]);
+          rl[i] = pk_f16(__builtin_fmaf(pv[0], sv[0], -lo_f(rh[i])), __builtin_fmaf(pv[1], sv[1], -hi_f(rh[i])));
         }
-        rh[i] = pk_f16(pv[0] * sv[0], pv[1] * sv[1]);
-        rl[i] = pk_f16(__builtin_fmaf(pv[0], sv[0], -lo_f(rh[i])), __builtin_fmaf(pv[1], sv[1], -hi_f(rh[i])));
-      }
-      const half8 Ah = pack8(rh[0], rh[1], rh[2], rh[3]);
-      const half8 Al = pack8(rl[0], rl[1], rl[2], rl[3]);
-      vbias += zsum;
+        Ah = pack8(rh[0], rh[1], rh[2], rh[3]);
+        Al = pack8(rl[0], rl[1], rl[2], rl[3]);
+        return zsum;
+      };
+      half8 Ah, Al;
+      vbias += build_a(d.vs, d.vz, Ah, Al);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < (PV2 ? 4 : 8); ++i) {
         const half8 bv = unpack_v<VF>(d.v, i);
         O[i] = mfma(Ah, bv, O[i]);
         O[i] = mfma(Al, bv, O[i]);
+      }
+      if constexpr (PV2) {
+        // second half: value groups 2, 3 (tiles 4-7), metadata read from the slot
+        float vs1[8], vz1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float* vm = (const float*)(ring + cur_slot * SLOT + OFF_VM) + 4 * vm_pos(8 * g + k) + vgrp + 2;
+          vs1[k] = vm[0];
+          vz1[k] = vm[128];
+        }
+        vbias1 += build_a(vs1, vz1, Ah, Al);
+#pragma unroll
+        for (int i = 4; i < 8; ++i) {
+          const half8 bv = unpack_v<VF>(d.v, i);
+          O[i] = mfma(Ah, bv, O[i]);
+          O[i] = mfma(Al, bv, O[i]);
+        }
       }
     } else {
       // FP8 values: A = p * v_scale; window values: A = p
@@ -928,6 +954,7 @@ attn_mfma(Plan p, Args a) {
   // ---- combine the wavefronts of the work-group ------------------------------------
   l_run = wave_sum16(l_run);
   vbias = wave_sum16(vbias);
+  if constexpr (PV2) vbias1 = wave_sum16(vbias1);
   if (g == 0 && n < n_rep) {
     red_ml[wave][n][0] = m_run;
     red_ml[wave][n][1] = l_run;
@@ -936,17 +963,23 @@ attn_mfma(Plan p, Args a) {
   // O rows -> LDS with the row's value bias added.  Accumulator row r of this
   // lane is A row R = 4g + r (value group R / n_rep, head R mod n_rep); tile i
   // keeps the rows of its own group.  Row R's bias lives in lane R.
-  float rbias[4];
+  float rbias[4], rbias1[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) rbias[r] = __shfl(vbias, (4 * g + r) & 15, 64);
+  for (int r = 0; r < 4; ++r) {
+    rbias[r] = __shfl(vbias, (4 * g + r) & 15, 64);
+    rbias1[r] = PV2 ? __shfl(vbias1, (4 * g + r) & 15, 64) : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = 16 * i + n;
-    const int gi = VINT ? (16 * i) / VGC : 0;
+    // tile i's value group, relative to its half's first group (PV2: tiles
+    // 4-7 are the second half, groups 2 and 3)
+    const bool h1 = PV2 && i >= 4;
+    const int gi = (VINT ? (16 * i) / VGC : 0) - (h1 ? 2 : 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int R = 4 * g + r;
-      if (R / n_rep == gi) red_o_w[R - gi * n_rep][c] = O[i][r] + (VINT ? rbias[r] : 0.0f);
+      if (R / n_rep == gi) red_o_w[R - gi * n_rep][c] = O[i][r] + (VINT ? (h1 ? rbias1[r] : rbias[r]) : 0.0f);
     }
   }
   __syncthreads();
@@ -996,15 +1029,26 @@ bool mfma_supported(const Plan& p) {
   if (p.pre_rope && is_f8(kf)) return false;
   // E5M2 pairs only with FP8 values / keys (other mixes run the generic kernel)
   if ((kf == BF8 || vf == BF8) && !(is_f8(kf) && is_f8(vf))) return false;
-  return p.n_rep * vgroups(p) <= 16;   // PV rows are (value group, head) pairs
+  // PV rows are (value group, head) pairs: 16 in one A operand, or 32 in two
+  // (8 heads x 4 value groups, INT2 / INT4 codes)
+  if (p.n_rep * vgroups(p) <= 16) return true;
+  return p.n_rep == 8 && vgroups(p) == 4 && (kf == INT2 || kf == INT4) && (vf == INT2 || vf == INT4);
 }
 
 template <int KF, int VF, int VG>
 static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
+  constexpr bool kPV2 = VG == 4 && (KF == INT2 || KF == INT4) && (VF == INT2 || VF == INT4);
+  if constexpr (kPV2) {
+    if (p.n_rep * VG > 16) {
+      if (p.pre_rope) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, true>), grid, dim3(256), 0, s, p, a);
+      else hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, true>), grid, dim3(256), 0, s, p, a);
+      return;
+    }
+  }
   if (p.pre_rope) {
-    if constexpr (!is_f8(KF)) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true>), grid, dim3(256), 0, s, p, a);
+    if constexpr (!is_f8(KF)) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, false>), grid, dim3(256), 0, s, p, a);
   } else {
-    hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false>), grid, dim3(256), 0, s, p, a);
+    hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, false>), grid, dim3(256), 0, s, p, a);
   }
 }
 

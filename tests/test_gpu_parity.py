@@ -259,3 +259,21 @@ def test_output_dtypes_round_the_fp32_result(kern):
         K.kvq_decode_attention(cfg, gc.arena, 700, q, out, sm, ws, kern)
         torch.cuda.synchronize()
         assert torch.equal(out, ref.to(tdt)), (kern, tdt)
+
+
+@pytest.mark.parametrize("name,fmt", [
+    ("int2ch32_int2tok32_R32_prerope", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True)),
+    ("int4ch128_int4tok32_R128", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 32), R=128)),
+    ("int2ch32_int4tok32_R0", dict(k=(A, 2, CH, 32), v=(A, 4, TOK, 32), R=0)),
+])
+def test_eight_heads_per_kv_head_four_value_groups(name, fmt):
+    """8 query heads per kv head with 32-channel value groups: 32 (value
+    group, head) PV rows, which the MFMA kernel covers with two A operands."""
+    case = Case(B=2, Hq=16, Hkv=2, D=128, dtype="bf16", **fmt)
+    gc, st, errs = run_case(case, 1100, _schedule("stream", 1100), seed=37)
+    assert K.KERNEL_MFMA in errs, "the MFMA kernel should cover this shape"
+    for s in (1, 3):
+        out = gc.attention(W.random_queries(37, case.B, case.Hq, case.D, dtype="bf16")[1],
+                           kernel=K.KERNEL_MFMA, num_splits=s)
+        assert attention_error(out, W.random_queries(37, case.B, case.Hq, case.D, dtype="bf16")[0],
+                               st, case) <= ATTN_TOL
