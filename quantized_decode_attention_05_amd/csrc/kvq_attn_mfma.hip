@@ -374,7 +374,7 @@ using namespace mf;
 // ROPE: keys cached before RoPE; VG: value channel groups (INT values);
 // PV2: 32 PV rows (8 heads x 4 value groups) in two A operands of 16 rows;
 // KSPLIT: rotated keys enter the matrix unit as hi + lo fp16 halves.
-// D = 128, n_rep <= 8.
+// D = 128, n_rep <= 8 (<= 16 with one value group).
 template <int KF, int VF, bool ROPE, int VG, bool KSPLIT, bool PV2>
 __global__ void __launch_bounds__(256)
 #if KVQ_MFMA_WAVES_PER_EU > 0
@@ -398,15 +398,19 @@ attn_mfma(Plan p, Args a) {
   constexpr int SLOT = OFF_KT + SZ_KT;
   constexpr int NB = KVQ_MFMA_STAGES > 0 ? KVQ_MFMA_STAGES : (SLOT <= 6144 ? 3 : 2);
   constexpr int N_DMA = SZ_K / 1024 + SZ_V / 1024 + (SZ_VM + 1023) / 1024 + (KINT ? 1 : 0) + (ROPE ? 1 : 0);
-  static_assert(SZ_K % 1024 == 0 && SZ_V % 1024 == 0 && NB * SLOT >= 8 * D * 4, "stage layout");
+  static_assert(SZ_K % 1024 == 0 && SZ_V % 1024 == 0 && NB * SLOT >= (VG == 1 ? 16 : 8) * D * 4,
+                "stage layout (a wavefront's ring holds its O rows after the loop)");
 
-  __shared__ float q_s[8][D];
+  // query rows: up to 16 heads per kv head with one value group (the PV rows
+  // are then the heads), 8 otherwise
+  constexpr int QROWS = VG == 1 ? 16 : 8;
+  __shared__ float q_s[QROWS][D];
   // fine RoPE table, pair-major with the token offset XOR-swizzled by the
   // lane row so that one row's 16 lanes (16 offsets, one pair) hit distinct banks
   __shared__ float2 fine_s[ROPE ? 64 : 1][ROPE ? 32 : 1];
   // the rings; after the streaming loop a wavefront's ring holds its O rows
   __shared__ __attribute__((aligned(16))) uint8_t ring_s[kWaves][NB * SLOT];
-  __shared__ float red_ml[kWaves][8][2];
+  __shared__ float red_ml[kWaves][QROWS][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
@@ -1023,7 +1027,8 @@ static int vfmt(const Plan& p) {
 static int vgroups(const Plan& p) { return is_fp8(p.v.scheme) ? 1 : 128 / p.v.group; }
 
 bool mfma_supported(const Plan& p) {
-  if (p.D != 128 || p.n_rep > 8) return false;
+  // n_rep > 8 only with one value group (checked below: n_rep * groups <= 16)
+  if (p.D != 128 || p.n_rep > 16) return false;
   const int kf = kfmt(p), vf = vfmt(p);
   if (kf < 0 || vf < 0) return false;
   if (p.pre_rope && is_f8(kf)) return false;

@@ -277,3 +277,16 @@ def test_eight_heads_per_kv_head_four_value_groups(name, fmt):
                            kernel=K.KERNEL_MFMA, num_splits=s)
         assert attention_error(out, W.random_queries(37, case.B, case.Hq, case.D, dtype="bf16")[0],
                                st, case) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("Hq,fmt", [
+    (32, dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128)),
+    (32, dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0)),
+    (24, dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 0), R=32, pre_rope=True)),
+])
+def test_up_to_sixteen_heads_per_kv_head(Hq, fmt):
+    """16 (and 12) query heads per kv head with one value group run on the
+    MFMA kernel: the 16 query columns and PV rows are the heads."""
+    case = Case(B=2, Hq=Hq, Hkv=2, D=128, dtype="bf16", **fmt)
+    gc, st, errs = run_case(case, 900, _schedule("stream", 900), seed=43)
+    assert K.KERNEL_MFMA in errs, "the MFMA kernel should cover this shape"
