@@ -216,6 +216,29 @@ int kvq_decode_attention(const kvq_config* cfg, const void* arena, int64_t T,
                          const kvq_attn_options* opt, hipStream_t stream);
 
 /*
+ * One decode step: append one token per sequence at position t0 (t0 >= 1, a
+ * cache started by kvq_quantize_append) and attend over T = t0 + 1 tokens.
+ * The result, cache bytes and output, equals kvq_quantize_append(t0, 1)
+ * followed by kvq_decode_attention(T) (the append order of the decode step:
+ * "...Need Different Axes", section "What should I actually turn on in
+ * production?", and the decode loop of the configs).  When the MFMA kernel
+ * serves the shape and the new token needs no fold (it enters the fp16
+ * window, or both sides are FP8 with no window), the append runs inside the
+ * attention launch: the work-group whose token range holds t0 writes the
+ * token before it reads the cache, so one launch does both; otherwise the
+ * two calls run in turn.  Arguments as in the two calls (k_new, v_new:
+ * [B][Hkv][1][D] in cfg->in_dtype; no FP8 scales or calibration here).
+ */
+int kvq_decode_step(const kvq_config* cfg, void* arena, int64_t t0, const void* k_new,
+                    const void* v_new, const void* q, void* out, float sm_scale,
+                    void* workspace, size_t workspace_bytes, const kvq_attn_options* opt,
+                    hipStream_t stream);
+
+/* Host only: 1 if kvq_decode_step at t0 appends inside the attention launch,
+ * 0 if it runs a separate append first; < 0 on an invalid argument. */
+int kvq_decode_step_fused(const kvq_config* cfg, int64_t t0, const kvq_attn_options* opt);
+
+/*
  * Dequantize the cache as stored (pre-RoPE keys stay unrotated) to fp32
  * [B][Hkv][T][D]: x_hat = code*scale + zero with two roundings (INT_ASYM),
  * code*scale (INT_SYM), E4M3(code)*scale (FP8), window tokens widened from
@@ -227,7 +250,8 @@ int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T,
 /* Static description of a status code. */
 const char* kvq_status_string(int status);
 
-/* ABI version: bumped when the arena layout or a signature changes. */
+/* ABI version: bumped when the arena layout or a signature changes, or an
+ * entry point is added (2: kvq_decode_step). */
 int kvq_abi_version(void);
 
 #ifdef __cplusplus

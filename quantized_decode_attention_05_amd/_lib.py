@@ -70,6 +70,9 @@ _sig = {
     "kvq_workspace_bytes": (C.c_int, [_CFG, C.c_int64, C.POINTER(AttnOptions), C.POINTER(C.c_size_t)]),
     "kvq_decode_attention": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, C.c_float, _P, C.c_size_t,
                                        C.POINTER(AttnOptions), _P]),
+    "kvq_decode_step": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P, _P, C.c_float, _P, C.c_size_t,
+                                  C.POINTER(AttnOptions), _P]),
+    "kvq_decode_step_fused": (C.c_int, [_CFG, C.c_int64, C.POINTER(AttnOptions)]),
     "kvq_dequantize": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P]),
     "kvq_status_string": (C.c_char_p, [C.c_int]),
     "kvq_abi_version": (C.c_int, []),
@@ -179,6 +182,25 @@ def kvq_decode_attention(cfg: Config, arena, T: int, q, out, sm_scale: float, wo
     st = _lib.kvq_decode_attention(C.byref(cfg), _ptr(arena), T, _ptr(q), _ptr(out), sm_scale,
                                    _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
     _check(st, "kvq_decode_attention")
+
+
+def kvq_decode_step(cfg: Config, arena, t0: int, k_new, v_new, q, out, sm_scale: float, workspace,
+                    kernel: int = 0, num_splits: int = 0, stream=None) -> None:
+    """Append one token per sequence at t0 (k_new, v_new: [B, Hkv, 1, D]) and
+    attend over t0 + 1 tokens (q: [B, Hq, D]; out: [B, Hq, D])."""
+    o = _opts(kernel, num_splits)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.kvq_decode_step(C.byref(cfg), _ptr(arena), t0, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                              sm_scale, _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
+    _check(st, "kvq_decode_step")
+
+
+def kvq_decode_step_fused(cfg: Config, t0: int, kernel: int = 0, num_splits: int = 0) -> bool:
+    """Whether kvq_decode_step at t0 appends inside the attention launch."""
+    r = _lib.kvq_decode_step_fused(C.byref(cfg), t0, C.byref(_opts(kernel, num_splits)))
+    if r < 0:
+        raise KvqError(int(r), "kvq_decode_step_fused")
+    return bool(r)
 
 
 def kvq_dequantize(cfg: Config, arena, T: int, k_out=None, v_out=None, stream=None) -> None:

@@ -162,7 +162,7 @@ using namespace kvq;
 
 extern "C" {
 
-int kvq_abi_version(void) { return 1; }
+int kvq_abi_version(void) { return 2; }
 
 const char* kvq_status_string(int s) {
   switch (s) {
@@ -301,6 +301,68 @@ int kvq_decode_attention(const kvq_config* cfg, const void* arena, int64_t T, co
   hipError_t e = launch_attention(p, ap, arena, q, out, sm_scale, workspace, stream);
   if (e == hipSuccess) e = hipGetLastError();
   return hip_status(e, "kvq_decode_attention");
+}
+
+// How a decode step at t0 runs: 1 = new token into the fp16 window inside the
+// attention launch, 2 = FP8 codes of the new token inside the attention
+// launch, 0 = a separate append first (a fold, or a shape the MFMA kernel
+// does not serve).
+static int step_mode(const Plan& p, const AttnPlan& ap, int64_t t0) {
+  if (ap.kernel != 2) return 0;
+  const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + 1);
+  if (q_hi == q_lo) return 1;
+  if (is_fp8(p.k.scheme) && is_fp8(p.v.scheme) && !p.window && q_hi == q_lo + 1) return 2;
+  return 0;
+}
+
+int kvq_decode_step_fused(const kvq_config* cfg, int64_t t0, const kvq_attn_options* opt) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if (t0 < 1) return KVQ_ERR_INVALID_ARG;
+  if (t0 + 1 > p.max_tokens) return KVQ_ERR_CAPACITY;
+  if (p.one_shot) return KVQ_ERR_UNSUPPORTED;
+  AttnPlan ap;
+  st = make_attn_plan(p, t0 + 1, opt, &ap);
+  if (st != KVQ_OK) return st;
+  return step_mode(p, ap, t0) != 0 ? 1 : 0;
+}
+
+int kvq_decode_step(const kvq_config* cfg, void* arena, int64_t t0, const void* k_new,
+                    const void* v_new, const void* q, void* out, float sm_scale, void* workspace,
+                    size_t workspace_bytes, const kvq_attn_options* opt, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if (t0 < 1) return KVQ_ERR_INVALID_ARG;                 // a cache is started by quantize_append
+  if (t0 + 1 > p.max_tokens) return KVQ_ERR_CAPACITY;
+  if (p.one_shot) return KVQ_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_ERR_INVALID_ARG;
+  const int64_t T = t0 + 1;
+  AttnPlan ap;
+  st = make_attn_plan(p, T, opt, &ap);
+  if (st != KVQ_OK) return st;
+  if (!arena || !k_new || !v_new || !q || !out || (ap.workspace_bytes && !workspace)) return KVQ_ERR_NULL;
+  if (!aligned(arena, 256) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q, 16) ||
+      !aligned(out, 16) || (workspace && !aligned(workspace, 256)))
+    return KVQ_ERR_ALIGN;
+  if (workspace_bytes < ap.workspace_bytes) return KVQ_ERR_WORKSPACE;
+  // one launch when the new token needs no fold: it goes to the fp16 window,
+  // or (FP8, no window) it is encoded alone with the stored scales
+  const int mode = step_mode(p, ap, t0);
+  if (log_enabled())
+    fprintf(stderr, "[kvq] decode step t0=%lld mode=%d kernel=%d splits=%d\n", (long long)t0, mode,
+            ap.kernel, ap.splits);
+  if (mode == 0) {
+    st = kvq_quantize_append(cfg, arena, t0, 1, k_new, v_new, nullptr, nullptr, 0, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_decode_attention(cfg, arena, T, q, out, sm_scale, workspace, workspace_bytes, opt, stream);
+  }
+  (void)hipGetLastError();
+  StepAppend app{k_new, v_new, t0, mode};
+  hipError_t e = launch_attention(p, ap, arena, q, out, sm_scale, workspace, stream, &app);
+  if (e == hipSuccess) e = hipGetLastError();
+  return hip_status(e, "kvq_decode_step");
 }
 
 int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T, float* k_out,

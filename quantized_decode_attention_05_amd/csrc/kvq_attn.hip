@@ -261,14 +261,15 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
 }
 
 hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                                 float sm_scale, void* ws, hipStream_t s);
+                                 float sm_scale, void* ws, hipStream_t s, const StepAppend* app);
 
 hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                            void* out, float sm_scale, void* ws, hipStream_t s) {
+                            void* out, float sm_scale, void* ws, hipStream_t s, const StepAppend* app) {
+  if (app && app->mode != 0 && ap.kernel != 2) return hipErrorInvalidValue;   // MFMA kernel only
   float* ws_o = (float*)((uint8_t*)ws + ap.ws_o);
   float* ws_ml = (float*)((uint8_t*)ws + ap.ws_ml);
   if (ap.kernel == 2) {
-    hipError_t e = launch_attention_mfma(p, ap, arena, q, sm_scale, ws, s);
+    hipError_t e = launch_attention_mfma(p, ap, arena, q, sm_scale, ws, s, app);
     if (e != hipSuccess) return e;
   } else {
     AttnArgs a{(const uint8_t*)arena, q, ws_o, ws_ml, ap.T, ap.Tq, ap.chunk, ap.splits,

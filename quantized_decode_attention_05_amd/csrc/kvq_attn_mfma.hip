@@ -39,6 +39,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_launch.h"
+#include "kvq_device.h"
 
 namespace kvq {
 
@@ -76,6 +77,13 @@ struct Args {
   int32_t S;
   float qscale;
   float neg1;   // -1.0f, passed in so that r - (float)h stays one mixed fp16/fp32 FMA
+  // decode step: the new token of every sequence, appended by the work-group
+  // whose range holds position t_new (mode 1: fp16 window, 2: FP8 codes)
+  const void* k_new;
+  const void* v_new;
+  int64_t t_new;
+  int32_t app_mode;
+  uint8_t* arena_w;   // the arena, writable (decode-step appends only)
 };
 
 __device__ __forceinline__ half8 pack8(u32 a, u32 b, u32 c, u32 d) {
@@ -420,6 +428,34 @@ attn_mfma(Plan p, Args a) {
   const int64_t bh = (int64_t)b * p.Hkv + kvh;
   const uint8_t* arena = a.arena;
 
+  // decode step: append the new token of this (sequence, kv head) first when
+  // it falls in this split (threads 0..D-1 write its key, D..2D-1 its value),
+  // exactly as the append kernels do; the stores complete before the barrier
+  // below, ahead of every read of the cache by this work-group.
+  if (a.app_mode != 0 && a.t_new >= (int64_t)split * a.chunk && a.t_new < (int64_t)split * a.chunk + a.chunk &&
+      tid < 2 * D) {
+    const bool is_v = tid >= D;
+    const int c = is_v ? tid - D : tid;
+    const int64_t t = a.t_new;
+    const float x = load_in(is_v ? a.v_new : a.k_new, bh * D + c, p.in_dtype);
+    if (a.app_mode == 1) {
+      const int64_t slot = t % p.Rs;
+      if (!is_v) {
+        ((_Float16*)(a.arena_w + p.ring_k))[(bh * p.Rs + slot) * D + c] = (_Float16)x;
+      } else {
+        const int rblock = kVBlock * D * 2;
+        uint8_t* base = a.arena_w + p.ring_v + (uint64_t)bh * (p.Rs / kVBlock) * rblock;
+        ((_Float16*)(base + vblock_word_byte(slot, c, D, 16, rblock)))[slot & 7] = (_Float16)x;
+      }
+    } else {
+      const SideFmt& f = is_v ? p.v : p.k;
+      const float s = ((const float*)(a.arena_w + f.scale))[kvh];
+      const uint8_t code = (uint8_t)(f.scheme == KVQ_FP8_E4M3 ? e4m3_encode(x / s) : e5m2_encode(x / s));
+      if (!is_v) a.arena_w[p.k.codes + (bh * p.Tc + t) * p.k_row_bytes + c] = code;
+      else a.arena_w[p.v.codes + bh * p.v_nblk * p.v_block_bytes + vblock_word_byte(t, c, D, 8, p.v_block_bytes) + (t & 7)] = code;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   for (int e = tid; e < n_rep * D; e += 256) {
     const int r = e / D, c = e % D;
     q_s[r][c] = load_in(a.q, ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c, p.in_dtype) * a.qscale;
@@ -1090,9 +1126,11 @@ static void launch_k(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
 }
 
 hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                                 float sm_scale, void* ws, hipStream_t s) {
+                                 float sm_scale, void* ws, hipStream_t s, const StepAppend* app) {
   Args a{(const uint8_t*)arena, q, (float*)((uint8_t*)ws + ap.ws_o), (float*)((uint8_t*)ws + ap.ws_ml),
-         ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e, -1.0f};
+         ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e, -1.0f,
+         app ? app->k : nullptr, app ? app->v : nullptr, app ? app->t : 0, app ? app->mode : 0,
+         (uint8_t*)arena};
   dim3 grid(ap.splits, p.Hkv, p.B);
   switch (kfmt(p)) {
     case INT2: launch_k<INT2>(p, grid, s, a); break;

@@ -16,6 +16,17 @@ struct AttnPlan {
 };
 
 int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPlan* ap);
+
+// One token per sequence appended by the attention launch itself (decode
+// step): mode 1 writes it into the fp16 window, mode 2 encodes it as FP8 (no
+// window); the work-group whose token range holds position t writes it before
+// it streams the cache.
+struct StepAppend {
+  const void* k;   // [B][Hkv][1][D] in in_dtype
+  const void* v;
+  int64_t t;
+  int32_t mode;    // 0: none
+};
 bool mfma_supported(const Plan& p);
 
 hipError_t launch_rope_tables(const Plan& p, void* arena, hipStream_t s);
@@ -29,6 +40,7 @@ hipError_t launch_ring_write(const Plan& p, void* arena, int64_t t0, int n_new, 
 hipError_t launch_dequantize(const Plan& p, const void* arena, int64_t T, float* k_out,
                              float* v_out, hipStream_t s);
 hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                            void* out, float sm_scale, void* ws, hipStream_t s);
+                            void* out, float sm_scale, void* ws, hipStream_t s,
+                            const StepAppend* app = nullptr);
 
 }  // namespace kvq

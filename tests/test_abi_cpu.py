@@ -202,3 +202,36 @@ def test_workspace_monotone_in_T(fmt):
                 ws = K.kvq_workspace_bytes(cfg, T, kern)
                 assert ws >= prev
                 prev = ws
+
+
+def test_decode_step_fusion_query_and_validation():
+    """Host-only: which decode steps append inside the attention launch, and
+    the step entry point's argument checks (no GPU needed)."""
+    win = _cfg(batch=2, num_q_heads=8, num_kv_heads=2, max_tokens=1000, k=(K.INT_ASYM, 2, K.PER_CHANNEL, 32),
+               v=(K.INT_ASYM, 2, K.PER_TOKEN, 32), residual=32)
+    # window 32, key group 32: the step that completes a group of 32 beyond the window folds
+    fused = [K.kvq_decode_step_fused(win, t) for t in range(64, 140)]
+    for t, f in zip(range(64, 140), fused):
+        folds = K.kvq_quantized_tokens(win, t + 1) != K.kvq_quantized_tokens(win, t)
+        assert f == (not folds), t
+    fp8 = _cfg(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E5M2, 8, 0, 0), residual=0)
+    assert all(K.kvq_decode_step_fused(fp8, t) for t in (1, 17, 500))
+    fp8w = _cfg(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0), residual=32)
+    assert not K.kvq_decode_step_fused(fp8w, 100)             # every step folds one token
+    assert not K.kvq_decode_step_fused(fp8, 100, kernel=K.KERNEL_GENERIC)
+    tok = _cfg(k=(K.INT_ASYM, 4, K.PER_TOKEN, 0), v=(K.INT_ASYM, 4, K.PER_TOKEN, 0), residual=0)
+    assert not K.kvq_decode_step_fused(tok, 100)              # quantizes the token (reductions)
+    with pytest.raises(K.KvqError):
+        K.kvq_decode_step_fused(win, 0)                       # a cache starts with quantize_append
+    raw = _lib.raw
+    ws = K.kvq_workspace_bytes(win, 101)
+    o = K.AttnOptions()
+
+    def step(t0=100, k=0x200000, v=0x300000, q=0x400000, out=0x500000, sm=0.088, w=0x600000, wb=ws):
+        return raw.kvq_decode_step(C.byref(win), 0x100000, t0, k, v, q, out, sm, w, wb, C.byref(o), None)
+    assert step(t0=0) == -1
+    assert step(t0=1000) == -3
+    assert step(k=0) == -5
+    assert step(v=0x300004) == -4
+    assert step(sm=0.0) == -1
+    assert step(wb=16) == -6

@@ -290,3 +290,50 @@ def test_up_to_sixteen_heads_per_kv_head(Hq, fmt):
     case = Case(B=2, Hq=Hq, Hkv=2, D=128, dtype="bf16", **fmt)
     gc, st, errs = run_case(case, 900, _schedule("stream", 900), seed=43)
     assert K.KERNEL_MFMA in errs, "the MFMA kernel should cover this shape"
+
+
+@pytest.mark.parametrize("name,fmt,fused", [
+    ("int2ch32_int2tok32_R32_prerope", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True), True),
+    ("int4ch128_int4tok_R128", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128), True),
+    ("fp8_e4m3", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0), True),
+    ("e4m3_k_e5m2_v", dict(k=(F8, 8, 0, 0), v=(E5, 8, 0, 0), R=0), True),
+    ("fp8_e4m3_R32", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=32), False),
+    ("int4tok_int4tok_R0", dict(k=(A, 4, TOK, 0), v=(A, 4, TOK, 0), R=0), False),
+])
+def test_decode_step_equals_append_then_attention(name, fmt, fused):
+    """kvq_decode_step (append inside the attention launch when no fold is due)
+    leaves the same cache bytes and gives the same output, bit for bit, as
+    kvq_quantize_append followed by kvq_decode_attention, over 40 steps that
+    cross fold boundaries."""
+    import math
+    import torch
+    from tests.kvq_harness import to_dev
+    case = Case(B=2, Hq=8, Hkv=2, D=128, dtype="bf16", **fmt)
+    T0, n = 360, 40
+    (Kf, Kp), (Vf, Vp) = W.random_case(47, case.B, case.Hkv, T0 + n, case.D, dtype="bf16")
+    ga, gb = GpuCache(case, cap=T0 + n), GpuCache(case, cap=T0 + n)
+    flags = K.CALIBRATE if case.k[0] == F8 else 0
+    ga.append(Kp[:, :, :T0], Vp[:, :, :T0], flags)
+    gb.append(Kp[:, :, :T0], Vp[:, :, :T0], flags)
+    sm = 1.0 / math.sqrt(case.D)
+    wa = torch.zeros(K.kvq_workspace_bytes(ga.cfg, T0 + n), dtype=torch.uint8, device="cuda")
+    wb = torch.zeros(K.kvq_workspace_bytes(gb.cfg, T0 + n), dtype=torch.uint8, device="cuda")
+    oa = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    n_fused = 0
+    for i in range(n):
+        t = T0 + i
+        kn, vn = to_dev(Kp[:, :, t:t + 1], case.dtype), to_dev(Vp[:, :, t:t + 1], case.dtype)
+        q = to_dev(W.random_queries(1000 + i, case.B, case.Hq, case.D, dtype="bf16")[1], case.dtype)
+        n_fused += K.kvq_decode_step_fused(ga.cfg, t)
+        oa.fill_(float("nan"))
+        ob.fill_(float("nan"))
+        K.kvq_decode_step(ga.cfg, ga.arena, t, kn, vn, q, oa, sm, wa)
+        K.kvq_quantize_append(gb.cfg, gb.arena, t, kn, vn)
+        K.kvq_decode_attention(gb.cfg, gb.arena, t + 1, q, ob, sm, wb)
+        torch.cuda.synchronize()
+        assert torch.equal(ga.arena, gb.arena), (name, t, "cache bytes differ")
+        assert torch.isfinite(oa).all() and torch.equal(oa, ob), (name, t, "outputs differ")
+    assert (n_fused > 0) == fused, (name, n_fused)
+    if fused and case.R:
+        assert n_fused < n     # the steps that fold run the append separately
