@@ -40,7 +40,7 @@ FORMATS = {
 LIMITER = {
     "c3_fp8_e4m3_gqa_8k": "hbm streaming (~6.7 TB/s marginal) plus ~8.6 us fixed per-launch cost",
     "c3_fp8_e5m2_gqa_8k": "hbm streaming plus fixed per-launch cost, as the E4M3 cache",
-    "c4_int4_llama70b_128k": "~15 us fixed per-launch cost (two kernels, start-up) over ~6.3 TB/s marginal streaming",
+    "c4_int4_llama70b_128k": "~11 us fixed per-launch cost at batch 1 (two kernels, start-up) over ~5.1 TB/s streaming, latency-bound 32-token steps at two wavefronts per SIMD",
     "c5_int2_kivi_prerope_32k": "vector-ALU issue (~90% busy): pre-RoPE dequantize, rotation and fp16 split per key pair",
 }
 DESCR = {
@@ -241,6 +241,12 @@ def main():
                          "workload appends nothing and its arena is under 1 GiB, else 1), so that "
                          "a cache small enough for MI355X's 256 MB Infinity Cache is not re-read "
                          "from it")
+    ap.add_argument("--context", type=int, default=0, metavar="T",
+                    help="prefill context length in place of the workload's own (same format, seeds "
+                         "and value recipe; a measurement of the format at another size, reported "
+                         "under a derived workload name)")
+    ap.add_argument("--batch", type=int, default=0, metavar="B",
+                    help="number of sequences in place of the workload's own (as --context)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device-to-device 3 times (a plain "
                          "copy kernel of known size that calibrates hardware byte counters)")
@@ -256,9 +262,15 @@ def main():
     import quantized_decode_attention_05_amd as K
     import workloads as W
 
-    name = a.workload
-    w = W.WORKLOADS[name]
-    fmt = FORMATS[name]
+    base = a.workload
+    name = base
+    w = W.WORKLOADS[base]
+    if a.context or a.batch:
+        # the same cache format and inputs recipe at another context / batch size
+        w = dict(w, T=a.context or w["T"], B=a.batch or w["B"])
+        name = f"{base}@B{w['B']}_T{w['T']}"
+        W.WORKLOADS[name] = w
+    fmt = FORMATS[base]
     kspec, vspec, R, pre_rope, calibrate = fmt
     B, Hq, Hkv, D, T0 = w["B"], w["Hq"], w["Hkv"], w["D"], w["T"]
     n_new = w.get("n_new", 0)
@@ -380,7 +392,7 @@ def main():
         "dtype": "int2+fp32" if kspec[1] == 2 else ({3: "fp8e4m3+fp32", 4: "fp8e5m2+fp32"}.get(kspec[0], "int4+fp32")),
         "data": "synthetic (seeded Gaussian K/V with fixed outlier key channels, bf16)",
         "config": {
-            "workload": name, "format": DESCR[name], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+            "workload": name, "format": DESCR[base], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
             "head_dim": D, "context_start": T_first, "context_end": T, "append_tokens_per_step": n_new,
             "attention_kernel": {1: "generic", 2: "mfma"}[used_kernel],
             "arena_copies": copies,
@@ -398,12 +410,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
             "kernel": "decode attention launch: pass 1 (split-K) + merge; mean of back-to-back launches between two HIP events on the launch stream",
-            "limiter": LIMITER[name],
+            "limiter": LIMITER[base] if name == base else "not recorded for this size",
         },
     }
     if warm_us is not None:
         res["attention_us_one_arena_warm"] = round(warm_us, 3)
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name) if name == base else None
     if traffic is not None:
         res["roofline"]["traffic"] = traffic["bytes_per_launch"]
         res["roofline"]["traffic_source"] = traffic["source"]
