@@ -352,13 +352,27 @@ __device__ __forceinline__ void load_dw(const uint8_t* p, u32* w) {
   }
 }
 
+// Lane pairs (l, l ^ 16) and (l, l ^ 32) through gfx950's permlane swaps (VALU
+// operations, no LDS round trip).  Swapping a value with itself leaves each lane
+// holding its own value in one result and its partner's in the other, so a
+// symmetric combination of the two equals x op partner in every lane (and fp32
+// addition and max are commutative, so the results match a shuffle exactly).
+// Called with the whole wavefront active.
 __device__ __forceinline__ float wave_max16(float x) {   // max over lanes n, n+16, n+32, n+48
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  const u32 b = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const u32 c = __float_as_uint(x);
+  const auto t = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float wave_sum16(float x) {
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
+  const u32 b = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const u32 c = __float_as_uint(x);
+  const auto t = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
