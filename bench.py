@@ -56,9 +56,10 @@ def code_bits(spec):
     return bits if scheme in (0, 1) else 8
 
 
-def algorithmic_bytes(w, fmt, T):
+def algorithmic_bytes(w, fmt, T, meta_bytes=4):
     """Bytes one decode attention over T tokens must move: every packed code, its
-    fp32 scale/zero and the fp16 window read once, q (bf16) read, out (fp32) written."""
+    scale/zero (fp32, or fp16 with meta_bytes=2) and the fp16 window read once,
+    q (bf16) read, out (fp32) written."""
     kspec, vspec, R, _, _ = fmt
     B, Hq, Hkv, D = w["B"], w["Hq"], w["Hkv"], w["D"]
     G = kspec[3] if (kspec[0] in (1, 2) and kspec[2] == 1 and kspec[3] > 0) else 1
@@ -69,18 +70,18 @@ def algorithmic_bytes(w, fmt, T):
         nmeta = 2 if spec[0] == 1 else 1
         if spec[0] in (1, 2):
             if spec[2] == 1:
-                per += (Tq // spec[3] if spec[3] else 1) * D * 4 * nmeta
+                per += (Tq // spec[3] if spec[3] else 1) * D * meta_bytes * nmeta
             elif spec[2] == 2:
-                per += Tq * (D // (spec[3] or D)) * 4 * nmeta
+                per += Tq * (D // (spec[3] or D)) * meta_bytes * nmeta
             else:
-                per += 4 * nmeta
+                per += meta_bytes * nmeta
     per += (T - Tq) * D * 2 * 2
     total = per * B * Hkv
     fp8_scales = 8 * Hkv if kspec[0] in (3, 4) else 0
     return total + fp8_scales + B * Hq * D * 2 + B * Hq * D * 4, Tq
 
 
-def cpu_baseline(name, w, fmt, T, bytes_per_step, budget_s=12.0):
+def cpu_baseline(name, w, fmt, T, bytes_per_step, budget_s=12.0, meta16=False):
     """The oracle as it stands, on host cores: per sampled (sequence, kv head),
     dequantize the cache from its codes and run fp64 attention for its query
     heads; scaled to the whole step."""
@@ -91,7 +92,8 @@ def cpu_baseline(name, w, fmt, T, bytes_per_step, budget_s=12.0):
 
     kspec, vspec, R, pre_rope, calibrate = fmt
     n_rep = w["Hq"] // w["Hkv"]
-    sub = OC.Cfg(1, n_rep, 1, w["D"], OC.Spec(*kspec), OC.Spec(*vspec), R, pre_rope, w.get("rope_base", 1e4))
+    sub = OC.Cfg(1, n_rep, 1, w["D"], OC.Spec(*kspec, meta16=meta16), OC.Spec(*vspec, meta16=meta16), R, pre_rope,
+                 w.get("rope_base", 1e4))
     q = W.bf16_bits_to_f32(W.query(name))
     sm = 1.0 / math.sqrt(w["D"])
     done, spent = 0, 0.0
@@ -245,6 +247,9 @@ def main():
                     help="prefill context length in place of the workload's own (same format, seeds "
                          "and value recipe; a measurement of the format at another size, reported "
                          "under a derived workload name)")
+    ap.add_argument("--meta-f16", action="store_true",
+                    help="store the INT sides' scales and zero-points in fp16 (reported under a "
+                         "derived workload name)")
     ap.add_argument("--batch", type=int, default=0, metavar="B",
                     help="number of sequences in place of the workload's own (as --context)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -270,6 +275,10 @@ def main():
         w = dict(w, T=a.context or w["T"], B=a.batch or w["B"])
         name = f"{base}@B{w['B']}_T{w['T']}"
         W.WORKLOADS[name] = w
+    if a.meta_f16:
+        name = f"{name}+meta16"
+        W.WORKLOADS[name] = w
+    meta_bytes = 2 if a.meta_f16 else 4
     fmt = FORMATS[base]
     kspec, vspec, R, pre_rope, calibrate = fmt
     B, Hq, Hkv, D, T0 = w["B"], w["Hq"], w["Hkv"], w["D"], w["T"]
@@ -278,7 +287,8 @@ def main():
     cap = T0 + n_new * (steps_total + 1) + 64
     cfg = K.make_config(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_tokens=cap,
                         k=kspec, v=vspec, in_dtype=K.BF16, out_dtype=K.F32, residual=R,
-                        pre_rope_k=pre_rope, rope_base=w.get("rope_base", 10000.0))
+                        pre_rope_k=pre_rope, rope_base=w.get("rope_base", 10000.0),
+                        meta_dtype=K.F16 if a.meta_f16 else K.F32)
     dev = torch.device("cuda:0")
     print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
     kp = torch.from_numpy(W.full_prefill(name, "k").view(np.int16)).view(torch.bfloat16).to(dev)
@@ -367,8 +377,8 @@ def main():
         torch.cuda.synchronize()
         warm_us = 1000.0 * w_start.elapsed_time(w_end) / a.steps
     T_mid = (T_first + T) // 2
-    bytes_step, Tq = algorithmic_bytes(w, fmt, T_mid)
-    bytes_attn = algorithmic_bytes(w, fmt, T)[0]       # the attention-only launches ran at T
+    bytes_step, Tq = algorithmic_bytes(w, fmt, T_mid, meta_bytes)
+    bytes_attn = algorithmic_bytes(w, fmt, T, meta_bytes)[0]   # the attention-only launches ran at T
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     used_kernel = a.kernel
@@ -396,6 +406,7 @@ def main():
             "head_dim": D, "context_start": T_first, "context_end": T, "append_tokens_per_step": n_new,
             "attention_kernel": {1: "generic", 2: "mfma"}[used_kernel],
             "arena_copies": copies,
+            "scale_zero_dtype": "f16" if a.meta_f16 else "f32",
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 2),
         "attention_us": round(attn_us, 3),
@@ -430,8 +441,8 @@ def main():
         res["copy_probe_bytes"] = nbytes
     if not a.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(name, w, fmt, T_first, algorithmic_bytes(w, fmt, T_first)[0],
-                                           a.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(name, w, fmt, T_first, algorithmic_bytes(w, fmt, T_first, meta_bytes)[0],
+                                           a.cpu_budget, meta16=a.meta_f16)
     print(json.dumps(res), flush=True)
 
 

@@ -106,8 +106,24 @@ typedef struct kvq_config {
   int32_t residual;       /* R: most recent tokens kept in fp16 (0 = none)       */
   int32_t pre_rope_k;     /* 1: keys are cached before RoPE and rotated in attention */
   float   rope_base;      /* RoPE base (theta_i = base^(-2i/D)) when pre_rope_k  */
-  int32_t reserved;       /* must be 0                                           */
+  int32_t meta_dtype;     /* storage of the scale / zero-point of INT sides:     */
+                          /* KVQ_F32 (0) or KVQ_F16 (1), see below               */
 } kvq_config;
+
+/*
+ * fp16 scale / zero-point metadata (meta_dtype = KVQ_F16; FP8 scales stay
+ * fp32).  Halves the metadata bytes, which for small groups are as large as
+ * the codes (INT2 with groups of 32: 8 bytes of fp32 scale and zero per 32
+ * two-bit codes).  The stored values are chosen so that the group still spans
+ * its range: asymmetric groups store z = the largest fp16 <= the group
+ * minimum and s = the smallest fp16 >= fl(max(fl(max - z), 1e-8) / (2^b - 1));
+ * symmetric groups s = the smallest fp16 >= fl(max(absmax, 1e-8) / 127).
+ * Codes and dequantization then use these fp16 values (exactly, in fp32) in
+ * the formulas of the fp32 case, so |x - x_hat| <= s / 2 still holds, with s
+ * the stored fp16 scale.  Values outside the fp16 range saturate the stored
+ * z or s at +-65504 (their codes then clip); the bound needs every group
+ * within +-65504 and ranges up to 65504 * (2^b - 1).
+ */
 
 /*
  * Arena layout.  One caller-allocated device buffer holds the whole cache; its
@@ -118,9 +134,11 @@ typedef struct kvq_config {
  *  k_codes  [B][H][Tc][D*bK/8]   token rows: channel c at bit bK*(c mod 8/bK)
  *                                of byte c*bK/8, low bits first; INT_SYM is
  *                                two's complement; NONE stores fp16/fp32 LE.
- *  k_scale  fp32 PER_TENSOR [B][H]; PER_CHANNEL [B][H][Tc/G or 1][D];
- *                PER_TOKEN [B][H][Tc][D/Gc]; FP8 [H] (1.0 for E5M2).
- *  k_zero   fp32, same shape as k_scale (INT_ASYM only; the group minimum).
+ *  k_scale  fp32 (fp16 for INT sides when meta_dtype = KVQ_F16)
+ *                PER_TENSOR [B][H]; PER_CHANNEL [B][H][Tc/G or 1][D];
+ *                PER_TOKEN [B][H][Tc][D/Gc]; FP8 [H] fp32 (1.0 for E5M2).
+ *  k_zero   same type and shape as k_scale (INT_ASYM only; the group
+ *                minimum, or its fp16 rounding toward -inf).
  *  v_codes  [B][H][Tc/32][32*D*bV/8]  32-token blocks: token t = 32*blk +
  *                8*g + k and channel c = 16*i + n go to word i of lane
  *                l = 16*g + n; each lane owns D/16 consecutive words of 8*bV
@@ -251,7 +269,7 @@ int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T,
 const char* kvq_status_string(int status);
 
 /* ABI version: bumped when the arena layout or a signature changes, or an
- * entry point is added (2: kvq_decode_step). */
+ * entry point is added (2: kvq_decode_step; 3: kvq_config.meta_dtype). */
 int kvq_abi_version(void);
 
 #ifdef __cplusplus

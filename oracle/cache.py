@@ -47,6 +47,7 @@ class Spec:
     bits: int = 8
     axis: int = PER_CHANNEL
     group: int = 0
+    meta16: bool = False    # INT scale / zero-point stored in fp16 (quant.asym_quantize)
 
 
 @dataclass
@@ -139,10 +140,10 @@ def quantize_part(x: np.ndarray, spec: Spec, fp8_scale=None):
         xg = x.reshape(B, H, T, D // Gc, Gc)
         red = 4
     if spec.scheme == INT_ASYM:
-        c, s, z = Q.asym_quantize(xg, spec.bits, axis=red)
+        c, s, z = Q.asym_quantize(xg, spec.bits, axis=red, meta16=spec.meta16)
         deq = Q.asym_dequantize(c, s, z)
     else:
-        c, s = Q.sym_quantize(xg, axis=red)
+        c, s = Q.sym_quantize(xg, axis=red, meta16=spec.meta16)
         z = None
         deq = Q.sym_dequantize(c, s)
     s = np.squeeze(s, axis=red)

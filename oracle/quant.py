@@ -48,22 +48,47 @@ def stage(x: np.ndarray, through_fp16: bool) -> np.ndarray:
 # asymmetric min-max (scale + zero-point = group minimum)
 # ----------------------------------------------------------------------------
 
-def asym_quantize(x: np.ndarray, bits: int, axis):
+F16_MAX = F32(65504.0)
+
+
+def f16_toward(x, up: bool) -> np.ndarray:
+    """The fp16 value next to fp32 ``x`` on the side of +inf (up) or -inf
+    (down), returned as fp32, saturated at +-65504 (fp16 storage of a scale or
+    zero-point that must not shrink the range it covers)."""
+    x = np.asarray(x, dtype=F32)
+    with np.errstate(over="ignore"):    # beyond +-65504: saturated below
+        h = x.astype(np.float16)
+        hf = h.astype(F32)
+        wrong = (hf < x) if up else (hf > x)
+        h = np.where(wrong, np.nextafter(h, np.float16(np.inf if up else -np.inf)), h)
+    return np.clip(h.astype(F32), -F16_MAX, F16_MAX).astype(F32)
+
+
+def asym_quantize(x: np.ndarray, bits: int, axis, meta16: bool = False):
     """Quantize fp32 ``x`` with one (scale, zero) per reduction over ``axis``.
 
     Returns (codes uint8, scale fp32, zero fp32) with scale/zero keeping the
     reduced dims (keepdims=True) so they broadcast against ``x``.
+
+    meta16: the scale and zero-point are stored in fp16.  The zero-point is the
+    group minimum rounded toward -inf and the scale is computed from it and
+    rounded toward +inf, so the stored grid still covers [min, max] and the
+    reconstruction error stays within half the stored scale; codes are then
+    taken against the stored values.
     """
     x = np.asarray(x, dtype=F32)
     qmax = F32(2 ** bits - 1)
     mn = x.min(axis=axis, keepdims=True)
     mx = x.max(axis=axis, keepdims=True)
-    d = np.maximum((mx - mn).astype(F32), EPS)
+    z = f16_toward(mn, up=False) if meta16 else mn
+    d = np.maximum((mx - z).astype(F32), EPS)
     s = (d / qmax).astype(F32)
-    t = ((x - mn).astype(F32) / s).astype(F32)
+    if meta16:
+        s = f16_toward(s, up=True)
+    t = ((x - z).astype(F32) / s).astype(F32)
     codes = np.clip(np.rint(t), F32(0), qmax).astype(np.uint8)
     # -0.0 vs 0.0 min is irrelevant for codes; keep the min as stored zero-point
-    return codes, s, mn.astype(F32)
+    return codes, s, z.astype(F32)
 
 
 def asym_dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
@@ -76,11 +101,14 @@ def asym_dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> n
 # symmetric absmax INT8
 # ----------------------------------------------------------------------------
 
-def sym_quantize(x: np.ndarray, axis):
-    """Symmetric INT8 with scale = max(absmax, 1e-8) / 127 and codes in [-127, 127]."""
+def sym_quantize(x: np.ndarray, axis, meta16: bool = False):
+    """Symmetric INT8 with scale = max(absmax, 1e-8) / 127 and codes in [-127, 127]
+    (meta16: the scale stored in fp16, rounded toward +inf)."""
     x = np.asarray(x, dtype=F32)
     a = np.abs(x).max(axis=axis, keepdims=True)
     s = (np.maximum(a, EPS) / F32(127.0)).astype(F32)
+    if meta16:
+        s = f16_toward(s, up=True)
     t = (x / s).astype(F32)
     codes = np.clip(np.rint(t), F32(-127), F32(127)).astype(np.int8)
     return codes, s

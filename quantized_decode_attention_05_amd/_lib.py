@@ -43,7 +43,7 @@ class Config(C.Structure):
                 ("head_dim", C.c_int32), ("max_tokens", C.c_int64), ("in_dtype", C.c_int32),
                 ("out_dtype", C.c_int32), ("k", TensorSpec), ("v", TensorSpec),
                 ("residual", C.c_int32), ("pre_rope_k", C.c_int32), ("rope_base", C.c_float),
-                ("reserved", C.c_int32)]
+                ("meta_dtype", C.c_int32)]
 
 
 class Layout(C.Structure):
@@ -100,10 +100,11 @@ def _check(st: int, where: str) -> int:
 
 def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, k, v,
                 in_dtype=BF16, out_dtype=F32, residual=0, pre_rope_k=False,
-                rope_base=10000.0) -> Config:
-    """k, v: (scheme, bits, axis, group) tuples."""
+                rope_base=10000.0, meta_dtype=F32) -> Config:
+    """k, v: (scheme, bits, axis, group) tuples; meta_dtype: F32 or F16 storage
+    of the INT sides' scales and zero-points."""
     return Config(batch, num_q_heads, num_kv_heads, head_dim, max_tokens, in_dtype, out_dtype,
-                  TensorSpec(*k), TensorSpec(*v), residual, int(bool(pre_rope_k)), rope_base, 0)
+                  TensorSpec(*k), TensorSpec(*v), residual, int(bool(pre_rope_k)), rope_base, meta_dtype)
 
 
 def _ptr(t):

@@ -87,7 +87,7 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   if (cfg->max_tokens < 1 || cfg->max_tokens > ((int64_t)1 << 31)) return KVQ_ERR_INVALID_ARG;
   if (cfg->in_dtype < KVQ_F32 || cfg->in_dtype > KVQ_BF16) return KVQ_ERR_INVALID_ARG;
   if (cfg->out_dtype < KVQ_F32 || cfg->out_dtype > KVQ_BF16) return KVQ_ERR_INVALID_ARG;
-  if (cfg->reserved != 0) return KVQ_ERR_INVALID_ARG;
+  if (cfg->meta_dtype != KVQ_F32 && cfg->meta_dtype != KVQ_F16) return KVQ_ERR_INVALID_ARG;
   if (cfg->residual < 0 || cfg->pre_rope_k < 0 || cfg->pre_rope_k > 1) return KVQ_ERR_INVALID_ARG;
   if (cfg->pre_rope_k && !(cfg->rope_base > 0.0f)) return KVQ_ERR_INVALID_ARG;
   int st;
@@ -113,6 +113,8 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   p->Tc = round_up(cfg->max_tokens, lcm);
   side_meta(cfg->k, D, p->Tc, p->Hkv, &p->k);
   side_meta(cfg->v, D, p->Tc, p->Hkv, &p->v);
+  p->k.meta16 = cfg->meta_dtype == KVQ_F16 && is_int(cfg->k.scheme);
+  p->v.meta16 = cfg->meta_dtype == KVQ_F16 && is_int(cfg->v.scheme);
   p->k_row_bytes = D * p->k.bits / 8;
   p->v_block_bytes = kVBlock * D * p->v.bits / 8;
   p->v_nblk = p->Tc / kVBlock;
@@ -124,7 +126,7 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   p->k.codes = take(BH * p->Tc * p->k_row_bytes);
   auto meta_bytes = [&](const SideFmt& f) -> uint64_t {
     if (is_fp8(f.scheme)) return (uint64_t)p->Hkv * 4;
-    return BH * f.meta_rows * f.meta_cols * 4;
+    return BH * f.meta_rows * f.meta_cols * (f.meta16 ? 2 : 4);
   };
   p->k.scale = (p->k.scheme == KVQ_NONE) ? NA : take(meta_bytes(p->k));
   p->k.zero = (p->k.scheme == KVQ_INT_ASYM) ? take(meta_bytes(p->k)) : NA;
@@ -162,7 +164,7 @@ using namespace kvq;
 
 extern "C" {
 
-int kvq_abi_version(void) { return 2; }
+int kvq_abi_version(void) { return 3; }
 
 const char* kvq_status_string(int s) {
   switch (s) {

@@ -214,6 +214,34 @@ __device__ __forceinline__ int pcw_pos(int p) { return 2 * km_pos(p >> 1) + (p &
 __device__ __forceinline__ int vm_pos(int t) { return (t & ~7) | ((t + (t >> 3)) & 7); }
 __device__ __forceinline__ int vm_src(int l) { return (l & ~7) | ((l - (l >> 3)) & 7); }
 
+// fp16 scale / zero-point rows staged at reg (scales in bytes [0, 8H), zero-
+// points in [8H, 16H), natural order; H = N / 2) -> the fp32 layout of the
+// same region: granule G < N holds the four values of granule perm(G mod H)
+// of the scale row (G < H) or the zero-point row.  PERM: 0 identity, 1 km_pos,
+// 2 vm_src.  The whole wavefront reads the staged rows before it writes over
+// them (one wavefront's LDS operations complete in order).
+template <int N, int PERM>
+__device__ __forceinline__ void widen_meta(uint8_t* reg, int lane) {
+  constexpr int H = N / 2, PER = (N + 63) / 64;
+  uint2 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int G = lane + 64 * i;
+    const int q = G % H;
+    const int src = PERM == 1 ? km_pos(q) : (PERM == 2 ? vm_src(q) : q);
+    if (G < N) v[i] = *(const uint2*)(reg + (G < H ? 0 : 8 * H) + 8 * src);
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int G = lane + 64 * i;
+    if (G < N) {
+      const half2v a = __builtin_bit_cast(half2v, v[i].x), b = __builtin_bit_cast(half2v, v[i].y);
+      *(float4*)(reg + 16 * G) = make_float4((float)a[0], (float)a[1], (float)b[0], (float)b[1]);
+    }
+  }
+}
+
 // ---- key operand unpacking -------------------------------------------------------
 
 // Exact fp16 codes of one lane's 32 key channels in kslot order, from KB dwords.
@@ -566,14 +594,28 @@ attn_mfma(Plan p, Args a) {
   // first quantized step and advanced by constant strides (the key-metadata
   // pointer by one row when a key group ends).
   const uint8_t *pk = nullptr, *pv = nullptr, *pvm0 = nullptr, *pvm1 = nullptr, *pkm = nullptr, *prp = nullptr;
+  // fp16 scale / zero-point metadata: the stage brings the two fp16 rows
+  // (scales, then zero-points, natural order) into the first half of the
+  // slot's metadata region and widen_meta rebuilds the fp32 granule layout
+  // below from them once the stage has landed
+  const bool vm16 = VINT && p.v.meta16, km16 = KINT && p.k.meta16;
+  const int vesz = vm16 ? 2 : 4, kesz = km16 ? 2 : 4;
   auto init_ptrs = [&](int64_t t0, int64_t kgrp) __attribute__((always_inline)) {
     pk = arena + p.k.codes + (bh * p.Tc + t0) * KROW + 16 * lane;
     pv = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V + 16 * lane;
     if constexpr (VINT) {
       // 16-byte granules: 8*VG of scales, then 8*VG of zero-points
-      const uint8_t* vs = arena + p.v.scale + (bh * p.Tc + t0) * VG * 4;
-      const uint8_t* vz = arena + p.v.zero + (bh * p.Tc + t0) * VG * 4;
-      if constexpr (VG == 8) {
+      const uint8_t* vs = arena + p.v.scale + (bh * p.Tc + t0) * VG * vesz;
+      const uint8_t* vz = arena + p.v.zero + (bh * p.Tc + t0) * VG * vesz;
+      if (vm16) {
+        // 4*VG granules of each fp16 row
+        if constexpr (VG == 8) {
+          pvm0 = vs + 16 * lane;
+          pvm1 = vz + 16 * lane;
+        } else {
+          pvm0 = lane < 4 * VG ? vs + 16 * lane : vz + 16 * (lane - 4 * VG);
+        }
+      } else if constexpr (VG == 8) {
         pvm0 = vs + 16 * lane;
         pvm1 = vz + 16 * lane;
       } else {
@@ -582,10 +624,12 @@ attn_mfma(Plan p, Args a) {
       }
     }
     if constexpr (KINT) {
-      // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key group
-      const int64_t mrow = (bh * p.k.meta_rows + kgrp) * D * 4;
-      pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * km_pos(lane)
-                      : arena + p.k.zero + mrow + 16 * km_pos(lane - 32);
+      // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key
+      // group; fp16 rows: lanes 0-15 and 16-31
+      const int64_t mrow = (bh * p.k.meta_rows + kgrp) * D * kesz;
+      if (km16) pkm = lane < 16 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 16);
+      else pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * km_pos(lane)
+                           : arena + p.k.zero + mrow + 16 * km_pos(lane - 32);
     }
     if constexpr (ROPE) prp = arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane;
   };
@@ -597,13 +641,20 @@ attn_mfma(Plan p, Args a) {
     for (int c = 0; c < SZ_V / 1024; ++c) dma16(sb + OFF_V + 1024 * c, pv + 1024 * c);
     if constexpr (VINT) {
       if constexpr (VG == 8) {
-        dma16(sb + OFF_VM, pvm0);
-        dma16(sb + OFF_VM + 1024, pvm1);
-      } else if (lane < 16 * VG) {
+        if (!vm16) {
+          dma16(sb + OFF_VM, pvm0);
+          dma16(sb + OFF_VM + 1024, pvm1);
+        } else if (lane < 32) {
+          dma16(sb + OFF_VM, pvm0);
+          dma16(sb + OFF_VM + 512, pvm1);
+        }
+      } else if (lane < (vm16 ? 8 : 16) * VG) {
         dma16(sb + OFF_VM, pvm0);
       }
     }
-    if constexpr (KINT) dma16(sb + OFF_KM, pkm);
+    if constexpr (KINT) {
+      if (!km16 || lane < 32) dma16(sb + OFF_KM, pkm);
+    }
     if constexpr (ROPE) {
       if (lane < 32) dma16(sb + OFF_KT, prp);
     }
@@ -612,10 +663,10 @@ attn_mfma(Plan p, Args a) {
     pk += SZ_K;
     pv += SZ_V;
     if constexpr (VINT) {
-      pvm0 += 32 * VG * 4;
-      if constexpr (VG == 8) pvm1 += 32 * VG * 4;
+      pvm0 += 32 * VG * vesz;
+      if constexpr (VG == 8) pvm1 += 32 * VG * vesz;
     }
-    if constexpr (KINT) { if (group_ends) pkm += D * 4; }
+    if constexpr (KINT) { if (group_ends) pkm += D * kesz; }
     if constexpr (ROPE) prp += 64 * 8;
   };
   // Registers of a quantized step from its LDS slot.
@@ -961,6 +1012,12 @@ attn_mfma(Plan p, Args a) {
     for (int64_t st = qs_beg; st < qs_end; ++st) {
       if (st + NB - 2 < qs_end) wait_vmem<N_DMA * (NB - 2)>();
       else wait_vmem<0>();
+      if constexpr (VINT) {
+        if (vm16) widen_meta<VG == 8 ? 128 : 16 * VG, VG == 4 ? 2 : 0>(ring + sl * SLOT + OFF_VM, lane);
+      }
+      if constexpr (KINT) {
+        if (km16) widen_meta<64, 1>(ring + sl * SLOT + OFF_KM, lane);
+      }
       StepData<KDW, VDW, VINT ? 8 : 1> d;
       read_slot(sl, d);
       cur_slot = sl;

@@ -49,6 +49,31 @@ __device__ __forceinline__ int64_t meta_index(const Plan& p, const SideFmt& f, i
   return (bh * p.Tc + t) * f.meta_cols + c / f.group;
 }
 
+// ---- fp16 scale / zero-point metadata ----------------------------------------
+
+// fp16 rounding of finite x toward +inf (up) or -inf (down): the RNE
+// conversion, moved one fp16 step when it landed on the wrong side; results
+// beyond the fp16 range saturate at +-65504.
+__device__ __forceinline__ _Float16 f16_directed(float x, bool up) {
+  _Float16 h = (_Float16)x;
+  const float hf = (float)h;
+  if (up ? hf < x : hf > x) {
+    uint16_t b = __builtin_bit_cast(uint16_t, h);
+    const bool neg = b & 0x8000u;
+    if (up) b = neg ? (b == 0x8000u ? 0x0001u : b - 1) : b + 1;
+    else b = neg ? b + 1 : (b == 0 ? 0x8001u : b - 1);
+    h = __builtin_bit_cast(_Float16, b);
+  }
+  const float r = (float)h;
+  if (r > 65504.0f) h = (_Float16)65504.0f;
+  if (r < -65504.0f) h = (_Float16)-65504.0f;
+  return h;
+}
+
+__device__ __forceinline__ float load_meta(const uint8_t* base, int64_t i, bool m16) {
+  return m16 ? (float)((const _Float16*)base)[i] : ((const float*)base)[i];
+}
+
 // ---- encodings ---------------------------------------------------------------
 
 __device__ __forceinline__ void asym_params(float mn, float mx, int bits, float* s) {
@@ -135,11 +160,11 @@ __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* aren
     return __uint_as_float(code);
   }
   const int64_t mi = meta_index(p, f, b, h, t, c);
-  const float s = ((const float*)(arena + f.scale))[mi];
+  const float s = load_meta(arena + f.scale, mi, f.meta16);
   if (f.scheme == KVQ_FP8_E4M3) return e4m3_decode(code) * s;
   if (f.scheme == KVQ_FP8_E5M2) return e5m2_decode(code) * s;
   if (f.scheme == KVQ_INT_SYM) return (float)(int8_t)(uint8_t)code * s;
-  const float z = ((const float*)(arena + f.zero))[mi];
+  const float z = load_meta(arena + f.zero, mi, f.meta16);
   const float prod = (float)code * s;
   return prod + z;
 }

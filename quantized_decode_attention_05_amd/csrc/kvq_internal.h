@@ -25,7 +25,7 @@ struct SideFmt {
   int32_t axis;       // enum kvq_axis (INT schemes)
   int32_t group;      // resolved: PER_CHANNEL tokens per group (0 = whole axis), PER_TOKEN channels
   int32_t meta_cols;  // innermost extent of scale/zero
-  int32_t pad_;
+  int32_t meta16;     // INT scale / zero stored as fp16 (else fp32)
   int64_t meta_rows;  // rows of scale/zero per (b, h)
   uint64_t codes, scale, zero;  // byte offsets in the arena (UINT64_MAX = absent)
 };

@@ -29,11 +29,11 @@ __device__ __forceinline__ uint32_t encode_elem(const Plan& p, const SideFmt& f,
     return __float_as_uint(x);
   }
   const int64_t mi = meta_index(p, f, b, h, t, c);
-  const float s = ((const float*)(arena + f.scale))[mi];
+  const float s = load_meta(arena + f.scale, mi, f.meta16);
   if (f.scheme == KVQ_FP8_E4M3) return e4m3_encode(x / s);
   if (f.scheme == KVQ_FP8_E5M2) return e5m2_encode(x / s);   // s = 1
   if (f.scheme == KVQ_INT_SYM) return sym_code(x, s);
-  const float z = ((const float*)(arena + f.zero))[mi];
+  const float z = load_meta(arena + f.zero, mi, f.meta16);
   return asym_code(x, s, z, f.bits);
 }
 
@@ -41,7 +41,18 @@ __device__ __forceinline__ uint32_t encode_elem(const Plan& p, const SideFmt& f,
 
 __device__ __forceinline__ void store_meta(const Plan& p, const SideFmt& f, uint8_t* arena,
                                            int64_t mi, float mn, float mx) {
-  if (f.scheme == KVQ_INT_ASYM) {
+  if (f.meta16) {
+    // fp16 storage that still spans the group: zero rounded down, scale up
+    if (f.scheme == KVQ_INT_ASYM) {
+      const _Float16 z = f16_directed(mn, false);
+      float s;
+      asym_params((float)z, mx, f.bits, &s);
+      ((_Float16*)(arena + f.scale))[mi] = f16_directed(s, true);
+      ((_Float16*)(arena + f.zero))[mi] = z;
+    } else {
+      ((_Float16*)(arena + f.scale))[mi] = f16_directed(fmaxf(mx, 1e-8f) / 127.0f, true);
+    }
+  } else if (f.scheme == KVQ_INT_ASYM) {
     float s;
     asym_params(mn, mx, f.bits, &s);
     ((float*)(arena + f.scale))[mi] = s;

@@ -43,16 +43,17 @@ class Case:
     rope_base: float = 10000.0
     dtype: str = "f32"
     cap: int = 0
+    meta16: bool = False     # INT scales / zero-points stored in fp16
 
     def lib_cfg(self, cap):
         return K.make_config(batch=self.B, num_q_heads=self.Hq, num_kv_heads=self.Hkv, head_dim=self.D,
                              max_tokens=cap, k=self.k, v=self.v, in_dtype=_DT[self.dtype][0],
                              out_dtype=K.F32, residual=self.R, pre_rope_k=self.pre_rope,
-                             rope_base=self.rope_base)
+                             rope_base=self.rope_base, meta_dtype=K.F16 if self.meta16 else K.F32)
 
     def oracle_cfg(self, B=None, Hq=None, Hkv=None):
-        return OC.Cfg(B or self.B, Hq or self.Hq, Hkv or self.Hkv, self.D, OC.Spec(*self.k),
-                      OC.Spec(*self.v), self.R, self.pre_rope, self.rope_base)
+        return OC.Cfg(B or self.B, Hq or self.Hq, Hkv or self.Hkv, self.D, OC.Spec(*self.k, meta16=self.meta16),
+                      OC.Spec(*self.v, meta16=self.meta16), self.R, self.pre_rope, self.rope_base)
 
 
 def to_dev(payload: np.ndarray, dtype: str) -> torch.Tensor:
@@ -175,12 +176,17 @@ def compare_sections(gc: GpuCache, st: dict, bh_sel=None):
             continue
         full, used = _meta_shape(spec, B, H, D, Tc, Tq)
         idx = (slice(None), slice(None)) + tuple(slice(0, u) for u in used[2:])
-        sc = sl(getattr(lay, side + "_scale"), full[2:], np.float32)[idx]
-        assert np.array_equal(sc.view(np.uint32), part["scale"].reshape(sc.shape).view(np.uint32)), \
-            f"{side} scales differ"
+        # fp16 metadata: the oracle's stored values are fp16 numbers held in fp32
+        mdt, bits_t = (np.float16, np.uint16) if c.meta16 else (np.float32, np.uint32)
+        sc = sl(getattr(lay, side + "_scale"), full[2:], mdt)[idx]
+        exp_s = part["scale"].reshape(sc.shape)
+        if c.meta16:
+            assert np.array_equal(exp_s.astype(np.float16).astype(np.float32), exp_s)
+        assert np.array_equal(sc.view(bits_t), exp_s.astype(mdt).view(bits_t)), f"{side} scales differ"
         if spec[0] == OC.INT_ASYM:
-            zz = sl(getattr(lay, side + "_zero"), full[2:], np.float32)[idx]
-            assert np.array_equal(zz, part["zero"].reshape(zz.shape)), f"{side} zero-points differ"
+            zz = sl(getattr(lay, side + "_zero"), full[2:], mdt)[idx]
+            exp_z = part["zero"].reshape(zz.shape)
+            assert np.array_equal(zz.astype(np.float32), exp_z), f"{side} zero-points differ"
 
     if T > Tq:
         Rs = lay.ring_slots

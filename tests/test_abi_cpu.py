@@ -235,3 +235,36 @@ def test_decode_step_fusion_query_and_validation():
     assert step(v=0x300004) == -4
     assert step(sm=0.0) == -1
     assert step(wb=16) == -6
+
+
+def test_fp16_metadata_halves_the_int_metadata_sections():
+    for k, v in [((K.INT_ASYM, 2, K.PER_CHANNEL, 32), (K.INT_ASYM, 2, K.PER_TOKEN, 32)),
+                 ((K.INT_SYM, 8, K.PER_TOKEN, 0), (K.INT_SYM, 8, K.PER_TOKEN, 32))]:
+        l32 = K.kvq_arena_layout(_cfg(k=k, v=v, residual=0))
+        l16 = K.kvq_arena_layout(_cfg(k=k, v=v, residual=0, meta_dtype=K.F16))
+        B, H = 2, 2
+        for side, spec in (("k", k), ("v", v)):
+            cols = getattr(l32, side + "_meta_cols")
+            assert cols == getattr(l16, side + "_meta_cols")
+            rows = (l32.token_capacity // spec[3]) if spec[2] == K.PER_CHANNEL else l32.token_capacity
+            n = B * H * rows * cols
+            def next_start(lay, off):
+                """start of the section after the one at off (sections are in order)"""
+                offs = [getattr(lay, f) for f in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
+                                                  "v_zero", "ring_k", "ring_v", "rope", "fp8_calib")]
+                return min([o for o in offs if off < o < (1 << 63)] + [lay.total_bytes])
+            # the scale section ends where the next one starts (256-byte aligned)
+            s16, s32 = getattr(l16, side + "_scale"), getattr(l32, side + "_scale")
+            assert next_start(l16, s16) - s16 == -(-2 * n // 256) * 256
+            assert next_start(l32, s32) - s32 == -(-4 * n // 256) * 256
+    # FP8 scales stay fp32 [H]; the option changes nothing for FP8 / NONE sides
+    f8 = dict(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0), residual=0)
+    a, b = K.kvq_arena_layout(_cfg(**f8)), K.kvq_arena_layout(_cfg(**f8, meta_dtype=K.F16))
+    assert a.total_bytes == b.total_bytes and a.v_codes == b.v_codes
+
+
+def test_meta_dtype_validation():
+    for bad in (2, -1, 7):
+        with pytest.raises(K.KvqError):
+            K.kvq_arena_bytes(_cfg(meta_dtype=bad))
+    assert K.kvq_abi_version() == 3

@@ -75,3 +75,15 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monk
     (tmp_path / bench.ATTN_SOURCES[0]).write_bytes(b"// changed\n" + open(os.path.join(ROOT, bench.ATTN_SOURCES[0]), "rb").read())
     assert bench.measured_traffic(name) is None
     assert bench.measured_traffic("c3_fp8_e4m3_gqa_8k") is None   # no record at all
+
+
+def test_fp16_metadata_bytes_int2_prerope():
+    # the same split with 2-byte scales / zero-points: codes 536.35 MB + metadata
+    # 268.18 MB + window 4.33 MB + q/out 0.79 MB at 32769 tokens
+    w, fmt = W.WORKLOADS["c5_int2_kivi_prerope_32k"], bench.FORMATS["c5_int2_kivi_prerope_32k"]
+    t32, _ = bench.algorithmic_bytes(w, fmt, 32769)
+    t16, _ = bench.algorithmic_bytes(w, fmt, 32769, meta_bytes=2)
+    pairs = w["B"] * w["Hkv"]
+    meta32 = pairs * (32736 // 32) * 128 * 8 + pairs * 32736 * 4 * 8
+    assert t32 - t16 == meta32 // 2
+    assert abs(t16 / 1e6 - 809.6) < 0.1

@@ -337,3 +337,43 @@ def test_decode_step_equals_append_then_attention(name, fmt, fused):
     assert (n_fused > 0) == fused, (name, n_fused)
     if fused and case.R:
         assert n_fused < n     # the steps that fold run the append separately
+
+
+# fp16 scale / zero-point metadata: every metadata staging path of the MFMA
+# kernel (value groups 1 / 2 / 4 / 8, two PV row halves, pre-RoPE keys, FP8 on
+# one side) and the generic-only formats (symmetric, per-token keys,
+# per-tensor), streamed across folds; (name, Hq for Hkv = 2, format, MFMA expected)
+META16 = [
+    ("int4ch128_int4tok_R128", 8, dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128), True),
+    ("int4ch128_int4tok64_R128", 8, dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 64), R=128), True),
+    ("int2ch32_int2tok32_R32", 8, dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32), True),
+    ("prerope_int2ch32_int2tok32_R32", 8, dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True), True),
+    ("int8ch64_int8tok16_R64", 4, dict(k=(A, 8, CH, 64), v=(A, 8, TOK, 16), R=64), True),
+    ("pv2_int4ch128_int4tok32_R128", 16, dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 32), R=128), True),
+    ("int4ch128_e4m3_R128", 8, dict(k=(A, 4, CH, 128), v=(F8, 8, 0, 0), R=128), True),
+    ("fp8k_int4tok", 8, dict(k=(F8, 8, 0, 0), v=(A, 4, TOK, 0), R=0), True),
+    ("int4ch128_e5m2_R128", 8, dict(k=(A, 4, CH, 128), v=(E5, 8, 0, 0), R=128), None),
+    ("sym8tok_sym8tok", 8, dict(k=(S, 8, TOK, 0), v=(S, 8, TOK, 32), R=0), None),
+    ("int4tok32_int2tok_R64", 8, dict(k=(A, 4, TOK, 32), v=(A, 2, TOK, 64), R=64), None),
+]
+
+
+@pytest.mark.parametrize("name,Hq,fmt,mfma", META16, ids=[m[0] for m in META16])
+def test_fp16_metadata(name, Hq, fmt, mfma):
+    """Codes, fp16 scales / zero-points and dequantized caches bit-exact against
+    the oracle's fp16 rule; attention within tolerance on both kernels."""
+    case = Case(B=2, Hq=Hq, Hkv=2, D=128, dtype="bf16", meta16=True, **fmt)
+    T = 1100
+    gc, st, errs = run_case(case, T, _schedule("stream", T), seed=zlib.crc32(name.encode()) % 1000)
+    if mfma:
+        assert K.KERNEL_MFMA in errs, "the MFMA kernel should cover this shape"
+        for s in (1, 3):   # splits that start inside key groups
+            out = gc.attention(W.random_queries(zlib.crc32(name.encode()) % 1000, case.B, case.Hq, case.D,
+                                                dtype="bf16")[1], kernel=K.KERNEL_MFMA, num_splits=s)
+            assert attention_error(out, W.random_queries(zlib.crc32(name.encode()) % 1000, case.B, case.Hq,
+                                                         case.D, dtype="bf16")[0], st, case) <= ATTN_TOL
+
+
+def test_fp16_metadata_one_shot_per_tensor():
+    case = Case(B=2, Hq=4, Hkv=2, D=128, dtype="f32", meta16=True, k=(A, 4, TEN, 0), v=(S, 8, TEN, 0))
+    run_case(case, 300, [300], seed=5)

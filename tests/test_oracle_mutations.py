@@ -58,7 +58,7 @@ def test_swapped_grouping_axis_is_caught(monkeypatch):
 
 
 def test_symmetric_scale_off_by_one_level_is_caught(monkeypatch):
-    def sym128(x, axis):
+    def sym128(x, axis, meta16=False):
         x = np.asarray(x, dtype=np.float32)
         a = np.abs(x).max(axis=axis, keepdims=True)
         s = (np.maximum(a, Q.EPS) / np.float32(128.0)).astype(np.float32)
@@ -169,3 +169,30 @@ def test_e5m2_wrong_bias_is_caught(monkeypatch):
     orig = Q.e5m2_value_of_code
     monkeypatch.setattr(Q, "e5m2_value_of_code", lambda c: orig(c) * 2.0)   # bias 14
     assert _fails(P.test_e5m2_grid_matches_library_decode)
+
+
+def test_fp16_metadata_rounded_to_nearest_is_caught(monkeypatch):
+    """Storing the fp16 zero-point / scale rounded to nearest (not toward the
+    side that keeps the group covered) must fail the fp16-metadata pins."""
+    from tests import test_meta16_oracle as M16
+    monkeypatch.setattr(Q, "f16_toward", lambda x, up: np.asarray(x, np.float32).astype(np.float16).astype(np.float32))
+    assert _fails(M16.test_directed_fp16_rounding_matches_brute_force)
+    assert _fails(M16.test_asym_fp16_metadata_rule_and_bound, 2)
+
+
+def test_fp16_metadata_codes_against_the_unrounded_range_are_caught(monkeypatch):
+    """Codes taken against the fp32 minimum while the fp16 zero-point is
+    stored must fail the reconstruction bound."""
+    from tests import test_meta16_oracle as M16
+    orig = Q.asym_quantize
+
+    def mixed(x, bits, axis, meta16=False):
+        c, s, z = orig(x, bits, axis, meta16)
+        if meta16:
+            x = np.asarray(x, np.float32)
+            mn = x.min(axis=axis, keepdims=True)
+            t = ((x - mn).astype(np.float32) / s).astype(np.float32)
+            c = np.clip(np.rint(t), 0, 2 ** bits - 1).astype(np.uint8)
+        return c, s, z
+    monkeypatch.setattr(Q, "asym_quantize", mixed)
+    assert _fails(M16.test_asym_fp16_metadata_rule_and_bound, 8)
