@@ -299,6 +299,8 @@ def test_up_to_sixteen_heads_per_kv_head(Hq, fmt):
     ("e4m3_k_e5m2_v", dict(k=(F8, 8, 0, 0), v=(E5, 8, 0, 0), R=0), True),
     ("fp8_e4m3_R32", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=32), False),
     ("int4tok_int4tok_R0", dict(k=(A, 4, TOK, 0), v=(A, 4, TOK, 0), R=0), False),
+    ("int2ch32_int2tok32_R32_prerope_meta16", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True,
+                                                   meta16=True), True),
 ])
 def test_decode_step_equals_append_then_attention(name, fmt, fused):
     """kvq_decode_step (append inside the attention launch when no fold is due)
