@@ -108,6 +108,11 @@ LARGE = {
     "c3_fp8_e5m2_gqa_8k": dict(k=(E5, 8, 0, 0), v=(E5, 8, 0, 0), R=0),
     "c4_int4_llama70b_128k": dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128),
     "c5_int2_kivi_prerope_32k": dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True),
+    # the same caches with fp16 scales / zero-points
+    "c4_int4_llama70b_128k+meta16": dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128, meta16=True,
+                                         workload="c4_int4_llama70b_128k"),
+    "c5_int2_kivi_prerope_32k+meta16": dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True,
+                                            meta16=True, workload="c5_int2_kivi_prerope_32k"),
 }
 
 
@@ -118,9 +123,10 @@ def _samples(w):
 
 @pytest.fixture(scope="module", params=list(LARGE))
 def large(request):
-    name = request.param
+    label = request.param
+    fmt = dict(LARGE[label])
+    name = fmt.pop("workload", label)     # the workload whose inputs are used
     w = W.WORKLOADS[name]
-    fmt = LARGE[name]
     case = Case(B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], D=w["D"], dtype="bf16", **fmt)
     say(f"[{name}] generating inputs")
     Kp = W.full_prefill(name, "k")
