@@ -520,9 +520,15 @@ attn_mfma(Plan p, Args a) {
   const int64_t s_w0 = w_beg & ~(int64_t)31;
   const int64_t nw = hi > w_beg ? (hi - s_w0 + 31) / 32 : 0;   // window steps
   const int64_t nsteps = nq + nw;
+  // Steps of this wavefront: FP8 caches (nothing per key group) take every
+  // kWaves-th step, so that the work-group streams one contiguous run of the
+  // cache; other formats take a contiguous block of steps (key groups span
+  // consecutive steps).
+  constexpr bool IL = !KINT && !VINT;
+  constexpr int64_t STRIDE = IL ? kWaves : 1;
   const int64_t per_wave = (nsteps + kWaves - 1) / kWaves;
-  const int64_t st_beg = wave * per_wave;
-  const int64_t st_end = st_beg + per_wave < nsteps ? st_beg + per_wave : nsteps;
+  const int64_t st_beg = IL ? wave : wave * per_wave;
+  const int64_t st_end = IL ? nsteps : (st_beg + per_wave < nsteps ? st_beg + per_wave : nsteps);
 
   // query columns: column n is head n mod n_rep (hi and lo fp16 halves of the
   // fp32 query in two operands).  Lane (n, g) is A row n of PV: value group
@@ -660,8 +666,8 @@ attn_mfma(Plan p, Args a) {
     }
   };
   auto advance_ptrs = [&](bool group_ends) __attribute__((always_inline)) {
-    pk += SZ_K;
-    pv += SZ_V;
+    pk += SZ_K * STRIDE;
+    pv += SZ_V * STRIDE;
     if constexpr (VINT) {
       pvm0 += 32 * VG * vesz;
       if constexpr (VG == 8) pvm1 += 32 * VG * vesz;
@@ -1001,16 +1007,22 @@ attn_mfma(Plan p, Args a) {
     init_ptrs(i_grp * kG + i_rem, i_grp);
     auto next_issue = [&](int sl_) __attribute__((always_inline)) {
       if (i_grp * kG + i_rem < iss_end) issue(sl_);
-      i_rem += 32;
-      const bool ends = i_rem == kG;
-      if (ends) { i_rem = 0; ++i_grp; }
-      advance_ptrs(ends);
+      if constexpr (IL) {
+        i_grp += STRIDE;           // kG = 32: one step per group, i_rem stays 0
+        advance_ptrs(true);
+      } else {
+        i_rem += 32;
+        const bool ends = i_rem == kG;
+        if (ends) { i_rem = 0; ++i_grp; }
+        advance_ptrs(ends);
+      }
     };
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) next_issue(i);
     int sl = 0;
-    for (int64_t st = qs_beg; st < qs_end; ++st) {
-      if (st + NB - 2 < qs_end) wait_vmem<N_DMA * (NB - 2)>();
+    for (int64_t st = qs_beg; st < qs_end; st += STRIDE) {
+      // stages of steps st, st + STRIDE, ... (those below qs_end) are in flight
+      if (st + (NB - 2) * STRIDE < qs_end) wait_vmem<N_DMA * (NB - 2)>();
       else wait_vmem<0>();
       if constexpr (VINT) {
         if (vm16) widen_meta<VG == 8 ? 128 : 16 * VG, VG == 4 ? 2 : 0>(ring + sl * SLOT + OFF_VM, lane);
@@ -1055,7 +1067,9 @@ attn_mfma(Plan p, Args a) {
       sl = sl == NB - 1 ? 0 : sl + 1;
     }
   }
-  for (int64_t st = (st_beg > nq ? st_beg : nq); st < st_end; ++st) {
+  // window steps: st_beg .. st_end (stride STRIDE) from nq on
+  const int64_t w_first = st_beg >= nq ? st_beg : (IL ? nq + ((st_beg - nq) % STRIDE + STRIDE) % STRIDE : nq);
+  for (int64_t st = w_first; st < st_end; st += STRIDE) {
     StepData<16, 32, 1> d;
     const int64_t t0 = s_w0 + (st - nq) * 32;
     load_r(t0, d);
