@@ -379,3 +379,22 @@ def test_fp16_metadata(name, Hq, fmt, mfma):
 def test_fp16_metadata_one_shot_per_tensor():
     case = Case(B=2, Hq=4, Hkv=2, D=128, dtype="f32", meta16=True, k=(A, 4, TEN, 0), v=(S, 8, TEN, 0))
     run_case(case, 300, [300], seed=5)
+
+
+@pytest.mark.parametrize("name,fmt", [
+    ("e4m3_R0", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0)),
+    ("e4m3_R32", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=32)),
+    ("e5m2_R0", dict(k=(E5, 8, 0, 0), v=(E5, 8, 0, 0), R=0)),
+])
+@pytest.mark.parametrize("T", [40, 161, 1100])
+def test_fp8_step_interleave_over_split_counts(name, fmt, T):
+    """FP8 caches hand the 32-token steps of a split to the four wavefronts in
+    turn: splits with fewer steps than wavefronts, window steps starting at any
+    offset, and one to many splits all stay within tolerance of the oracle."""
+    case = Case(B=2, Hq=8, Hkv=2, D=128, dtype="bf16", **fmt)
+    seed = zlib.crc32(f"{name}{T}".encode()) % 1000
+    gc, st, errs = run_case(case, T, _schedule("stream", T), seed=seed)
+    qf, qp = W.random_queries(seed, case.B, case.Hq, case.D, dtype="bf16")
+    for s in (1, 2, 3, 5, 16, 64):
+        out = gc.attention(qp, kernel=K.KERNEL_MFMA, num_splits=s)
+        assert attention_error(out, qf, st, case) <= ATTN_TOL, (name, T, s)
