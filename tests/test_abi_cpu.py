@@ -268,3 +268,34 @@ def test_meta_dtype_validation():
         with pytest.raises(K.KvqError):
             K.kvq_arena_bytes(_cfg(meta_dtype=bad))
     assert K.kvq_abi_version() == 3
+
+
+def test_plain_c_caller(tmp_path):
+    """include/kvq.h compiles as C11 and a C program links the library and
+    calls its host-only entry points; its results match the Python binding."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("gcc or the HIP headers are not available")
+    pkg = os.path.dirname(_lib.__file__)
+    exe = str(tmp_path / "host_queries")
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c_abi", "host_queries.c"), "-L", pkg, "-lkvq",
+           f"-Wl,-rpath,{pkg}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    head, msg = r.stdout.split(" msg=", 1)
+    got = dict(kv.split("=", 1) for kv in head.split())
+    cfg = K.make_config(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, max_tokens=32832,
+                        k=(K.INT_ASYM, 2, K.PER_CHANNEL, 32), v=(K.INT_ASYM, 2, K.PER_TOKEN, 32),
+                        residual=32, pre_rope_k=True)
+    assert int(got["abi"]) == K.kvq_abi_version()
+    assert int(got["arena"]) == K.kvq_arena_bytes(cfg)
+    cfg.meta_dtype = K.F16
+    assert int(got["arena16"]) == K.kvq_arena_bytes(cfg)
+    assert int(got["tq"]) == 32736
+    assert int(got["bad"]) == -1 and msg.strip() == K.kvq_status_string(-1)
