@@ -421,12 +421,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
             "kernel": "decode attention launch: pass 1 (split-K) + merge; mean of back-to-back launches between two HIP events on the launch stream",
-            "limiter": LIMITER[base] if name == base else "not recorded for this size",
+            "limiter": LIMITER[base] if name in (base, base + "+meta16") else "not recorded for this size",
         },
     }
     if warm_us is not None:
         res["attention_us_one_arena_warm"] = round(warm_us, 3)
-    traffic = measured_traffic(name) if name == base else None
+    traffic = measured_traffic(name) if name in (base, base + "+meta16") else None
     if traffic is not None:
         res["roofline"]["traffic"] = traffic["bytes_per_launch"]
         res["roofline"]["traffic_source"] = traffic["source"]
