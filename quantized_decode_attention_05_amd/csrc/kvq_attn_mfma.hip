@@ -446,14 +446,23 @@ attn_mfma(Plan p, Args a) {
   constexpr int SZ_VM = VINT ? 2 * 32 * VG * 4 : 0, SZ_KM = KINT ? 2 * D * 4 : 0, SZ_KT = ROPE ? 64 * 8 : 0;
   constexpr int OFF_V = SZ_K, OFF_VM = OFF_V + SZ_V, OFF_KM = OFF_VM + SZ_VM, OFF_KT = OFF_KM + SZ_KM;
   constexpr int SLOT = OFF_KT + SZ_KT;
-  constexpr int NB = KVQ_MFMA_STAGES > 0 ? KVQ_MFMA_STAGES : (SLOT <= 6144 ? 3 : 2);
+  // query rows: up to 16 heads per kv head with one value group (the PV rows
+  // are then the heads), 8 otherwise
+  constexpr int QROWS = VG == 1 ? 16 : 8;
+  // Stages per wavefront: 3 (2 for slots over 6 KB), but no more than keep
+  // two work-groups on a CU (80 KB of LDS each, with the query rows, the RoPE
+  // table and the reduction scratch), at least 2, and enough to hold the
+  // wavefront's O rows after the loop.
+  constexpr int LDS_FIXED = QROWS * D * 4 + (ROPE ? 64 * 32 * 8 : 8) + kWaves * QROWS * 2 * 4;
+  constexpr int NB_FIT = (80 * 1024 - 512 - LDS_FIXED) / (kWaves * SLOT);
+  constexpr int NB_DEF = SLOT <= 6144 ? 3 : 2;
+  constexpr int NB_LDS = NB_FIT < NB_DEF ? (NB_FIT > 2 ? NB_FIT : 2) : NB_DEF;
+  constexpr int NB_O = (QROWS * D * 4 + SLOT - 1) / SLOT;
+  constexpr int NB = KVQ_MFMA_STAGES > 0 ? KVQ_MFMA_STAGES : (NB_LDS > NB_O ? NB_LDS : NB_O);
   constexpr int N_DMA = SZ_K / 1024 + SZ_V / 1024 + (SZ_VM + 1023) / 1024 + (KINT ? 1 : 0) + (ROPE ? 1 : 0);
   static_assert(SZ_K % 1024 == 0 && SZ_V % 1024 == 0 && NB * SLOT >= (VG == 1 ? 16 : 8) * D * 4,
                 "stage layout (a wavefront's ring holds its O rows after the loop)");
 
-  // query rows: up to 16 heads per kv head with one value group (the PV rows
-  // are then the heads), 8 otherwise
-  constexpr int QROWS = VG == 1 ? 16 : 8;
   __shared__ float q_s[QROWS][D];
   // fine RoPE table, pair-major with the token offset XOR-swizzled by the
   // lane row so that one row's 16 lanes (16 offsets, one pair) hit distinct banks
