@@ -73,9 +73,10 @@ enum kvq_scheme {
   KVQ_FP8_E4M3 = 3,  /* OCP E4M3FN bytes with one fp32 scale per kv head           */
   KVQ_FP8_E5M2 = 4   /* OCP E5M2 bytes, no scales (stored scale fixed at 1.0);      */
                      /* saturates at +-57344 ("FP8 KV Cache Quantization: Why Keys */
-                     /* Break Before Values", sections "Why do per-tensor scales  */
-                     /* waste bits on the K cache?" and "How do I turn it on in   */
-                     /* vLLM without wrecking long context?")                     */
+                     /* Break Before Values", section "Why do per-tensor scales   */
+                     /* waste bits on the K cache?"; that it needs no scales:     */
+                     /* section "How do you configure asymmetric KV cache         */
+                     /* quantization?")                                           */
 };
 enum kvq_axis {      /* grouping axis of INT schemes (ignored for NONE / FP8)      */
   KVQ_PER_TENSOR  = 0, /* one (scale, zero) per (sequence, kv head)                */

@@ -72,13 +72,36 @@ def decode_attention(q: np.ndarray, K_hat: np.ndarray, V_hat: np.ndarray, sm_sca
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:
+    """||a - ref||_2 / ||ref||_2 in fp64 (the relative output error of "FP8 KV
+    Cache Quantization: Why Keys Break Before Values", section "Why does the K
+    cache break before the V cache?").  inf when either side holds a non-finite
+    value, or when ref is zero and a is not; 0 when both are zero."""
     a = np.asarray(a, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
+    if not (np.isfinite(a).all() and np.isfinite(ref).all()):
+        return float("inf")
+    num = float(np.linalg.norm(a - ref))
+    den = float(np.linalg.norm(ref))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den
 
 
 def max_rel_l2_per_head(out: np.ndarray, ref: np.ndarray, heads=None) -> float:
-    """max over (b, hq) of ||out - ref|| / ||ref|| (per-head relative L2)."""
-    B, Hq, _ = ref.shape
+    """Largest per-(sequence, query head) relative L2 error of out [B, Hq, D]
+    against ref, over every pair (heads=None) or the listed (b, hq) pairs.
+
+    A pair whose output or reference holds a NaN or an infinity counts as an
+    infinite error, so an output a kernel never wrote (left NaN) fails any
+    tolerance wherever it sits.  The loop keeps the running maximum explicitly
+    (Python's max() would skip a NaN that is not the first element)."""
+    B, Hq = ref.shape[0], ref.shape[1]
     todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
-    return max(rel_l2(out[b, h], ref[b, h]) for b, h in todo)
+    if not todo:
+        raise ValueError("no (sequence, head) pairs to compare")
+    worst = 0.0
+    for b, h in todo:
+        e = rel_l2(out[b, h], ref[b, h])
+        if not (e <= worst):        # also true for e = nan or inf
+            worst = e if e == e else float("inf")
+    return worst

@@ -232,19 +232,6 @@ def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
     return acc.astype(np.uint8)
 
 
-def unpack_rows(rows: np.ndarray, bits: int, D: int, signed=False, fp=False) -> np.ndarray:
-    if bits == 16:
-        return np.ascontiguousarray(rows).view(np.float16).reshape(*rows.shape[:-1], D)
-    if bits == 32:
-        return np.ascontiguousarray(rows).view(np.float32).reshape(*rows.shape[:-1], D)
-    if bits == 8:
-        return rows.view(np.int8) if signed else rows.copy()
-    per = 8 // bits
-    mask = (1 << bits) - 1
-    out = np.stack([(rows >> (bits * r)) & mask for r in range(per)], axis=-1)
-    return out.reshape(*rows.shape[:-1], D).astype(np.uint8)
-
-
 def pack_vblocks(codes: np.ndarray, bits: int) -> np.ndarray:
     """V layout: 32-token blocks.  Token t = 32*blk + 8*g + k, channel c = 16*i + n.
     Inside a block, lane l = 16*g + n owns a contiguous run of D/16 words; word i

@@ -21,8 +21,8 @@ ties to even):
   cache?": 3 mantissa bits, saturation at +-448): encoded here by an explicit
   nearest-point search over the 254 finite code points, ties to the even code.
 * FP8 E5M2 (same section: 2 mantissa bits, saturation at +-57344; the section
-  "How do I turn it on in vLLM without wrecking long context?" adds that it
-  needs no scales): OCP E5M2, bias 15, the same nearest-point search over its
+  "How do you configure asymmetric KV cache quantization?" adds that it needs
+  no scales): OCP E5M2, bias 15, the same nearest-point search over its
   246 finite code points, applied to the value itself (unit scale).
 """
 from __future__ import annotations

@@ -111,6 +111,69 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+_TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+
+
+def _need(t, name, *, dtype=None, shape=None, min_bytes=None):
+    """Check a tensor argument before its pointer crosses the ABI: the C entry
+    points take raw pointers and (for the arena) no size, so a wrong shape,
+    dtype, layout or a too-small buffer here would become an out-of-bounds
+    device access.  Checks run in this order (contiguity, dtype, shape, byte
+    size) and raise ValueError naming the argument; each wrapper checks that
+    its tensors live on the GPU (_on_gpu) after every argument passed these."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs at least {min_bytes}")
+    return t
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _in_dtype(cfg):
+    dt = _TORCH_DTYPE.get(cfg.in_dtype)
+    if dt is None:
+        raise ValueError(f"unknown in_dtype {cfg.in_dtype}")
+    return dt
+
+
+def _out_dtype(cfg):
+    dt = _TORCH_DTYPE.get(cfg.out_dtype)
+    if dt is None:
+        raise ValueError(f"unknown out_dtype {cfg.out_dtype}")
+    return dt
+
+
+def _check_arena(cfg, arena):
+    return _need(arena, "arena", min_bytes=kvq_arena_bytes(cfg))
+
+
+def _check_new_tokens(cfg, k_new, v_new):
+    _need(k_new, "k_new", dtype=_in_dtype(cfg))
+    if k_new.dim() != 4 or tuple(k_new.shape[:2]) != (cfg.batch, cfg.num_kv_heads) or \
+            k_new.shape[3] != cfg.head_dim:
+        raise ValueError(f"k_new has shape {tuple(k_new.shape)}, expected "
+                         f"({cfg.batch}, {cfg.num_kv_heads}, n_new, {cfg.head_dim})")
+    _need(v_new, "v_new", dtype=_in_dtype(cfg), shape=k_new.shape)
+
+
+def _check_query_out(cfg, q, out):
+    _need(q, "q", dtype=_in_dtype(cfg), shape=(cfg.batch, cfg.num_q_heads, cfg.head_dim))
+    _need(out, "out", dtype=_out_dtype(cfg), shape=(cfg.batch, cfg.num_q_heads, cfg.head_dim))
+
+
 def _stream(stream, *tensors):
     if stream is not None:
         return C.c_void_p(stream)
@@ -167,7 +230,14 @@ def kvq_workspace_bytes(cfg: Config, T: int, kernel: int = 0, num_splits: int = 
 
 def kvq_quantize_append(cfg: Config, arena, t0: int, k_new, v_new, k_scale=None, v_scale=None,
                         flags: int = 0, stream=None) -> None:
-    """k_new, v_new: device tensors [B, Hkv, n_new, D] in cfg.in_dtype."""
+    """k_new, v_new: device tensors [B, Hkv, n_new, D] in cfg.in_dtype;
+    k_scale, v_scale: fp32 [Hkv] (FP8 E4M3 sides only) or None."""
+    _check_arena(cfg, arena)
+    _check_new_tokens(cfg, k_new, v_new)
+    for nm, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if sc is not None:
+            _need(sc, nm, dtype=torch.float32, shape=(cfg.num_kv_heads,))
+    _on_gpu(arena=arena, k_new=k_new, v_new=v_new, k_scale=k_scale, v_scale=v_scale)
     n_new = int(k_new.shape[2])
     st = _lib.kvq_quantize_append(C.byref(cfg), _ptr(arena), t0, n_new, _ptr(k_new), _ptr(v_new),
                                   _ptr(k_scale), _ptr(v_scale), flags,
@@ -179,6 +249,11 @@ def kvq_decode_attention(cfg: Config, arena, T: int, q, out, sm_scale: float, wo
                          kernel: int = 0, num_splits: int = 0, stream=None) -> None:
     """q: [B, Hq, D] in cfg.in_dtype; out: [B, Hq, D] in cfg.out_dtype."""
     o = _opts(kernel, num_splits)
+    _check_arena(cfg, arena)
+    _check_query_out(cfg, q, out)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_gpu(arena=arena, q=q, out=out, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.kvq_decode_attention(C.byref(cfg), _ptr(arena), T, _ptr(q), _ptr(out), sm_scale,
                                    _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
@@ -190,6 +265,14 @@ def kvq_decode_step(cfg: Config, arena, t0: int, k_new, v_new, q, out, sm_scale:
     """Append one token per sequence at t0 (k_new, v_new: [B, Hkv, 1, D]) and
     attend over t0 + 1 tokens (q: [B, Hq, D]; out: [B, Hq, D])."""
     o = _opts(kernel, num_splits)
+    _check_arena(cfg, arena)
+    _check_new_tokens(cfg, k_new, v_new)
+    if k_new.shape[2] != 1:
+        raise ValueError(f"k_new has {k_new.shape[2]} tokens per sequence, a decode step appends 1")
+    _check_query_out(cfg, q, out)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_gpu(arena=arena, k_new=k_new, v_new=v_new, q=q, out=out, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.kvq_decode_step(C.byref(cfg), _ptr(arena), t0, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
                               sm_scale, _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
@@ -206,6 +289,11 @@ def kvq_decode_step_fused(cfg: Config, t0: int, kernel: int = 0, num_splits: int
 
 def kvq_dequantize(cfg: Config, arena, T: int, k_out=None, v_out=None, stream=None) -> None:
     """k_out, v_out: fp32 device tensors [B, Hkv, T, D] (either may be None)."""
+    _check_arena(cfg, arena)
+    for nm, t in (("k_out", k_out), ("v_out", v_out)):
+        if t is not None:
+            _need(t, nm, dtype=torch.float32, shape=(cfg.batch, cfg.num_kv_heads, T, cfg.head_dim))
+    _on_gpu(arena=arena, k_out=k_out, v_out=v_out)
     st = _lib.kvq_dequantize(C.byref(cfg), _ptr(arena), T, _ptr(k_out), _ptr(v_out),
                              _stream(stream, arena))
     _check(st, "kvq_dequantize")

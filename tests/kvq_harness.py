@@ -92,7 +92,10 @@ class GpuCache:
         sm = 1.0 / math.sqrt(c.D) if sm_scale is None else sm_scale
         K.kvq_decode_attention(self.cfg, self.arena, T, q, out, sm, ws, kernel, num_splits)
         torch.cuda.synchronize()
-        return out.cpu().numpy()
+        o = out.cpu().numpy()
+        assert np.isfinite(o).all(), f"attention output not finite (unwritten heads?) kernel={kernel} " \
+                                     f"splits={num_splits} T={T}"
+        return o
 
     def dequantize(self, T=None, bh_sel=None):
         T = self.T if T is None else T

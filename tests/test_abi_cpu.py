@@ -299,3 +299,70 @@ def test_plain_c_caller(tmp_path):
     assert int(got["arena16"]) == K.kvq_arena_bytes(cfg)
     assert int(got["tq"]) == 32736
     assert int(got["bad"]) == -1 and msg.strip() == K.kvq_status_string(-1)
+
+
+# ---------------------------------------------------------------------------
+# the Python binding's argument checks (CPU tensors: each rejection fires
+# before the device check, and a fully correct CPU tensor is refused last)
+# ---------------------------------------------------------------------------
+
+def _tensors(cfg, T=16, n_new=4):
+    import torch
+    dt = {K.F32: torch.float32, K.F16: torch.float16, K.BF16: torch.bfloat16}[cfg.in_dtype]
+    B, Hq, Hkv, D = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    return dict(arena=torch.zeros(K.kvq_arena_bytes(cfg), dtype=torch.uint8),
+                k=torch.zeros(B, Hkv, n_new, D, dtype=dt), v=torch.zeros(B, Hkv, n_new, D, dtype=dt),
+                q=torch.zeros(B, Hq, D, dtype=dt), out=torch.zeros(B, Hq, D, dtype=torch.float32),
+                ws=torch.zeros(K.kvq_workspace_bytes(cfg, T), dtype=torch.uint8),
+                ko=torch.zeros(B, Hkv, T, D, dtype=torch.float32))
+
+
+def _rejects(fn, *args, match, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*args, **kw)
+
+
+def test_binding_rejects_bad_append_arguments():
+    import torch
+    cfg = _cfg(in_dtype=K.BF16)
+    t = _tensors(cfg)
+    ap = K.kvq_quantize_append
+    _rejects(ap, cfg, t["arena"][:-1], 0, t["k"], t["v"], match="arena holds")
+    _rejects(ap, cfg, t["arena"], 0, t["k"].float(), t["v"], match="k_new has dtype")
+    _rejects(ap, cfg, t["arena"], 0, t["k"][:, :1].contiguous(), t["v"][:, :1].contiguous(), match="k_new has shape")
+    _rejects(ap, cfg, t["arena"], 0, t["k"].transpose(2, 3).contiguous().transpose(2, 3), t["v"],
+             match="k_new must be contiguous")
+    _rejects(ap, cfg, t["arena"], 0, t["k"], t["v"][:, :, :2].contiguous(), match="v_new has shape")
+    _rejects(ap, cfg, t["arena"], 0, t["k"], t["v"], torch.ones(3), match="k_scale has shape")
+    _rejects(ap, cfg, t["arena"], 0, t["k"], t["v"], match="arena must be a GPU tensor")
+    _rejects(ap, cfg, t["arena"], 0, t["k"], None, match="v_new is required")
+
+
+def test_binding_rejects_bad_attention_arguments():
+    cfg = _cfg(in_dtype=K.BF16)
+    t = _tensors(cfg)
+    at = K.kvq_decode_attention
+    sm = 0.088
+    _rejects(at, cfg, t["arena"], 16, t["q"].float(), t["out"], sm, t["ws"], match="q has dtype")
+    _rejects(at, cfg, t["arena"], 16, t["q"][:1], t["out"], sm, t["ws"], match="q has shape")
+    _rejects(at, cfg, t["arena"], 16, t["q"], t["out"].half(), sm, t["ws"], match="out has dtype")
+    _rejects(at, cfg, t["arena"], 16, t["q"], t["out"][:, :4].contiguous(), sm, t["ws"], match="out has shape")
+    _rejects(at, cfg, t["arena"][:100], 16, t["q"], t["out"], sm, t["ws"], match="arena holds")
+    _rejects(at, cfg, t["arena"], 16, t["q"], t["out"], sm, t["ws"], match="arena must be a GPU tensor")
+    st = K.kvq_decode_step
+    k1, v1 = t["k"][:, :, :1].contiguous(), t["v"][:, :, :1].contiguous()
+    _rejects(st, cfg, t["arena"], 16, t["k"], t["v"], t["q"], t["out"], sm, t["ws"],
+             match="a decode step appends 1")
+    _rejects(st, cfg, t["arena"], 16, k1, v1, t["q"].T.contiguous().T, t["out"], sm, t["ws"],
+             match="q must be contiguous")
+    _rejects(st, cfg, t["arena"], 16, k1, v1, t["q"], t["out"], sm, t["ws"], match="arena must be a GPU tensor")
+
+
+def test_binding_rejects_bad_dequantize_arguments():
+    cfg = _cfg(in_dtype=K.BF16)
+    t = _tensors(cfg, T=16)
+    dq = K.kvq_dequantize
+    _rejects(dq, cfg, t["arena"], 16, t["ko"][:, :, :8].contiguous(), match="k_out has shape")
+    _rejects(dq, cfg, t["arena"], 16, t["ko"].double(), match="k_out has dtype")
+    _rejects(dq, cfg, t["arena"], 16, None, t["ko"].half(), match="v_out has dtype")
+    _rejects(dq, cfg, t["arena"], 16, t["ko"], match="arena must be a GPU tensor")

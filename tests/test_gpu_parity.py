@@ -302,11 +302,15 @@ def test_up_to_sixteen_heads_per_kv_head(Hq, fmt):
     ("int2ch32_int2tok32_R32_prerope_meta16", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True,
                                                    meta16=True), True),
 ])
-def test_decode_step_equals_append_then_attention(name, fmt, fused):
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+def test_decode_step_equals_append_then_attention(name, fmt, fused, splits):
     """kvq_decode_step (append inside the attention launch when no fold is due)
     leaves the same cache bytes and gives the same output, bit for bit, as
     kvq_quantize_append followed by kvq_decode_attention, over 40 steps that
-    cross fold boundaries."""
+    cross fold boundaries.  With 3 and 7 splits (chunks of 192 and 64 tokens)
+    the new token lands in different splits and the window straddles the
+    chunk boundary at 384, so only the work-group owning the new position may
+    write it."""
     import math
     import torch
     from tests.kvq_harness import to_dev
@@ -318,8 +322,8 @@ def test_decode_step_equals_append_then_attention(name, fmt, fused):
     ga.append(Kp[:, :, :T0], Vp[:, :, :T0], flags)
     gb.append(Kp[:, :, :T0], Vp[:, :, :T0], flags)
     sm = 1.0 / math.sqrt(case.D)
-    wa = torch.zeros(K.kvq_workspace_bytes(ga.cfg, T0 + n), dtype=torch.uint8, device="cuda")
-    wb = torch.zeros(K.kvq_workspace_bytes(gb.cfg, T0 + n), dtype=torch.uint8, device="cuda")
+    wa = torch.zeros(K.kvq_workspace_bytes(ga.cfg, T0 + n, 0, splits), dtype=torch.uint8, device="cuda")
+    wb = torch.zeros(K.kvq_workspace_bytes(gb.cfg, T0 + n, 0, splits), dtype=torch.uint8, device="cuda")
     oa = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
     ob = torch.empty_like(oa)
     n_fused = 0
@@ -327,12 +331,12 @@ def test_decode_step_equals_append_then_attention(name, fmt, fused):
         t = T0 + i
         kn, vn = to_dev(Kp[:, :, t:t + 1], case.dtype), to_dev(Vp[:, :, t:t + 1], case.dtype)
         q = to_dev(W.random_queries(1000 + i, case.B, case.Hq, case.D, dtype="bf16")[1], case.dtype)
-        n_fused += K.kvq_decode_step_fused(ga.cfg, t)
+        n_fused += K.kvq_decode_step_fused(ga.cfg, t, 0, splits)
         oa.fill_(float("nan"))
         ob.fill_(float("nan"))
-        K.kvq_decode_step(ga.cfg, ga.arena, t, kn, vn, q, oa, sm, wa)
+        K.kvq_decode_step(ga.cfg, ga.arena, t, kn, vn, q, oa, sm, wa, 0, splits)
         K.kvq_quantize_append(gb.cfg, gb.arena, t, kn, vn)
-        K.kvq_decode_attention(gb.cfg, gb.arena, t + 1, q, ob, sm, wb)
+        K.kvq_decode_attention(gb.cfg, gb.arena, t + 1, q, ob, sm, wb, 0, splits)
         torch.cuda.synchronize()
         assert torch.equal(ga.arena, gb.arena), (name, t, "cache bytes differ")
         assert torch.isfinite(oa).all() and torch.equal(oa, ob), (name, t, "outputs differ")

@@ -196,3 +196,80 @@ def test_fp16_metadata_codes_against_the_unrounded_range_are_caught(monkeypatch)
         return c, s, z
     monkeypatch.setattr(Q, "asym_quantize", mixed)
     assert _fails(M16.test_asym_fp16_metadata_rule_and_bound, 8)
+
+
+# ---------------------------------------------------------------------------
+# the parity checker itself: every GPU attention assertion goes through it
+# ---------------------------------------------------------------------------
+
+def _checker(reduce_fn):
+    def mutated(out, ref, heads=None):
+        B, Hq = ref.shape[0], ref.shape[1]
+        todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+        return reduce_fn([A.rel_l2(out[b, h], ref[b, h]) for b, h in todo])
+    return mutated
+
+
+def _checker_nan_skipping(out, ref, heads=None):
+    """The old form: Python's max() over the heads, whose comparisons skip a
+    NaN that is not the first element, and rel_l2 without a finiteness check."""
+    B, Hq = ref.shape[0], ref.shape[1]
+    todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+    return max(float(np.linalg.norm(out[b, h] - ref[b, h]) / np.linalg.norm(ref[b, h])) for b, h in todo)
+
+
+def _checker_ignores_heads(out, ref, heads=None):
+    return max(A.rel_l2(out[b, h], ref[b, h]) for b in range(ref.shape[0]) for h in range(ref.shape[1]))
+
+
+@pytest.mark.parametrize("bug", ["min", "mean", "median", "first"])
+def test_checker_wrong_reduction_is_caught(monkeypatch, bug):
+    fn = {"min": min, "mean": lambda v: float(np.mean(v)), "median": lambda v: float(np.median(v)),
+          "first": lambda v: v[0]}[bug]
+    monkeypatch.setattr(A, "max_rel_l2_per_head", _checker(fn))
+    assert _fails(P.test_max_rel_l2_per_head_hand_values)
+
+
+def test_checker_skipping_nan_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "max_rel_l2_per_head", _checker_nan_skipping)
+    assert _fails(P.test_max_rel_l2_per_head_non_finite_is_infinite, 0, 1)
+
+
+def test_checker_ignoring_the_head_list_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "max_rel_l2_per_head", _checker_ignores_heads)
+    assert _fails(P.test_max_rel_l2_per_head_hand_values)
+
+
+def test_dequantize_part_bugs_are_caught(monkeypatch):
+    """A zero-point dropped from the stored-code rebuild, or per-channel scales
+    taken from the wrong group row, fail the hand-value pin."""
+    orig = C.dequantize_part
+
+    def no_zero(part, spec):
+        if spec.scheme == C.INT_ASYM:
+            part = dict(part, zero=np.zeros_like(part["zero"]))
+        return orig(part, spec)
+
+    monkeypatch.setattr(C, "dequantize_part", no_zero)
+    assert _fails(P.test_dequantize_part_hand_values)
+
+    def first_group_only(part, spec):
+        if spec.scheme == C.INT_ASYM and spec.axis == C.PER_CHANNEL:
+            s, z = part["scale"].copy(), part["zero"].copy()
+            s[:, :, 1:] = s[:, :, :1]
+            z[:, :, 1:] = z[:, :, :1]
+            part = dict(part, scale=s, zero=z)
+        return orig(part, spec)
+
+    monkeypatch.setattr(C, "dequantize_part", first_group_only)
+    assert _fails(P.test_dequantize_part_hand_values)
+
+
+def test_window_slot_bugs_are_caught(monkeypatch):
+    orig = C.ring_slots
+    monkeypatch.setattr(C, "ring_slots", lambda cfg: max(orig(cfg) - 32, 0))
+    assert _fails(P.test_window_slots_hand_values_and_no_collisions)
+    monkeypatch.setattr(C, "ring_slots", orig)
+    monkeypatch.setattr(C, "window_slots", lambda cfg, Tq, T: (np.arange(Tq, T) % max(orig(cfg), 1)) if
+                        orig(cfg) == 0 else (np.arange(Tq, T) - Tq) % orig(cfg))
+    assert _fails(P.test_window_slots_hand_values_and_no_collisions)

@@ -446,10 +446,127 @@ def test_window_holds_fp16_values():
     assert st["k"]["zero"][0, 0, 0, 0] == mn
 
 
+# ---------------------------------------------------------------------------
+# dequantization from stored codes, window slots, and the parity checker
+# ---------------------------------------------------------------------------
+
+def test_dequantize_part_hand_values():
+    """Codes, scales and zero-points written by hand, with dequantized values
+    worked out by hand (x_hat = code * scale + zero; code * scale; E4M3 value *
+    scale; the stored fp16 value).  Every scale is a power of two and every
+    zero-point a small dyadic number, so each x_hat below is exact.  Each group
+    gets its own scale so a mix-up of which group a scale belongs to fails."""
+    # INT2 per-channel, group of 2 tokens, D = 2: scale/zero per (group, channel)
+    part = dict(codes=np.array([[0, 3], [1, 2], [2, 1], [3, 0]], np.uint8)[None, None],
+                scale=np.array([[0.5, 0.25], [2.0, 4.0]], np.float32)[None, None],
+                zero=np.array([[-1.0, 1.0], [0.5, -8.0]], np.float32)[None, None])
+    spec = C.Spec(C.INT_ASYM, 2, C.PER_CHANNEL, 2)
+    want = np.array([[-1.0, 1.75], [-0.5, 1.5], [4.5, -4.0], [6.5, -8.0]], np.float32)
+    assert np.array_equal(C.dequantize_part(part, spec)[0, 0], want)
+    # INT4 per-token, groups of 2 channels, D = 4: scale/zero per (token, group)
+    part = dict(codes=np.array([[15, 0, 1, 2], [3, 4, 5, 6]], np.uint8)[None, None],
+                scale=np.array([[0.125, 1.0], [2.0, 0.5]], np.float32)[None, None],
+                zero=np.array([[0.0, -2.0], [1.0, 0.25]], np.float32)[None, None])
+    spec = C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 2)
+    want = np.array([[1.875, 0.0, -1.0, 0.0], [7.0, 9.0, 2.75, 3.25]], np.float32)
+    assert np.array_equal(C.dequantize_part(part, spec)[0, 0], want)
+    # symmetric INT8, per tensor: one scale per (sequence, head)
+    part = dict(codes=np.array([[-127, 5], [0, 127]], np.int8)[None, None],
+                scale=np.array([0.5], np.float32).reshape(1, 1, 1, 1), zero=None)
+    want = np.array([[-63.5, 2.5], [0.0, 63.5]], np.float32)
+    assert np.array_equal(C.dequantize_part(part, C.Spec(C.INT_SYM, 8, C.PER_TENSOR, 0))[0, 0], want)
+    # FP8 E4M3 with per-kv-head scales: 0x38 = 1.0, 0xC0 = -2.0, 0x7E = 448, 0x01 = 2^-9
+    codes = np.array([[0x38, 0xC0], [0x7E, 0x01]], np.uint8)
+    part = dict(codes=np.stack([codes, codes])[None], scale=np.array([0.25, 2.0], np.float32), zero=None)
+    got = C.dequantize_part(part, C.Spec(C.FP8_E4M3, 8, 0, 0))[0]
+    assert np.array_equal(got[0], np.array([[0.25, -0.5], [112.0, 2.0 ** -11]], np.float32))
+    assert np.array_equal(got[1], np.array([[2.0, -4.0], [896.0, 2.0 ** -8]], np.float32))
+    # E5M2 (no scale): 0x3C = 1.0, 0x7B = 57344, 0x80 = -0.0
+    part = dict(codes=np.array([[0x3C, 0x7B, 0x80]], np.uint8)[None, None], scale=np.ones(1, np.float32), zero=None)
+    got = C.dequantize_part(part, C.Spec(C.FP8_E5M2, 8, 0, 0))[0, 0]
+    assert got.tolist() == [[1.0, 57344.0, -0.0]] and np.signbit(got[0, 2])
+    # unquantized fp16 storage
+    part = dict(codes=np.array([[1.5, -0.25]], np.float16)[None, None], scale=None, zero=None)
+    assert C.dequantize_part(part, C.Spec(C.NONE, 16, 0, 0))[0, 0].tolist() == [[1.5, -0.25]]
+
+
 @pytest.mark.parametrize("spec", [C.Spec(C.INT_ASYM, 2, C.PER_CHANNEL, 32), C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 32),
                                   C.Spec(C.INT_SYM, 8, C.PER_TENSOR, 0), C.Spec(C.INT_SYM, 8, C.PER_CHANNEL, 0),
                                   C.Spec(C.FP8_E4M3, 8, 0, 0), C.Spec(C.NONE, 16, 0, 0)])
-def test_dequantize_part_rebuilds_values(spec):
+def test_dequantize_part_agrees_with_quantize_part(spec):
+    """Consistency only (both use the same element rule): the hand-value test
+    above is the pin."""
     (K, _), _ = W.random_case(8, 2, 2, 64, 32)
     part = C.quantize_part(K, spec, np.array([0.5, 2.0], np.float32))
     assert np.array_equal(C.dequantize_part(part, spec), part["deq"])
+
+
+def test_window_slots_hand_values_and_no_collisions():
+    """Ring slots (cache layout: window token t sits in slot t mod Rs, Rs =
+    R + G rounded up to 32): hand values, and no two tokens of any reachable
+    window share a slot."""
+    cfg = C.Cfg(1, 1, 1, 32, C.Spec(C.INT_ASYM, 2, C.PER_CHANNEL, 32), C.Spec(C.INT_ASYM, 2, C.PER_TOKEN, 32), R=32)
+    assert C.ring_slots(cfg) == 64
+    assert C.window_slots(cfg, 64, 100).tolist() == list(range(0, 36))
+    assert C.window_slots(cfg, 96, 159).tolist() == list(range(32, 64)) + list(range(0, 31))
+    cfg = C.Cfg(1, 1, 1, 32, C.Spec(C.INT_ASYM, 4, C.PER_CHANNEL, 128), C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 0), R=128)
+    assert C.ring_slots(cfg) == 256
+    assert C.window_slots(cfg, 256, 260).tolist() == [0, 1, 2, 3]
+    cfg = C.Cfg(1, 1, 1, 32, C.Spec(C.FP8_E4M3, 8, 0, 0), C.Spec(C.FP8_E4M3, 8, 0, 0), R=5)
+    assert C.ring_slots(cfg) == 32            # R + 1 = 6 -> 32
+    assert C.window_slots(cfg, 95, 100).tolist() == [31, 0, 1, 2, 3]
+    cfg = C.Cfg(1, 1, 1, 32, C.Spec(C.FP8_E4M3, 8, 0, 0), C.Spec(C.FP8_E4M3, 8, 0, 0), R=0)
+    assert C.ring_slots(cfg) == 0 and C.window_slots(cfg, 7, 7).size == 0
+    for R, G in ((0, 32), (32, 32), (64, 16), (128, 128), (96, 32)):
+        cfg = C.Cfg(1, 1, 1, 32, C.Spec(C.INT_ASYM, 4, C.PER_CHANNEL, G), C.Spec(C.INT_ASYM, 4, C.PER_TOKEN, 0), R=R)
+        for T in range(0, 4 * (R + G) + 3):
+            tq = C.quantized_tokens(cfg, T)
+            sl = C.window_slots(cfg, tq, T)
+            assert len(set(sl.tolist())) == T - tq <= C.ring_slots(cfg)
+
+
+def _per_head_case():
+    """ref[b, h] = 2 e_0 (norm 2) and out = ref + d[b, h] e_1, so the relative
+    L2 error of head (b, h) is exactly d[b, h] / 2 (powers of two, exact in fp64)."""
+    B, H, D = 2, 3, 8
+    ref = np.zeros((B, H, D))
+    ref[..., 0] = 2.0
+    d = np.array([[2.0 ** -10, 2.0 ** -4, 2.0 ** -8], [2.0 ** -6, 2.0 ** -12, 2.0 ** -3]])
+    out = ref.copy()
+    out[..., 1] = d
+    return out, ref, d / 2
+
+
+def test_max_rel_l2_per_head_hand_values():
+    out, ref, e = _per_head_case()
+    assert A.max_rel_l2_per_head(out, ref) == 2.0 ** -4           # the largest, head (1, 2)
+    assert A.max_rel_l2_per_head(out, ref, heads=[(0, 0), (1, 1)]) == 2.0 ** -11
+    assert A.max_rel_l2_per_head(out, ref, heads=[(0, 1)]) == 2.0 ** -5
+    for b in range(2):
+        for h in range(3):
+            assert A.rel_l2(out[b, h], ref[b, h]) == e[b, h]
+    # the head carrying the largest error is found wherever it sits
+    for b in range(2):
+        for h in range(3):
+            o = ref.copy()
+            o[b, h, 1] = 0.5
+            assert A.max_rel_l2_per_head(o, ref) == 0.25
+
+
+@pytest.mark.parametrize("b,h", [(0, 0), (0, 1), (1, 2)])
+def test_max_rel_l2_per_head_non_finite_is_infinite(b, h):
+    """A NaN or infinity anywhere in an output (an unwritten head) fails."""
+    out, ref, _ = _per_head_case()
+    for bad in (np.nan, np.inf, -np.inf):
+        o = out.copy()
+        o[b, h, 3] = bad
+        assert A.max_rel_l2_per_head(o, ref) == np.inf
+    o = out.copy()
+    o[b, h] = np.nan
+    assert not (A.max_rel_l2_per_head(o, ref) <= 2e-3)
+
+
+def test_rel_l2_zero_reference():
+    z = np.zeros(4)
+    assert A.rel_l2(z, z) == 0.0
+    assert A.rel_l2(np.ones(4), z) == np.inf
