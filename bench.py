@@ -222,6 +222,46 @@ def summarize_counters(workload, fetch_dir, write_dir, copy_bytes, command):
     print(json.dumps(out))
 
 
+def timed_window(qtok, T0, warmup, steps, period):
+    """Untimed positioning steps to run after the warm-up so that the timed
+    decode steps hold a fold of the fp16 window, as a long decode run does once
+    every ``period`` steps (the key group).  qtok(T) is the number of quantized
+    tokens of a cache holding T tokens; step i appends at T0 + i.  Returns
+    (extra, folds): the extra steps, and the offsets inside the timed window of
+    the steps that fold.  Caches without a window (period <= 1) fold never."""
+    if period <= 1:
+        return 0, []
+
+    def folds_at(i):
+        return qtok(T0 + i + 1) > qtok(T0 + i)
+
+    first = next((i for i in range(2 * period + 1) if folds_at(i)), None)
+    if first is None:
+        return 0, []
+    f = first
+    while f < warmup + steps // 2:
+        f += period
+    extra = f - steps // 2 - warmup
+    start = warmup + extra
+    return extra, [i - start for i in range(start, start + steps) if folds_at(i)]
+
+
+def gpu_clock_record():
+    """Clock and power of the GPU as rocm-smi reports them (sampled while
+    attention launches are queued), or the reason there is none."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception as e:  # noqa: BLE001  (a record, never a failure)
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    card = next((v for k, v in sorted(data.items()) if k.startswith("card")), {})
+    keep = {k.strip(): v for k, v in card.items()
+            if any(x in k.lower() for x in ("sclk", "mclk", "fclk", "power"))}
+    return keep or {"raw": str(data)[:300]}
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
         # bench.py --summarize-counters WORKLOAD FETCH_DIR WRITE_DIR COPY_MIB "COMMAND"
@@ -253,8 +293,10 @@ def main():
     ap.add_argument("--batch", type=int, default=0, metavar="B",
                     help="number of sequences in place of the workload's own (as --context)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="after the timed region, copy MIB MiB device-to-device 3 times (a plain "
-                         "copy kernel of known size that calibrates hardware byte counters)")
+                    help="size of the device-to-device copy that measures the copy ceiling (default "
+                         "2048 MiB); the same copy kernel calibrates hardware byte counters")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the attention-only timings of the other serving-shaped workloads")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
@@ -283,13 +325,24 @@ def main():
     kspec, vspec, R, pre_rope, calibrate = fmt
     B, Hq, Hkv, D, T0 = w["B"], w["Hq"], w["Hkv"], w["D"], w["T"]
     n_new = w.get("n_new", 0)
-    steps_total = a.warmup + a.steps
-    cap = T0 + n_new * (steps_total + 1) + 64
-    cfg = K.make_config(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_tokens=cap,
-                        k=kspec, v=vspec, in_dtype=K.BF16, out_dtype=K.F32, residual=R,
-                        pre_rope_k=pre_rope, rope_base=w.get("rope_base", 10000.0),
-                        meta_dtype=K.F16 if a.meta_f16 else K.F32)
     dev = torch.device("cuda:0")
+
+    def make_cfg(cap):
+        return K.make_config(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_tokens=cap,
+                             k=kspec, v=vspec, in_dtype=K.BF16, out_dtype=K.F32, residual=R,
+                             pre_rope_k=pre_rope, rope_base=w.get("rope_base", 10000.0),
+                             meta_dtype=K.F16 if a.meta_f16 else K.F32)
+
+    # positioning: the timed steps hold a fold of the fp16 window (one every
+    # `period` steps), and a whole fold period is timed on its own afterwards
+    probe = make_cfg(T0 + 4096)
+    lay = K.kvq_arena_layout(probe)
+    period = lay.token_group if (n_new == 1 and lay.ring_slots > 0) else 1
+    extra, folds_in_window = timed_window(lambda T: K.kvq_quantized_tokens(probe, T), T0, a.warmup, a.steps,
+                                          period)
+    steps_total = a.warmup + extra + a.steps + (period if period > 1 else 0)
+    cap = T0 + n_new * (steps_total + 1) + 64
+    cfg = make_cfg(cap)
     print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
     kp = torch.from_numpy(W.full_prefill(name, "k").view(np.int16)).view(torch.bfloat16).to(dev)
     vp = torch.from_numpy(W.full_prefill(name, "v").view(np.int16)).view(torch.bfloat16).to(dev)
@@ -311,6 +364,7 @@ def main():
         raise SystemExit("bench.py: --arena-copies > 1 needs a workload without appends")
     arenas = [arena] + [arena.clone() for _ in range(copies - 1)]
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
 
     def step(T):
         """One decode step: append the new token of every sequence at T, attend
@@ -324,61 +378,76 @@ def main():
         K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel, a.splits)
         return T
 
+    def timed(fn, n):
+        """Mean ms of fn(i) over n back-to-back calls, between two HIP events
+        recorded on the launch stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     # Clock spin-up (untimed, leaves the cache unchanged): the GPU raises its
     # clocks only under sustained load, so attention at the starting context is
     # launched for a.spinup seconds before the warm-up steps.
     spin_end = time.perf_counter() + a.spinup
-    while time.perf_counter() < spin_end:
+    clocks = None
+    while time.perf_counter() < spin_end or clocks is None:
         for i in range(10):
             K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws, a.kernel, a.splits)
+        if clocks is None:
+            for i in range(40):   # keep the GPU busy while rocm-smi samples it
+                K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws, a.kernel, a.splits)
+            clocks = gpu_clock_record()
         torch.cuda.synchronize()
-    for _ in range(a.warmup):
+    for _ in range(a.warmup + extra):
         T = step(T)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
     T_first = T + n_new
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(a.steps):
-        if n_new:
-            T = step(T)
-        else:
-            K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws, a.kernel, a.splits)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    if n_new:
+        box = [T]
+
+        def one(i):
+            box[0] = step(box[0])
+        ms_per_step = timed(one, a.steps)
+        T = box[0]
+    else:
+        ms_per_step = timed(lambda i: K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws,
+                                                              a.kernel, a.splits), a.steps)
     wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / a.steps
     if n_new:
         # decode attention alone (pass 1 + merge) at the final context, for the
-        # roofline (the steps above also appended): back-to-back launches
-        # bracketed by one pair of events on the launch stream
-        a_start = torch.cuda.Event(enable_timing=True)
-        a_end = torch.cuda.Event(enable_timing=True)
-        a_start.record(stream)
-        for i in range(a.steps):
-            K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel, a.splits)
-        a_end.record(stream)
-        torch.cuda.synchronize()
-        attn_us = 1000.0 * a_start.elapsed_time(a_end) / a.steps
+        # roofline (the steps above also appended)
+        attn_us = 1000.0 * timed(lambda i: K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel,
+                                                                   a.splits), a.steps)
     else:
         attn_us = 1000.0 * ms_per_step
+    fold_period = None
+    if period > 1:
+        # a whole fold period of decode steps: exactly one of them folds
+        T_p0 = T
+        box = [T]
+
+        def one(i):
+            box[0] = step(box[0])
+        ms_p = timed(one, period)
+        T = box[0]
+        fold_period = {"steps": period, "context_start": T_p0 + 1, "context_end": T,
+                       "ms_per_step": round(ms_p, 5), "decode_steps_per_s": round(1000.0 / ms_p, 2),
+                       "note": "fold-amortized rate: the fp16 window folds once in these steps"}
     warm_us = None
     if copies > 1:
         # the same launches on one arena only (cache-warm), reported separately
-        w_start = torch.cuda.Event(enable_timing=True)
-        w_end = torch.cuda.Event(enable_timing=True)
-        w_start.record(stream)
-        for i in range(a.steps):
-            K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel, a.splits)
-        w_end.record(stream)
-        torch.cuda.synchronize()
-        warm_us = 1000.0 * w_start.elapsed_time(w_end) / a.steps
-    T_mid = (T_first + T) // 2
+        warm_us = 1000.0 * timed(lambda i: K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel,
+                                                                   a.splits), a.steps)
+    T_last = T_first + a.steps - 1 if n_new else T
+    T_mid = (T_first + T_last) // 2
     bytes_step, Tq = algorithmic_bytes(w, fmt, T_mid, meta_bytes)
-    bytes_attn = algorithmic_bytes(w, fmt, T, meta_bytes)[0]   # the attention-only launches ran at T
+    T_attn = T
+    bytes_attn = algorithmic_bytes(w, fmt, T_attn, meta_bytes)[0]
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     used_kernel = a.kernel
@@ -388,6 +457,17 @@ def main():
             used_kernel = 2
         except K.KvqError:
             used_kernel = 1
+    # copy ceiling: a plain device-to-device copy (HIP's copy kernel) of a
+    # 2 GiB buffer, reads + writes over time; the same copy calibrates counters
+    del arenas
+    copy_bytes = (a.copy_probe or 2048) << 20
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    copy_ms = timed(lambda i: dst.copy_(src), 5)
+    copy_gbs = 2.0 * copy_bytes / (copy_ms * 1e-3) / 1e9
+    del src, dst
     res = {
         "metric": "quantized decode-attention HBM GB/s (% of peak) + decode steps/s at 32K ctx",
         "value": round(value, 2),
@@ -403,10 +483,12 @@ def main():
         "data": "synthetic (seeded Gaussian K/V with fixed outlier key channels, bf16)",
         "config": {
             "workload": name, "format": DESCR[base], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
-            "head_dim": D, "context_start": T_first, "context_end": T, "append_tokens_per_step": n_new,
+            "head_dim": D, "context_start": T_first, "context_end": T_last, "append_tokens_per_step": n_new,
             "attention_kernel": {1: "generic", 2: "mfma"}[used_kernel],
             "arena_copies": copies,
             "scale_zero_dtype": "f16" if a.meta_f16 else "f32",
+            "untimed_positioning_steps": extra,
+            "folds_in_timed_steps": len(folds_in_window),
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 2),
         "attention_us": round(attn_us, 3),
@@ -420,10 +502,17 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
+            "copy_gbs": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
+            "copy": f"device-to-device copy of {copy_bytes >> 20} MiB (HIP copy kernel), reads + writes / time, "
+                    f"mean of 5 between HIP events",
             "kernel": "decode attention launch: pass 1 (split-K) + merge; mean of back-to-back launches between two HIP events on the launch stream",
             "limiter": LIMITER[base] if name in (base, base + "+meta16") else "not recorded for this size",
         },
+        "gpu_clocks": clocks,
     }
+    if fold_period is not None:
+        res["fold_period"] = fold_period
     if warm_us is not None:
         res["attention_us_one_arena_warm"] = round(warm_us, 3)
     traffic = measured_traffic(name) if name in (base, base + "+meta16") else None
@@ -431,19 +520,80 @@ def main():
         res["roofline"]["traffic"] = traffic["bytes_per_launch"]
         res["roofline"]["traffic_source"] = traffic["source"]
     if a.copy_probe > 0:
-        nbytes = a.copy_probe << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_probe_bytes"] = nbytes
+        res["copy_probe_bytes"] = copy_bytes
+    del arena, ws
+    torch.cuda.empty_cache()
+    if not a.no_secondary and name == base:
+        res["secondary"] = {}
+        for other in SECONDARY:
+            if other == base:
+                continue
+            print(f"[bench] secondary: {other} attention only", file=sys.stderr, flush=True)
+            res["secondary"][other] = attention_only(K, W, torch, other, a.steps, min(a.spinup, 0.5))
     if not a.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(name, w, fmt, T_first, algorithmic_bytes(w, fmt, T_first, meta_bytes)[0],
                                            a.cpu_budget, meta16=a.meta_f16)
     print(json.dumps(res), flush=True)
+
+
+# the other serving-shaped workloads, timed (attention only) in the same run
+SECONDARY = ("c3_fp8_e4m3_gqa_8k", "c4_int4_llama70b_128k", "c5_int2_kivi_prerope_32k")
+
+
+def attention_only(K, W, torch, name, steps, spinup):
+    """Decode attention (pass 1 + merge) of a workload's full-size cache after
+    its prefill and, where the workload appends, its first new token: mean of
+    `steps` back-to-back launches rotated over identical arenas (4 when the
+    arena is under 1 GiB, so the 256 MB Infinity Cache cannot hold them)."""
+    import numpy as np
+    w = W.WORKLOADS[name]
+    kspec, vspec, R, pre_rope, calibrate = FORMATS[name]
+    B, Hq, Hkv, D = w["B"], w["Hq"], w["Hkv"], w["D"]
+    n_new = w.get("n_new", 0)
+    T = w["T"] + n_new
+    dev = torch.device("cuda:0")
+    cfg = K.make_config(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_tokens=T, k=kspec, v=vspec,
+                        in_dtype=K.BF16, out_dtype=K.F32, residual=R, pre_rope_k=pre_rope,
+                        rope_base=w.get("rope_base", 10000.0))
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    arena = torch.empty(K.kvq_arena_bytes(cfg), dtype=torch.uint8, device=dev)
+    kp, vp = up(W.full_prefill(name, "k")), up(W.full_prefill(name, "v"))
+    K.kvq_quantize_append(cfg, arena, 0, kp, vp, flags=K.CALIBRATE if calibrate else 0)
+    del kp, vp
+    if n_new:
+        K.kvq_quantize_append(cfg, arena, w["T"], up(W.full_new_tokens(name, "k")), up(W.full_new_tokens(name, "v")))
+    q = up(W.query(name))
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.zeros(K.kvq_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    copies = 4 if arena.numel() < (1 << 30) else 1
+    arenas = [arena] + [arena.clone() for _ in range(copies - 1)]
+    sm = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream(dev)
+    end = time.perf_counter() + spinup
+    while time.perf_counter() < end:
+        for i in range(10):
+            K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / steps
+    nbytes = algorithmic_bytes(w, FORMATS[name], T)[0]
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del arenas, arena, ws
+    torch.cuda.empty_cache()
+    return {"attention_us": round(us, 3), "achieved_gbs": round(gbs, 1),
+            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "attention_launches_per_s": round(1e6 / us, 1), "context": T, "arena_copies": copies,
+            "algorithmic_bytes": int(nbytes)}
 
 
 if __name__ == "__main__":

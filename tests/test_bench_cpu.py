@@ -87,3 +87,27 @@ def test_fp16_metadata_bytes_int2_prerope():
     meta32 = pairs * (32736 // 32) * 128 * 8 + pairs * 32736 * 4 * 8
     assert t32 - t16 == meta32 // 2
     assert abs(t16 / 1e6 - 809.6) < 0.1
+
+
+@pytest.mark.parametrize("warmup,steps", [(5, 20), (10, 50), (0, 1), (3, 31), (0, 64)])
+def test_timed_window_holds_a_fold(warmup, steps):
+    """The INT2 cache folds its 32-token window once every 32 decode steps; the
+    timed steps are positioned to hold one fold (two when they span more than
+    a period), at the offsets the fold rule gives."""
+    from oracle import cache as OC
+    cfg = OC.Cfg(1, 4, 1, 128, OC.Spec(1, 2, 1, 32), OC.Spec(1, 2, 2, 32), R=32)
+    qtok = lambda T: OC.quantized_tokens(cfg, T)   # noqa: E731
+    T0 = 32768
+    extra, folds = bench.timed_window(qtok, T0, warmup, steps, 32)
+    assert extra >= 0 and 1 <= len(folds) <= 1 + steps // 32
+    start = warmup + extra
+    for i in range(steps):
+        t = T0 + start + i
+        assert (qtok(t + 1) > qtok(t)) == (i in folds)
+    assert steps // 2 in folds
+
+
+def test_timed_window_without_a_window_is_empty():
+    from oracle import cache as OC
+    cfg = OC.Cfg(1, 4, 1, 128, OC.Spec(3, 8, 0, 0), OC.Spec(3, 8, 0, 0), R=0)
+    assert bench.timed_window(lambda T: OC.quantized_tokens(cfg, T), 8192, 5, 20, 1) == (0, [])

@@ -63,10 +63,13 @@ def _schedule(kind, T):
 
 
 def run_case(case: Case, T: int, schedule, seed=0, kernels=None, fp8_mode="calibrate",
-             num_splits=0):
+             num_splits=0, inputs=None, queries=None):
     say(f"[case] {case} T={T} sched={schedule[:4]}... seed={seed}")
-    (Kf, Kp), (Vf, Vp) = W.random_case(seed, case.B, case.Hkv, T, case.D, dtype=case.dtype)
-    qf, qp = W.random_queries(seed, case.B, case.Hq, case.D, dtype=case.dtype)
+    if inputs is None:
+        (Kf, Kp), (Vf, Vp) = W.random_case(seed, case.B, case.Hkv, T, case.D, dtype=case.dtype)
+    else:
+        (Kf, Kp), (Vf, Vp) = inputs
+    qf, qp = W.random_queries(seed, case.B, case.Hq, case.D, dtype=case.dtype) if queries is None else queries
     gc = GpuCache(case, cap=T + 5)
     fp8 = case.k[0] == F8 or case.v[0] == F8
     ks = vs = None
@@ -402,3 +405,48 @@ def test_fp8_step_interleave_over_split_counts(name, fmt, T):
     for s in (1, 2, 3, 5, 16, 64):
         out = gc.attention(qp, kernel=K.KERNEL_MFMA, num_splits=s)
         assert attention_error(out, qf, st, case) <= ATTN_TOL, (name, T, s)
+
+
+# Quantizer corner cases (workloads.edge_case_inputs): constant groups (the
+# 1e-8 range floor), a group of -0.0, fp16-subnormal ranges (fp16 metadata then
+# stores subnormal scales), exact half-way ties, -0.0 mixed with positives,
+# and values near or beyond the fp16 range.  Codes, scales, zero-points, window
+# and dequantized values must match the oracle bit for bit; attention stays
+# within tolerance on every kernel that serves the format.
+# (name, format, code bits of the tie pattern, values beyond fp16, FP8 mode)
+EDGE = [
+    ("int2ch32_int2tok32_R32", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32), 2, False),
+    ("int2ch32_int2tok32_R32_meta16", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, meta16=True), 2, False),
+    ("prerope_int2ch32_int2tok32_R32", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True), 2, False),
+    ("int4ch128_int4tok_R128", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128), 4, False),
+    ("int4ch128_int4tok_R128_meta16", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128, meta16=True), 4, False),
+    ("int8ch64_int8tok16_R64", dict(k=(A, 8, CH, 64), v=(A, 8, TOK, 16), R=64), 8, False),
+    ("int8ch64_int8tok16_R64_meta16", dict(k=(A, 8, CH, 64), v=(A, 8, TOK, 16), R=64, meta16=True), 8, False),
+    ("sym8tok_sym8tok32", dict(k=(S, 8, TOK, 0), v=(S, 8, TOK, 32), R=0), 8, True),
+    ("int4tok_int2tok32_R0_big", dict(k=(A, 4, TOK, 0), v=(A, 2, TOK, 32), R=0), 4, True),
+    ("int4tok_int2tok32_R0_big_meta16", dict(k=(A, 4, TOK, 0), v=(A, 2, TOK, 32), R=0, meta16=True), 4, True),
+    ("sym8tok_sym8tok32_big_meta16", dict(k=(S, 8, TOK, 0), v=(S, 8, TOK, 32), R=0, meta16=True), 8, True),
+    ("fp8_e4m3_calibrated", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0), 4, False),
+    ("fp8_e5m2_big", dict(k=(E5, 8, 0, 0), v=(E5, 8, 0, 0), R=0), 4, True),
+]
+
+
+@pytest.mark.parametrize("name,fmt,bits,big", EDGE, ids=[e[0] for e in EDGE])
+@pytest.mark.parametrize("sched", ["oneshot", "stream"])
+def test_quantizer_edge_cases(name, fmt, bits, big, sched):
+    case = Case(B=1, Hq=8, Hkv=2, D=128, dtype="f32", **fmt)
+    T = 300
+    Kf, Vf = W.edge_case_inputs(zlib.crc32(name.encode()) % 1000, case.B, case.Hkv, T, case.D, bits, big=big)
+    # the query ignores key channel 5 (values near or beyond the fp16 range), so
+    # the logits stay O(1) and the attention check measures the cache
+    qf, _ = W.random_queries(2, case.B, case.Hq, case.D)
+    qf = qf.copy()
+    qf[..., 5] = 0.0
+    _, st, _ = run_case(case, T, _schedule(sched, T), seed=1, inputs=((Kf, Kf), (Vf, Vf)), queries=(qf, qf))
+    # the planted groups reached the encoders: ties rounded to even somewhere,
+    # a constant group stored the range floor
+    if fmt["k"][0] == A and fmt["k"][2] == CH and st["Tq"] >= fmt["k"][3]:
+        s_k = np.asarray(st["k"]["scale"])[0, 0, 0]
+        assert s_k[0] == np.float32(np.float32(1e-8) / np.float32(2 ** bits - 1)) or fmt.get("meta16")
+        codes = st["k"]["codes"][0, 0, :32, 3]
+        assert set(codes.tolist()) <= set(range(2 ** bits)) and (codes % 2 == 0).sum() > (codes % 2 == 1).sum()

@@ -116,9 +116,15 @@ LARGE = {
 }
 
 
+N_STEPS = 40          # decode steps of test_large_decode_steps_against_oracle
+
+
 def _samples(w):
+    """Every kv head of the first and the last sequence (all heads of a
+    batch-1 workload): 16 pairs for the batch-16 and batch-32 caches, 8 for
+    the batch-1 one."""
     B, H = w["B"], w["Hkv"]
-    return sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)})
+    return sorted({(b, h) for b in (0, B - 1) for h in range(H)})
 
 
 @pytest.fixture(scope="module", params=list(LARGE))
@@ -133,7 +139,7 @@ def large(request):
     Vp = W.full_prefill(name, "v")
     n_new = w.get("n_new", 0)
     T = w["T"] + n_new
-    gc = GpuCache(case, cap=T)
+    gc = GpuCache(case, cap=T + (N_STEPS if n_new else 0))
     fp8 = fmt["k"][0] == F8
     say(f"[{name}] prefill append T={w['T']}")
     gc.append(Kp, Vp, K.CALIBRATE if fp8 else 0)
@@ -151,7 +157,7 @@ def large(request):
         scales = (OQ.fp8_scale_from_absmax(amax_k), OQ.fp8_scale_from_absmax(amax_v))
     del Kp, Vp
     q = W.query(name)
-    yield dict(name=name, w=w, case=case, gc=gc, T=T, scales=scales, q=q)
+    yield dict(name=name, w=w, case=case, gc=gc, T=T, scales=scales, q=q, oracle={})
     del gc
     torch.cuda.empty_cache()
 
@@ -172,11 +178,20 @@ def _oracle_pair(name, w, case, b, h, T, scales):
     return OC.quantize_cache(sub, Kf, Vf, T, k_scale=ks, v_scale=vs)
 
 
+def _oracle_cached(L, b, h):
+    """The oracle state of one (sequence, kv head) of the fixture's cache,
+    computed once per module and shared by the tests below."""
+    key = (b, h)
+    if key not in L["oracle"]:
+        L["oracle"][key] = _oracle_pair(L["name"], L["w"], L["case"], b, h, L["T"], L["scales"])
+    return L["oracle"][key]
+
+
 def test_large_sections_bit_exact(large):
     L = large
     for (b, h) in _samples(L["w"]):
         say(f"[{L['name']}] sections of (b={b}, h={h})")
-        st = _oracle_pair(L["name"], L["w"], L["case"], b, h, L["T"], L["scales"])
+        st = _oracle_cached(L, b, h)
         compare_sections(L["gc"], st, bh_sel=(b, h))
         compare_dequant(L["gc"], st, bh_sel=(b, h))
 
@@ -189,7 +204,7 @@ def test_large_attention(large):
     sm = 1.0 / math.sqrt(case.D)
     outs = {kern: gc.attention(L["q"], kernel=kern) for kern in _kernels_for(gc)}
     for (b, h) in _samples(L["w"]):
-        st = _oracle_pair(L["name"], L["w"], case, b, h, T, L["scales"])
+        st = _oracle_cached(L, b, h)
         qs = qf[b:b + 1, h * n_rep:(h + 1) * n_rep]
         ref = OA.decode_attention(qs, st["k_hat"], st["v_hat"], sm,
                                   pre_rope_base=case.rope_base if case.pre_rope else None)
@@ -206,3 +221,66 @@ def test_large_attention(large):
         say(f"[{L['name']}] MFMA vs generic over all {rel.size} heads: max {rel.max():.2e} "
             f"mean {rel.mean():.2e} p99 {np.percentile(rel, 99):.2e}")
         assert rel.max() <= ATTN_TOL
+
+
+def test_large_decode_steps_against_oracle(large):
+    """kvq_decode_step, the call bench.py times, in its default launch
+    configuration at the workload's full size: N_STEPS consecutive steps (the
+    INT2 cache folds its fp16 window once among them; the FP8 caches encode the
+    new token inside the attention launch), each with its own new tokens and
+    query.  Afterwards the cache bytes of sampled (sequence, kv head) pairs
+    match the oracle bit for bit, and the outputs of the first step, the first
+    fold step and the last step are within tolerance of the oracle's attention
+    over the cache as it stood at that step.  Runs after the tests above (it
+    appends to the shared cache)."""
+    L = large
+    w, case, gc, name = L["w"], L["case"], L["gc"], L["name"]
+    if not w.get("n_new"):
+        pytest.skip("this workload appends nothing")
+    B, Hq, Hkv, D = case.B, case.Hq, case.Hkv, case.D
+    n_rep = Hq // Hkv
+    T0 = gc.T
+    sm = 1.0 / math.sqrt(D)
+    ocfg = case.oracle_cfg()
+    folds = [i for i in range(N_STEPS) if OC.quantized_tokens(ocfg, T0 + i + 1) > OC.quantized_tokens(ocfg, T0 + i)]
+    if OC.token_group(ocfg) > 1:
+        assert folds, "the steps should cross a fold"
+    checks = sorted({0, N_STEPS - 1} | set(folds[:1]))
+    ws = torch.zeros(K.kvq_workspace_bytes(gc.cfg, T0 + N_STEPS), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    outs = {}
+    say(f"[{name}] {N_STEPS} decode steps from T={T0}, folds at steps {folds[:3]}")
+    for i in range(N_STEPS):
+        kn = to_dev(W.step_tokens_all(name, "k", i), "bf16")
+        vn = to_dev(W.step_tokens_all(name, "v", i), "bf16")
+        q = to_dev(W.step_query(name, i), "bf16")
+        out.fill_(float("nan"))
+        K.kvq_decode_step(gc.cfg, gc.arena, T0 + i, kn, vn, q, out, sm, ws)
+        if i in checks:
+            torch.cuda.synchronize()
+            outs[i] = out.cpu().numpy()
+            assert np.isfinite(outs[i]).all(), f"step {i}: outputs not written"
+    torch.cuda.synchronize()
+    gc.T = T0 + N_STEPS
+    pairs = sorted({(0, 0), (0, Hkv - 1), (B - 1, 0), (B - 1, Hkv - 1)})
+    sub = case.oracle_cfg(B=1, Hq=n_rep, Hkv=1)
+    for (b, h) in pairs:
+        kb = np.concatenate([W.kv_chunk(name, b, h, "k"), W.new_token_chunk(name, b, h, "k"),
+                             W.step_tokens(name, b, h, "k", 0, N_STEPS)])
+        vb = np.concatenate([W.kv_chunk(name, b, h, "v"), W.new_token_chunk(name, b, h, "v"),
+                             W.step_tokens(name, b, h, "v", 0, N_STEPS)])
+        Kf, Vf = W.bf16_bits_to_f32(kb)[None, None], W.bf16_bits_to_f32(vb)[None, None]
+        ks = vs = None
+        if L["scales"] is not None:
+            ks, vs = L["scales"][0][h:h + 1], L["scales"][1][h:h + 1]
+        st = OC.quantize_cache(sub, Kf, Vf, T0 + N_STEPS, k_scale=ks, v_scale=vs)
+        compare_sections(gc, st, bh_sel=(b, h))
+        compare_dequant(gc, st, bh_sel=(b, h))
+        for i in checks:
+            sti = OC.quantize_cache(sub, Kf, Vf, T0 + i + 1, k_scale=ks, v_scale=vs)
+            qf = W.bf16_bits_to_f32(W.step_query(name, i))[b:b + 1, h * n_rep:(h + 1) * n_rep]
+            ref = OA.decode_attention(qf, sti["k_hat"], sti["v_hat"], sm,
+                                      pre_rope_base=case.rope_base if case.pre_rope else None)
+            err = OA.max_rel_l2_per_head(outs[i][b:b + 1, h * n_rep:(h + 1) * n_rep], ref)
+            say(f"[{name}] step {i} (T={T0 + i + 1}) (b={b}, h={h}) max rel-L2 {err:.2e}")
+            assert err <= ATTN_TOL, (name, i, b, h, err)

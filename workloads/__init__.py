@@ -28,6 +28,7 @@ import numpy as np
 
 # tensor ids for the per-chunk seeds
 _TID_K, _TID_V, _TID_Q, _TID_KNEW, _TID_VNEW, _TID_OUTLIER = 1, 2, 3, 4, 5, 6
+_TID_STEP_K, _TID_STEP_V, _TID_STEP_Q = 7, 8, 9
 
 # ----------------------------------------------------------------------------
 # dtype helpers (bit-pattern conversions of generated inputs)
@@ -145,6 +146,39 @@ def new_token_chunk(name: str, b: int, h: int, which: str):
     return f32_to_bf16_bits(x)
 
 
+def step_tokens(name: str, b: int, h: int, which: str, first: int, n: int) -> np.ndarray:
+    """bf16 bits [n, D] of decode steps first .. first+n-1 of (b, h): the token
+    appended at step i is drawn from its own seed (keys carry the head's fixed
+    outlier channels), so any step can be regenerated alone."""
+    w = WORKLOADS[name]
+    rows = []
+    for i in range(first, first + n):
+        x = np.random.default_rng((w["seed"], _TID_STEP_K if which == "k" else _TID_STEP_V, b, h, i)) \
+            .standard_normal((1, w["D"]), dtype=np.float32)
+        if which == "k":
+            x[:, outlier_channels(name)[h]] *= np.float32(w["outlier_scale"])
+        rows.append(x)
+    return f32_to_bf16_bits(np.concatenate(rows) if rows else np.zeros((0, w["D"]), np.float32))
+
+
+def step_tokens_all(name: str, which: str, step: int) -> np.ndarray:
+    """bf16 bits [B, Hkv, 1, D] of decode step ``step`` for every (b, h)."""
+    w = WORKLOADS[name]
+    out = np.empty((w["B"], w["Hkv"], 1, w["D"]), dtype=np.uint16)
+    for b in range(w["B"]):
+        for h in range(w["Hkv"]):
+            out[b, h] = step_tokens(name, b, h, which, step, 1)
+    return out
+
+
+def step_query(name: str, step: int) -> np.ndarray:
+    """bf16 bits [B, Hq, D] of the query of decode step ``step``."""
+    w = WORKLOADS[name]
+    x = np.random.default_rng((w["seed"], _TID_STEP_Q, step)).standard_normal((w["B"], w["Hq"], w["D"]),
+                                                                            dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
 def query(name: str) -> np.ndarray:
     """bf16 bits [B, Hq, D] of the decode query (already rotated when keys are pre-RoPE)."""
     w = WORKLOADS[name]
@@ -241,6 +275,54 @@ def rope_study_case(seed: int, B: int, Hq: int, Hkv: int, T: int, D: int,
                 K[:, h, :, c] *= np.float32(magnitude)
     q = rng.standard_normal((B, Hq, D), dtype=np.float32)
     return K, V, q
+
+
+def edge_case_inputs(seed: int, B: int, Hkv: int, T: int, D: int, bits: int, big: bool = False):
+    """fp32 K, V [B, Hkv, T, D] whose quantization groups hit the encoders'
+    corner cases, planted over N(0, 1) background values.  Every planted value
+    is an fp16 number (so staging through an fp16 window keeps it), except
+    with big=True, which plants values beyond +-65504 (for caches without a
+    window).  Keys (per-channel groups along tokens) get, per channel:
+      0  the constant 3.0 (max - min = 0: the range floor decides the scale),
+      1  -0.0 everywhere (a constant group whose minimum is negative zero),
+      2  tiny values j * 2^-24 (fp16 subnormals; a scale far below fp16's
+         normal range),
+      3  exact half-way ties: 0 and 2^bits - 1 in every group of 32 tokens
+         plus k + 1/2 elsewhere, so (x - min) / scale lands on k + 1/2,
+      4  -0.0 and 0.0 mixed with 1, 2, 3,
+      5  big=True: +-1e5 and 7e4 (beyond fp16), else large fp16 values +-6e4.
+    Values (per-token groups along channels) get the same patterns along the
+    channels of tokens 0..5 of every 32-token block."""
+    rng = np.random.default_rng((seed, 81))
+    K = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    V = rng.standard_normal((B, Hkv, T, D), dtype=np.float32)
+    qmax = float(2 ** bits - 1)
+
+    def pattern(n, kind):
+        j = np.arange(n)
+        if kind == 0:
+            return np.full(n, 3.0)
+        if kind == 1:
+            return np.full(n, -0.0)
+        if kind == 2:
+            return (j % 29 + 1) * 2.0 ** -24
+        if kind == 3:
+            v = (j % int(qmax)) + 0.5
+            v[j % 32 == 0] = 0.0
+            v[j % 32 == 1] = qmax
+            return v
+        if kind == 4:
+            return np.array([-0.0, 0.0, 1.0, 2.0, 3.0, -0.0, 0.0])[j % 7]
+        if big:
+            return np.array([1e5, -1e5, 7e4, 2.0, -3.0])[j % 5]
+        return np.array([6e4, -6e4, 0.5, 1.0])[j % 4]
+
+    for kind in range(6):
+        K[:, :, :, kind] = pattern(T, kind).astype(np.float32)
+        for t0 in range(0, T, 32):
+            if t0 + kind < T:
+                V[:, :, t0 + kind, :] = pattern(D, kind).astype(np.float32)
+    return K, V
 
 
 def random_queries(seed: int, B: int, Hq: int, D: int, dtype: str = "f32"):
