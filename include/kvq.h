@@ -235,6 +235,26 @@ int kvq_decode_attention(const kvq_config* cfg, const void* arena, int64_t T,
                          const kvq_attn_options* opt, hipStream_t stream);
 
 /*
+ * Decode attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same computation, kernels and result,
+ * bit for bit, as kvq_decode_attention with the same options; the split
+ * partials go to a device array of KVQ_STATIC_WORKSPACE_BYTES owned by the
+ * library (one per GPU, held until the process ends) instead of a caller
+ * workspace.  Nothing is allocated: a call whose kvq_workspace_bytes(cfg, T,
+ * opt) exceeds the array returns KVQ_ERR_WORKSPACE before any HIP call (use
+ * fewer splits or kvq_decode_attention).  The array belongs to the current
+ * device; `stream` must be a stream of that device.  Every call on one GPU
+ * shares the array: calls that may overlap on one GPU (different streams, or
+ * host threads) race and give wrong results; serialize them.  The first call
+ * on a device looks up the array's address (KVQ_ERR_HIP if that fails).
+ */
+#define KVQ_STATIC_WORKSPACE_BYTES (16u << 20)
+int kvq_decode_attention_static(const kvq_config* cfg, const void* arena, int64_t T,
+                                const void* q, void* out, float sm_scale,
+                                const kvq_attn_options* opt, hipStream_t stream);
+
+/*
  * One decode step: append one token per sequence at position t0 (t0 >= 1, a
  * cache started by kvq_quantize_append) and attend over T = t0 + 1 tokens.
  * The result, cache bytes and output, equals kvq_quantize_append(t0, 1)
@@ -270,7 +290,8 @@ int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T,
 const char* kvq_status_string(int status);
 
 /* ABI version: bumped when the arena layout or a signature changes, or an
- * entry point is added (2: kvq_decode_step; 3: kvq_config.meta_dtype). */
+ * entry point is added (2: kvq_decode_step; 3: kvq_config.meta_dtype;
+ * 4: kvq_decode_attention_static). */
 int kvq_abi_version(void);
 
 #ifdef __cplusplus

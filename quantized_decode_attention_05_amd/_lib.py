@@ -70,6 +70,7 @@ _sig = {
     "kvq_workspace_bytes": (C.c_int, [_CFG, C.c_int64, C.POINTER(AttnOptions), C.POINTER(C.c_size_t)]),
     "kvq_decode_attention": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, C.c_float, _P, C.c_size_t,
                                        C.POINTER(AttnOptions), _P]),
+    "kvq_decode_attention_static": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, C.c_float, C.POINTER(AttnOptions), _P]),
     "kvq_decode_step": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P, _P, C.c_float, _P, C.c_size_t,
                                   C.POINTER(AttnOptions), _P]),
     "kvq_decode_step_fused": (C.c_int, [_CFG, C.c_int64, C.POINTER(AttnOptions)]),
@@ -258,6 +259,22 @@ def kvq_decode_attention(cfg: Config, arena, T: int, q, out, sm_scale: float, wo
     st = _lib.kvq_decode_attention(C.byref(cfg), _ptr(arena), T, _ptr(q), _ptr(out), sm_scale,
                                    _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
     _check(st, "kvq_decode_attention")
+
+
+STATIC_WORKSPACE_BYTES = 16 << 20   # KVQ_STATIC_WORKSPACE_BYTES
+
+
+def kvq_decode_attention_static(cfg: Config, arena, T: int, q, out, sm_scale: float, kernel: int = 0,
+                                num_splits: int = 0, stream=None) -> None:
+    """kvq_decode_attention with the split partials in the library's own
+    device array (no workspace argument; calls on one GPU must not overlap)."""
+    o = _opts(kernel, num_splits)
+    _check_arena(cfg, arena)
+    _check_query_out(cfg, q, out)
+    _on_gpu(arena=arena, q=q, out=out)
+    st = _lib.kvq_decode_attention_static(C.byref(cfg), _ptr(arena), T, _ptr(q), _ptr(out), sm_scale,
+                                          C.byref(o), _stream(stream, arena, q))
+    _check(st, "kvq_decode_attention_static")
 
 
 def kvq_decode_step(cfg: Config, arena, t0: int, k_new, v_new, q, out, sm_scale: float, workspace,

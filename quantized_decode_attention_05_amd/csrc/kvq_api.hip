@@ -1,6 +1,7 @@
 // Host side of the C ABI: config validation, arena layout, and the order of
 // kernel launches for append / attention / dequantize.  Everything here runs
 // on the host; validation finishes before the first HIP call.
+#include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -158,13 +159,43 @@ static int hip_status(hipError_t e, const char* where) {
   return KVQ_ERR_HIP;
 }
 
+// Split-K partials of kvq_decode_attention_static: a file-scope device array
+// (one copy per GPU, alive until the process ends) in place of a caller
+// workspace.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is a stand-in, not a device address): each device's address
+// is taken once with hipGetSymbolAddress, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[KVQ_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+static int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "kvq_decode_attention_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e,
+                                                   "kvq_decode_attention_static: hipGetSymbolAddress");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
 }  // namespace kvq
 
 using namespace kvq;
 
 extern "C" {
 
-int kvq_abi_version(void) { return 3; }
+int kvq_abi_version(void) { return 4; }
 
 const char* kvq_status_string(int s) {
   switch (s) {
@@ -303,6 +334,31 @@ int kvq_decode_attention(const kvq_config* cfg, const void* arena, int64_t T, co
   hipError_t e = launch_attention(p, ap, arena, q, out, sm_scale, workspace, stream);
   if (e == hipSuccess) e = hipGetLastError();
   return hip_status(e, "kvq_decode_attention");
+}
+
+int kvq_decode_attention_static(const kvq_config* cfg, const void* arena, int64_t T, const void* q,
+                                void* out, float sm_scale, const kvq_attn_options* opt,
+                                hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if (T < 1 || T > p.max_tokens) return KVQ_ERR_CAPACITY;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_ERR_INVALID_ARG;
+  AttnPlan ap;
+  st = make_attn_plan(p, T, opt, &ap);
+  if (st != KVQ_OK) return st;
+  if (ap.workspace_bytes > KVQ_STATIC_WORKSPACE_BYTES) return KVQ_ERR_WORKSPACE;
+  if (!arena || !q || !out) return KVQ_ERR_NULL;
+  if (!aligned(arena, 256) || !aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != KVQ_OK) return st;
+  if (log_enabled())
+    fprintf(stderr, "[kvq] attention (static scratch) T=%lld kernel=%d splits=%d bytes=%llu\n",
+            (long long)T, ap.kernel, ap.splits, (unsigned long long)ap.workspace_bytes);
+  (void)hipGetLastError();
+  hipError_t e = launch_attention(p, ap, arena, q, out, sm_scale, ws, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  return hip_status(e, "kvq_decode_attention_static");
 }
 
 // How a decode step at t0 runs: 1 = new token into the fp16 window inside the

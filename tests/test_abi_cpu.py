@@ -267,7 +267,7 @@ def test_meta_dtype_validation():
     for bad in (2, -1, 7):
         with pytest.raises(K.KvqError):
             K.kvq_arena_bytes(_cfg(meta_dtype=bad))
-    assert K.kvq_abi_version() == 3
+    assert K.kvq_abi_version() == 4
 
 
 def test_plain_c_caller(tmp_path):
@@ -366,3 +366,33 @@ def test_binding_rejects_bad_dequantize_arguments():
     _rejects(dq, cfg, t["arena"], 16, t["ko"].double(), match="k_out has dtype")
     _rejects(dq, cfg, t["arena"], 16, None, t["ko"].half(), match="v_out has dtype")
     _rejects(dq, cfg, t["arena"], 16, t["ko"], match="arena must be a GPU tensor")
+
+
+def test_static_scratch_entry_point_validation():
+    """kvq_decode_attention_static refuses, before any HIP call, a request whose
+    split partials exceed its device array, and bad pointers."""
+    raw = _lib.raw
+    cfg = _cfg()
+    opt = K.AttnOptions()
+
+    def call(c=cfg, T=500, arena=0x100000, q=0x200000, out=0x300000, o=opt):
+        return raw.kvq_decode_attention_static(C.byref(c), arena, T, q, out, 0.088, C.byref(o), None)
+
+    assert call(T=0) == -3
+    assert call(q=None) == -5
+    assert call(arena=0x100010) == -4
+    big = _cfg(batch=64, num_q_heads=64, num_kv_heads=8, max_tokens=131072, k=(K.INT_ASYM, 4, K.PER_CHANNEL, 128),
+               v=(K.INT_ASYM, 4, K.PER_TOKEN, 0), residual=128)
+    o64 = K.AttnOptions()
+    o64.num_splits = 64
+    assert K.kvq_workspace_bytes(big, 131072, 0, 64) > K.STATIC_WORKSPACE_BYTES
+    assert call(c=big, T=131072, o=o64) == -6
+    # the serving-shaped workloads fit with their automatic split counts
+    import workloads as W
+    import bench
+    for name in ("c3_fp8_e4m3_gqa_8k", "c4_int4_llama70b_128k", "c5_int2_kivi_prerope_32k"):
+        w = W.WORKLOADS[name]
+        kspec, vspec, R, pre, _ = bench.FORMATS[name]
+        c = K.make_config(batch=w["B"], num_q_heads=w["Hq"], num_kv_heads=w["Hkv"], head_dim=128,
+                          max_tokens=w["T"] + 64, k=kspec, v=vspec, residual=R, pre_rope_k=pre)
+        assert K.kvq_workspace_bytes(c, w["T"] + 1) <= K.STATIC_WORKSPACE_BYTES, name
