@@ -437,11 +437,13 @@ def test_quantizer_edge_cases(name, fmt, bits, big, sched):
     case = Case(B=1, Hq=8, Hkv=2, D=128, dtype="f32", **fmt)
     T = 300
     Kf, Vf = W.edge_case_inputs(zlib.crc32(name.encode()) % 1000, case.B, case.Hkv, T, case.D, bits, big=big)
-    # the query ignores key channel 5 (values near or beyond the fp16 range), so
-    # the logits stay O(1) and the attention check measures the cache
+    # the query ignores key channels 4 and 5 (channel 5 holds values near or
+    # beyond the fp16 range, and RoPE mixes it into its pair partner 4), so the
+    # logits stay O(1) and the attention check measures the cache rather than
+    # fp32 rounding of logits in the thousands
     qf, _ = W.random_queries(2, case.B, case.Hq, case.D)
     qf = qf.copy()
-    qf[..., 5] = 0.0
+    qf[..., 4:6] = 0.0
     _, st, _ = run_case(case, T, _schedule(sched, T), seed=1, inputs=((Kf, Kf), (Vf, Vf)), queries=(qf, qf))
     # the planted groups reached the encoders: ties rounded to even somewhere,
     # a constant group stored the range floor
