@@ -56,27 +56,37 @@ def code_bits(spec):
     return bits if scheme in (0, 1) else 8
 
 
-def algorithmic_bytes(w, fmt, T, meta_bytes=4):
+def algorithmic_bytes(w, fmt, T, meta_bytes=4, lens=None):
     """Bytes one decode attention over T tokens must move: every packed code, its
     scale/zero (fp32, or fp16 with meta_bytes=2) and the fp16 window read once,
-    q (bf16) read, out (fp32) written."""
+    q (bf16) read, out (fp32) written.  lens: per-sequence lengths of a ragged
+    batch (T is then ignored); returns (bytes, Tq of the last length)."""
     kspec, vspec, R, _, _ = fmt
     B, Hq, Hkv, D = w["B"], w["Hq"], w["Hkv"], w["D"]
     G = kspec[3] if (kspec[0] in (1, 2) and kspec[2] == 1 and kspec[3] > 0) else 1
-    Tq = G * (max(T - R, 0) // G) if (R > 0 or G > 1) else T
-    per = 0.0
-    per += Tq * D * code_bits(kspec) / 8 + Tq * D * code_bits(vspec) / 8
-    for spec in (kspec, vspec):
-        nmeta = 2 if spec[0] == 1 else 1
-        if spec[0] in (1, 2):
-            if spec[2] == 1:
-                per += (Tq // spec[3] if spec[3] else 1) * D * meta_bytes * nmeta
-            elif spec[2] == 2:
-                per += Tq * (D // (spec[3] or D)) * meta_bytes * nmeta
-            else:
-                per += meta_bytes * nmeta
-    per += (T - Tq) * D * 2 * 2
-    total = per * B * Hkv
+
+    def per_seq(T):
+        Tq = G * (max(T - R, 0) // G) if (R > 0 or G > 1) else T
+        per = 0.0
+        per += Tq * D * code_bits(kspec) / 8 + Tq * D * code_bits(vspec) / 8
+        for spec in (kspec, vspec):
+            nmeta = 2 if spec[0] == 1 else 1
+            if spec[0] in (1, 2):
+                if spec[2] == 1:
+                    per += (Tq // spec[3] if spec[3] else 1) * D * meta_bytes * nmeta
+                elif spec[2] == 2:
+                    per += Tq * (D // (spec[3] or D)) * meta_bytes * nmeta
+                else:
+                    per += meta_bytes * nmeta
+        per += (T - Tq) * D * 2 * 2
+        return per, Tq
+
+    if lens is None:
+        lens = [T] * B
+    total, Tq = 0.0, 0
+    for t in lens:
+        per, Tq = per_seq(int(t))
+        total += per * Hkv
     fp8_scales = 8 * Hkv if kspec[0] in (3, 4) else 0
     return total + fp8_scales + B * Hq * D * 2 + B * Hq * D * 4, Tq
 
@@ -297,6 +307,11 @@ def main():
                          "2048 MiB); the same copy kernel calibrates hardware byte counters")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the attention-only timings of the other serving-shaped workloads")
+    ap.add_argument("--paged", type=int, default=0, metavar="P",
+                    help="a paged cache of P-token pages handed out in a shuffled order (block tables; "
+                         "reported under a derived workload name)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="with --paged: sequence b holds T - (1021 b mod 8192) tokens instead of T")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
@@ -320,6 +335,11 @@ def main():
     if a.meta_f16:
         name = f"{name}+meta16"
         W.WORKLOADS[name] = w
+    if a.ragged and not a.paged:
+        raise SystemExit("bench.py: --ragged needs --paged")
+    if a.paged:
+        name = f"{name}+paged{a.paged}" + ("+ragged" if a.ragged else "")
+        W.WORKLOADS[name] = w
     meta_bytes = 2 if a.meta_f16 else 4
     fmt = FORMATS[base]
     kspec, vspec, R, pre_rope, calibrate = fmt
@@ -327,11 +347,13 @@ def main():
     n_new = w.get("n_new", 0)
     dev = torch.device("cuda:0")
 
-    def make_cfg(cap):
+    def make_cfg(cap, paged=False):
+        P = a.paged if paged else 0
+        pages = B * (-(-cap // P)) + 8 if paged else 0
         return K.make_config(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_tokens=cap,
                              k=kspec, v=vspec, in_dtype=K.BF16, out_dtype=K.F32, residual=R,
                              pre_rope_k=pre_rope, rope_base=w.get("rope_base", 10000.0),
-                             meta_dtype=K.F16 if a.meta_f16 else K.F32)
+                             meta_dtype=K.F16 if a.meta_f16 else K.F32, page_tokens=P, num_pages=pages)
 
     # positioning: the timed steps hold a fold of the fp16 window (one every
     # `period` steps), and a whole fold period is timed on its own afterwards
@@ -342,7 +364,20 @@ def main():
                                           period)
     steps_total = a.warmup + extra + a.steps + (period if period > 1 else 0)
     cap = T0 + n_new * (steps_total + 1) + 64
-    cfg = make_cfg(cap)
+    cfg = make_cfg(cap, paged=a.paged > 0)
+    # paged caches: lengths base[b] + s after s decode steps (s = T - T0 for
+    # the uniform-length bookkeeping below), one device array per s prepared
+    # up front so the timed steps launch nothing else
+    base = np.array([T0 - (1021 * b) % 8192 for b in range(B)] if a.ragged else [T0] * B, dtype=np.int64)
+    if a.paged:
+        pages = K.kvq_arena_layout(cfg).pages
+        nblk = -(-cap // a.paged)
+        perm = np.random.default_rng(1234).permutation(pages)[:B * nblk].astype(np.int32)
+        bt = torch.from_numpy(perm.reshape(B, nblk)).to(dev)
+        lens_dev = [torch.from_numpy((base + i).astype(np.int32)).to(dev) for i in range(steps_total + 3)]
+
+    def lens_at(T):
+        return base + (T - T0)
     print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
     kp = torch.from_numpy(W.full_prefill(name, "k").view(np.int16)).view(torch.bfloat16).to(dev)
     vp = torch.from_numpy(W.full_prefill(name, "v").view(np.int16)).view(torch.bfloat16).to(dev)
@@ -355,7 +390,12 @@ def main():
     ws = torch.zeros(K.kvq_workspace_bytes(cfg, cap, a.kernel, a.splits), dtype=torch.uint8, device=dev)
     sm = 1.0 / math.sqrt(D)
     print(f"[bench] prefill T={T0}", file=sys.stderr, flush=True)
-    K.kvq_quantize_append(cfg, arena, 0, kp, vp, flags=K.CALIBRATE if calibrate else 0)
+    if a.paged:
+        zero = torch.zeros(B, dtype=torch.int32, device=dev)
+        K.kvq_paged_quantize_append(cfg, arena, bt, zero, kp, vp, lens_dev[0],
+                                    flags=K.INIT | (K.CALIBRATE if calibrate else 0))
+    else:
+        K.kvq_quantize_append(cfg, arena, 0, kp, vp, flags=K.CALIBRATE if calibrate else 0)
     del kp, vp
     torch.cuda.synchronize()
     T = T0
@@ -366,9 +406,21 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
+    def attend(arena_i, T):
+        """Decode attention over T tokens (paged: the lengths after T - T0 steps)."""
+        if a.paged:
+            K.kvq_paged_decode_attention(cfg, arena_i, bt, lens_dev[T - T0], int(lens_at(T).max()), q, out, sm, ws,
+                                         a.kernel, a.splits)
+        else:
+            K.kvq_decode_attention(cfg, arena_i, T, q, out, sm, ws, a.kernel, a.splits)
+
     def step(T):
         """One decode step: append the new token of every sequence at T, attend
         over T + 1 (kvq_decode_step: one launch unless a fold is due)."""
+        if n_new == 1 and a.paged:
+            K.kvq_paged_decode_step(cfg, arena, bt, lens_dev[T - T0], int(lens_at(T).max()) + 1, kn, vn, q, out, sm,
+                                    ws, a.kernel, a.splits)
+            return T + 1
         if n_new == 1:
             K.kvq_decode_step(cfg, arena, T, kn, vn, q, out, sm, ws, a.kernel, a.splits)
             return T + 1
@@ -396,10 +448,10 @@ def main():
     clocks = None
     while time.perf_counter() < spin_end or clocks is None:
         for i in range(10):
-            K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws, a.kernel, a.splits)
+            attend(arenas[i % copies], T)
         if clocks is None:
             for i in range(40):   # keep the GPU busy while rocm-smi samples it
-                K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws, a.kernel, a.splits)
+                attend(arenas[i % copies], T)
             clocks = gpu_clock_record()
         torch.cuda.synchronize()
     for _ in range(a.warmup + extra):
@@ -415,14 +467,12 @@ def main():
         ms_per_step = timed(one, a.steps)
         T = box[0]
     else:
-        ms_per_step = timed(lambda i: K.kvq_decode_attention(cfg, arenas[i % copies], T, q, out, sm, ws,
-                                                              a.kernel, a.splits), a.steps)
+        ms_per_step = timed(lambda i: attend(arenas[i % copies], T), a.steps)
     wall = time.perf_counter() - wall0
     if n_new:
         # decode attention alone (pass 1 + merge) at the final context, for the
         # roofline (the steps above also appended)
-        attn_us = 1000.0 * timed(lambda i: K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel,
-                                                                   a.splits), a.steps)
+        attn_us = 1000.0 * timed(lambda i: attend(arena, T), a.steps)
     else:
         attn_us = 1000.0 * ms_per_step
     fold_period = None
@@ -441,13 +491,13 @@ def main():
     warm_us = None
     if copies > 1:
         # the same launches on one arena only (cache-warm), reported separately
-        warm_us = 1000.0 * timed(lambda i: K.kvq_decode_attention(cfg, arena, T, q, out, sm, ws, a.kernel,
-                                                                   a.splits), a.steps)
+        warm_us = 1000.0 * timed(lambda i: attend(arena, T), a.steps)
     T_last = T_first + a.steps - 1 if n_new else T
     T_mid = (T_first + T_last) // 2
-    bytes_step, Tq = algorithmic_bytes(w, fmt, T_mid, meta_bytes)
+    rag = (lambda T: lens_at(T)) if a.paged else (lambda T: None)
+    bytes_step, Tq = algorithmic_bytes(w, fmt, T_mid, meta_bytes, lens=rag(T_mid))
     T_attn = T
-    bytes_attn = algorithmic_bytes(w, fmt, T_attn, meta_bytes)[0]
+    bytes_attn = algorithmic_bytes(w, fmt, T_attn, meta_bytes, lens=rag(T_attn))[0]
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     used_kernel = a.kernel
@@ -489,6 +539,9 @@ def main():
             "scale_zero_dtype": "f16" if a.meta_f16 else "f32",
             "untimed_positioning_steps": extra,
             "folds_in_timed_steps": len(folds_in_window),
+            "layout": (f"paged, {a.paged}-token pages in a shuffled order" if a.paged else "contiguous"),
+            "lengths": ("ragged " + f"{int(base.min())}..{int(base.max())} at the start" if a.ragged
+                        else "uniform"),
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 2),
         "attention_us": round(attn_us, 3),

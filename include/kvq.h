@@ -86,6 +86,8 @@ enum kvq_axis {      /* grouping axis of INT schemes (ignored for NONE / FP8)   
 enum kvq_dtype { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 };
 
 #define KVQ_CALIBRATE 1u     /* quantize_append flag: FP8 scales = absmax / 448   */
+#define KVQ_INIT      2u     /* paged append flag: this call starts the cache      */
+                             /* (writes the RoPE tables and the FP8 scales)        */
 
 typedef struct kvq_tensor_spec {
   int32_t scheme;  /* enum kvq_scheme                                            */
@@ -109,6 +111,10 @@ typedef struct kvq_config {
   float   rope_base;      /* RoPE base (theta_i = base^(-2i/D)) when pre_rope_k  */
   int32_t meta_dtype;     /* storage of the scale / zero-point of INT sides:     */
                           /* KVQ_F32 (0) or KVQ_F16 (1), see below               */
+  int32_t page_tokens;    /* P > 0: paged cache of num_pages pages of P tokens,  */
+                          /* addressed through block tables (see "Paged        */
+                          /* caches" below); 0: contiguous per sequence         */
+  int32_t num_pages;      /* pages in the pool (paged caches; 0 otherwise)       */
 } kvq_config;
 
 /*
@@ -131,6 +137,10 @@ typedef struct kvq_config {
  * sections are listed below in order, each starting at a 256-byte aligned
  * offset (SIZE_MAX when absent).  Shapes use Tc = token_capacity (max_tokens
  * rounded up to a multiple of 32 and of the per-channel group), H = Hkv.
+ * The token sections (codes and INT metadata) of a contiguous cache hold one
+ * page of Tc tokens per sequence; a paged cache (page_tokens = P > 0) holds
+ * num_pages pages of P tokens, so below [B][H][Tc] reads [num_pages][H][P]
+ * and token t of sequence b sits in page block_table[b][t / P] at t mod P.
  *
  *  k_codes  [B][H][Tc][D*bK/8]   token rows: channel c at bit bK*(c mod 8/bK)
  *                                of byte c*bK/8, low bits first; INT_SYM is
@@ -170,6 +180,9 @@ typedef struct kvq_layout {
   int32_t ring_slots;        /* Rs                                                */
   int32_t token_group;       /* Gt                                                */
   int32_t k_meta_cols, v_meta_cols;  /* innermost extent of the scale arrays     */
+  int64_t page_tokens;       /* tokens per page: P, or Tc for a contiguous cache  */
+  int32_t pages;             /* pages of the token sections: num_pages, or B      */
+  int32_t reserved;
 } kvq_layout;
 
 /* Validate a config (host only).  Returns KVQ_OK or KVQ_ERR_INVALID_ARG. */
@@ -185,7 +198,17 @@ int kvq_arena_bytes(const kvq_config* cfg, size_t* bytes);
 int64_t kvq_quantized_tokens(const kvq_config* cfg, int64_t T);
 
 /*
- * Append n_new tokens at positions [t0, t0 + n_new) of every sequence.
+ * Append n_new tokens at positions [t0, t0 + n_new) of every sequence: keys
+ * per channel over groups of tokens, values per token over groups of channels
+ * ("KV Cache Quantization: Why Keys and Values Need Different Axes", section
+ * "Why does per-token key quantization destroy accuracy?", whose
+ * quant_dequant listing gives the min-max encoding), symmetric INT8 as the
+ * qint8 listing of "FP8 KV Cache Quantization: Why Keys Break Before Values"
+ * (section "Why does the K cache break before the V cache?"), FP8 E4M3 with
+ * per-head scales and their failure modes as that page's section "Why do
+ * per-tensor scales waste bits on the K cache?" describes them, and the most
+ * recent tokens kept in fp16 and folded in blocks ("...Need Different Axes",
+ * section "What should I actually turn on in production?").
  *   k_new, v_new: device [B][Hkv][n_new][D] in cfg->in_dtype (values as
  *                 computed by the model: pre-RoPE keys when cfg->pre_rope_k).
  *   k_scale, v_scale: FP8 E4M3 only; device fp32 [Hkv] scales to store at
@@ -279,19 +302,107 @@ int kvq_decode_step_fused(const kvq_config* cfg, int64_t t0, const kvq_attn_opti
 
 /*
  * Dequantize the cache as stored (pre-RoPE keys stay unrotated) to fp32
- * [B][Hkv][T][D]: x_hat = code*scale + zero with two roundings (INT_ASYM),
+ * [B][Hkv][T][D], the dequantize halves of the listings cited at
+ * kvq_quantize_append: x_hat = code*scale + zero with two roundings (INT_ASYM),
  * code*scale (INT_SYM), E4M3(code)*scale (FP8), window tokens widened from
  * fp16.  Either output may be NULL.
  */
 int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T,
                    float* k_out, float* v_out, hipStream_t stream);
 
+/*
+ * Paged caches (page_tokens = P > 0).  The pages describe the paged,
+ * append-only caches of serving stacks, where per-channel key groups are
+ * formed within fixed-size blocks and the most recent tokens stay in full
+ * precision ("FP8 KV Cache Quantization: Why Keys Break Before Values",
+ * section "Should you quantize keys pre-RoPE or post-RoPE?"; "KV Cache
+ * Quantization: Why Keys and Values Need Different Axes", section "What
+ * should I actually turn on in production?": the window is folded in
+ * blocks).  A page holds P consecutive tokens of one sequence for all kv
+ * heads; P is a multiple of 32 and of the key group Gt, so a page holds whole
+ * key groups and whole 32-token value blocks and no group straddles pages.
+ * The fp16 window stays per sequence (ring_k / ring_v).  Whole-axis and
+ * per-tensor groups (which would rescale history on append) are refused.
+ *
+ * Common arguments:
+ *   block_table: device int32 [B][max_blocks]: page of tokens
+ *                [j*P, (j+1)*P) of sequence b at block_table[b*max_blocks + j].
+ *                Pages are owned by the caller, who hands each sequence the
+ *                pages its length needs (distinct sequences use distinct
+ *                pages).  An entry outside [0, num_pages) is never written
+ *                through (its tokens are skipped by appends) and reads as page
+ *                0 (that sequence's attention is then unspecified).
+ *   seq_lens:    device int32 [B]: tokens each sequence holds (before the call
+ *                for appends and decode steps; at the call for attention and
+ *                dequantize).  Sequences differ in length (ragged batches).
+ * Lengths are device data: a sequence whose range does not fit max_tokens
+ * or its block-table row is skipped by appends (its cache is left unchanged),
+ * and attention clamps lengths to [0, max_seq_len]; a sequence of length 0
+ * gets a zero output.
+ */
+
+/*
+ * Paged append: append new_lens[b] tokens (n_max if new_lens is NULL) at
+ * positions [seq_lens[b], seq_lens[b] + new_lens[b]) of each sequence b.
+ *   k_new, v_new: device [B][Hkv][n_max][D] in cfg->in_dtype; sequence b uses
+ *                 its first new_lens[b] tokens.
+ *   flags: KVQ_INIT on the call that starts the cache (every sequence empty):
+ *          it writes the RoPE tables and the FP8 scales (k_scale / v_scale if
+ *          given, absmax / 448 over the call's tokens of all sequences with
+ *          KVQ_CALIBRATE, else 1.0; E5M2 as in kvq_quantize_append).
+ * Per-channel key groups and per-token value groups are formed and packed in
+ * one pass (staged through fp16 when the cache has a window); tokens leaving
+ * the window are folded in blocks of Gt.  Bytes written equal those of
+ * kvq_quantize_append on a contiguous cache with the same tokens.
+ */
+int kvq_paged_quantize_append(const kvq_config* cfg, void* arena, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              const int32_t* new_lens, int32_t n_max, const void* k_new,
+                              const void* v_new, const float* k_scale, const float* v_scale,
+                              uint32_t flags, hipStream_t stream);
+
+/*
+ * Paged decode attention of one query per (sequence, query head) over the
+ * seq_lens[b] cached tokens of each sequence (as kvq_decode_attention).
+ * max_seq_len (host) bounds every seq_lens[b]; it sizes the split grid and
+ * the workspace (kvq_workspace_bytes(cfg, max_seq_len, opt)) and must satisfy
+ * max_seq_len <= max_tokens and max_seq_len <= max_blocks * P.
+ */
+int kvq_paged_decode_attention(const kvq_config* cfg, const void* arena,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seq_lens, int64_t max_seq_len, const void* q,
+                               void* out, float sm_scale, void* workspace,
+                               size_t workspace_bytes, const kvq_attn_options* opt,
+                               hipStream_t stream);
+
+/*
+ * Paged decode step: append one token per sequence at seq_lens[b] (k_new,
+ * v_new: [B][Hkv][1][D]) and attend over seq_lens[b] + 1 tokens; max_seq_len
+ * bounds seq_lens[b] + 1.  Equals kvq_paged_quantize_append followed by
+ * kvq_paged_decode_attention with the lengths plus one.  The caller advances
+ * its seq_lens afterwards.
+ */
+int kvq_paged_decode_step(const kvq_config* cfg, void* arena, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* seq_lens, int64_t max_seq_len,
+                          const void* k_new, const void* v_new, const void* q, void* out,
+                          float sm_scale, void* workspace, size_t workspace_bytes,
+                          const kvq_attn_options* opt, hipStream_t stream);
+
+/*
+ * Paged dequantize: sequence b's first seq_lens[b] tokens to fp32
+ * [B][Hkv][max_seq_len][D] (later rows are left as they are).
+ */
+int kvq_paged_dequantize(const kvq_config* cfg, const void* arena, const int32_t* block_table,
+                         int32_t max_blocks, const int32_t* seq_lens, int64_t max_seq_len,
+                         float* k_out, float* v_out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kvq_status_string(int status);
 
 /* ABI version: bumped when the arena layout or a signature changes, or an
  * entry point is added (2: kvq_decode_step; 3: kvq_config.meta_dtype;
- * 4: kvq_decode_attention_static). */
+ * 4: kvq_decode_attention_static; 5: paged caches, kvq_config.page_tokens /
+ * num_pages, kvq_layout.page_tokens / pages). */
 int kvq_abi_version(void);
 
 #ifdef __cplusplus

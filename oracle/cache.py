@@ -223,7 +223,8 @@ def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
     values stored little-endian.  codes [..., T, D] -> uint8 [..., T, D*b/8]."""
     u = _code_bytes_le(codes, bits)
     if bits >= 8:
-        return np.ascontiguousarray(u).view(np.uint8).reshape(*u.shape[:-1], -1)
+        # row width given explicitly so that zero tokens give a [..., 0, D*b/8] array
+        return np.ascontiguousarray(u).view(np.uint8).reshape(*u.shape[:-1], u.shape[-1] * (bits // 8))
     per = 8 // bits
     g = u.reshape(*u.shape[:-1], u.shape[-1] // per, per).astype(np.uint16)
     acc = np.zeros(g.shape[:-1], dtype=np.uint16)

@@ -31,6 +31,7 @@ NONE, INT_ASYM, INT_SYM, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 PER_TENSOR, PER_CHANNEL, PER_TOKEN = 0, 1, 2
 F32, F16, BF16 = 0, 1, 2
 CALIBRATE = 1
+INIT = 2            # paged appends: the call that starts the cache
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA = 0, 1, 2
 
 
@@ -43,7 +44,7 @@ class Config(C.Structure):
                 ("head_dim", C.c_int32), ("max_tokens", C.c_int64), ("in_dtype", C.c_int32),
                 ("out_dtype", C.c_int32), ("k", TensorSpec), ("v", TensorSpec),
                 ("residual", C.c_int32), ("pre_rope_k", C.c_int32), ("rope_base", C.c_float),
-                ("meta_dtype", C.c_int32)]
+                ("meta_dtype", C.c_int32), ("page_tokens", C.c_int32), ("num_pages", C.c_int32)]
 
 
 class Layout(C.Structure):
@@ -52,7 +53,8 @@ class Layout(C.Structure):
                                           "total_bytes")] + \
                [("token_capacity", C.c_int64), ("k_row_bytes", C.c_int32), ("v_block_bytes", C.c_int32),
                 ("ring_slots", C.c_int32), ("token_group", C.c_int32), ("k_meta_cols", C.c_int32),
-                ("v_meta_cols", C.c_int32)]
+                ("v_meta_cols", C.c_int32), ("page_tokens", C.c_int64), ("pages", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class AttnOptions(C.Structure):
@@ -75,6 +77,13 @@ _sig = {
                                   C.POINTER(AttnOptions), _P]),
     "kvq_decode_step_fused": (C.c_int, [_CFG, C.c_int64, C.POINTER(AttnOptions)]),
     "kvq_dequantize": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P]),
+    "kvq_paged_quantize_append": (C.c_int, [_CFG, _P, _P, C.c_int32, _P, _P, C.c_int32, _P, _P, _P, _P,
+                                            C.c_uint32, _P]),
+    "kvq_paged_decode_attention": (C.c_int, [_CFG, _P, _P, C.c_int32, _P, C.c_int64, _P, _P, C.c_float, _P,
+                                             C.c_size_t, C.POINTER(AttnOptions), _P]),
+    "kvq_paged_decode_step": (C.c_int, [_CFG, _P, _P, C.c_int32, _P, C.c_int64, _P, _P, _P, _P, C.c_float, _P,
+                                        C.c_size_t, C.POINTER(AttnOptions), _P]),
+    "kvq_paged_dequantize": (C.c_int, [_CFG, _P, _P, C.c_int32, _P, C.c_int64, _P, _P, _P]),
     "kvq_status_string": (C.c_char_p, [C.c_int]),
     "kvq_abi_version": (C.c_int, []),
 }
@@ -101,11 +110,13 @@ def _check(st: int, where: str) -> int:
 
 def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, k, v,
                 in_dtype=BF16, out_dtype=F32, residual=0, pre_rope_k=False,
-                rope_base=10000.0, meta_dtype=F32) -> Config:
+                rope_base=10000.0, meta_dtype=F32, page_tokens=0, num_pages=0) -> Config:
     """k, v: (scheme, bits, axis, group) tuples; meta_dtype: F32 or F16 storage
-    of the INT sides' scales and zero-points."""
+    of the INT sides' scales and zero-points; page_tokens > 0: a paged cache
+    of num_pages pages of page_tokens tokens."""
     return Config(batch, num_q_heads, num_kv_heads, head_dim, max_tokens, in_dtype, out_dtype,
-                  TensorSpec(*k), TensorSpec(*v), residual, int(bool(pre_rope_k)), rope_base, meta_dtype)
+                  TensorSpec(*k), TensorSpec(*v), residual, int(bool(pre_rope_k)), rope_base, meta_dtype,
+                  page_tokens, num_pages)
 
 
 def _ptr(t):
@@ -318,3 +329,84 @@ def kvq_dequantize(cfg: Config, arena, T: int, k_out=None, v_out=None, stream=No
 
 # raw entry points for tests that pass pointers directly
 raw = _lib
+
+
+# ---- paged caches ----------------------------------------------------------------
+
+def _check_paged_tables(cfg, block_table, seq_lens, new_lens=None):
+    _need(block_table, "block_table", dtype=torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != cfg.batch:
+        raise ValueError(f"block_table has shape {tuple(block_table.shape)}, expected ({cfg.batch}, max_blocks)")
+    _need(seq_lens, "seq_lens", dtype=torch.int32, shape=(cfg.batch,))
+    if new_lens is not None:
+        _need(new_lens, "new_lens", dtype=torch.int32, shape=(cfg.batch,))
+    return int(block_table.shape[1])
+
+
+def kvq_paged_quantize_append(cfg: Config, arena, block_table, seq_lens, k_new, v_new, new_lens=None,
+                              k_scale=None, v_scale=None, flags: int = 0, stream=None) -> None:
+    """Append to a paged cache: block_table int32 [B, max_blocks], seq_lens /
+    new_lens int32 [B] (device), k_new / v_new [B, Hkv, n_max, D]."""
+    _check_arena(cfg, arena)
+    max_blocks = _check_paged_tables(cfg, block_table, seq_lens, new_lens)
+    _check_new_tokens(cfg, k_new, v_new)
+    for nm, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if sc is not None:
+            _need(sc, nm, dtype=torch.float32, shape=(cfg.num_kv_heads,))
+    _on_gpu(arena=arena, block_table=block_table, seq_lens=seq_lens, new_lens=new_lens, k_new=k_new,
+            v_new=v_new, k_scale=k_scale, v_scale=v_scale)
+    st = _lib.kvq_paged_quantize_append(C.byref(cfg), _ptr(arena), _ptr(block_table), max_blocks, _ptr(seq_lens),
+                                        _ptr(new_lens), int(k_new.shape[2]), _ptr(k_new), _ptr(v_new),
+                                        _ptr(k_scale), _ptr(v_scale), flags, _stream(stream, arena, k_new))
+    _check(st, "kvq_paged_quantize_append")
+
+
+def kvq_paged_decode_attention(cfg: Config, arena, block_table, seq_lens, max_seq_len: int, q, out,
+                               sm_scale: float, workspace, kernel: int = 0, num_splits: int = 0,
+                               stream=None) -> None:
+    o = _opts(kernel, num_splits)
+    _check_arena(cfg, arena)
+    max_blocks = _check_paged_tables(cfg, block_table, seq_lens)
+    _check_query_out(cfg, q, out)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_gpu(arena=arena, block_table=block_table, seq_lens=seq_lens, q=q, out=out, workspace=workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.kvq_paged_decode_attention(C.byref(cfg), _ptr(arena), _ptr(block_table), max_blocks,
+                                         _ptr(seq_lens), max_seq_len, _ptr(q), _ptr(out), sm_scale,
+                                         _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
+    _check(st, "kvq_paged_decode_attention")
+
+
+def kvq_paged_decode_step(cfg: Config, arena, block_table, seq_lens, max_seq_len: int, k_new, v_new, q, out,
+                          sm_scale: float, workspace, kernel: int = 0, num_splits: int = 0,
+                          stream=None) -> None:
+    o = _opts(kernel, num_splits)
+    _check_arena(cfg, arena)
+    max_blocks = _check_paged_tables(cfg, block_table, seq_lens)
+    _check_new_tokens(cfg, k_new, v_new)
+    if k_new.shape[2] != 1:
+        raise ValueError(f"k_new has {k_new.shape[2]} tokens per sequence, a decode step appends 1")
+    _check_query_out(cfg, q, out)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_gpu(arena=arena, block_table=block_table, seq_lens=seq_lens, k_new=k_new, v_new=v_new, q=q, out=out,
+            workspace=workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.kvq_paged_decode_step(C.byref(cfg), _ptr(arena), _ptr(block_table), max_blocks, _ptr(seq_lens),
+                                    max_seq_len, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), sm_scale,
+                                    _ptr(workspace), ws_bytes, C.byref(o), _stream(stream, arena, q))
+    _check(st, "kvq_paged_decode_step")
+
+
+def kvq_paged_dequantize(cfg: Config, arena, block_table, seq_lens, max_seq_len: int, k_out=None, v_out=None,
+                         stream=None) -> None:
+    _check_arena(cfg, arena)
+    max_blocks = _check_paged_tables(cfg, block_table, seq_lens)
+    for nm, t in (("k_out", k_out), ("v_out", v_out)):
+        if t is not None:
+            _need(t, nm, dtype=torch.float32, shape=(cfg.batch, cfg.num_kv_heads, max_seq_len, cfg.head_dim))
+    _on_gpu(arena=arena, block_table=block_table, seq_lens=seq_lens, k_out=k_out, v_out=v_out)
+    st = _lib.kvq_paged_dequantize(C.byref(cfg), _ptr(arena), _ptr(block_table), max_blocks, _ptr(seq_lens),
+                                   max_seq_len, _ptr(k_out), _ptr(v_out), _stream(stream, arena))
+    _check(st, "kvq_paged_dequantize")

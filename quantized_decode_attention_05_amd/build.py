@@ -22,6 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 SOURCES = {
     "kvq_api.hip": [],
     "kvq_quant.hip": ["-ffp-contract=off"],
+    "kvq_append.hip": ["-ffp-contract=off"],
     "kvq_attn.hip": [],
     # keep MFMA accumulators in VGPRs (no AGPR <-> VGPR copies around the softmax rescale)
     "kvq_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -100,6 +100,9 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   const bool one_shot = spec_one_shot(cfg->k) || spec_one_shot(cfg->v);
   if (one_shot && (cfg->residual != 0 || Gt > 1)) return KVQ_ERR_INVALID_ARG;
   if (cfg->residual % Gt) return KVQ_ERR_INVALID_ARG;
+  if (cfg->page_tokens < 0 || cfg->num_pages < 0) return KVQ_ERR_INVALID_ARG;
+  const bool paged = cfg->page_tokens > 0;
+  if (!paged && cfg->num_pages != 0) return KVQ_ERR_INVALID_ARG;
 
   p->B = cfg->batch; p->Hq = cfg->num_q_heads; p->Hkv = cfg->num_kv_heads; p->D = D;
   p->n_rep = p->Hq / p->Hkv;
@@ -120,18 +123,47 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   p->v_block_bytes = kVBlock * D * p->v.bits / 8;
   p->v_nblk = p->Tc / kVBlock;
 
+  // the one-pass append kernel: key groups of up to 128 tokens (or none),
+  // value groups along channels, no whole-axis / per-tensor group
+  const auto fused_side = [&](const kvq_tensor_spec& sp, bool is_v) {
+    if (sp.scheme == KVQ_NONE || is_fp8(sp.scheme)) return true;
+    if (sp.axis == KVQ_PER_TOKEN) return true;
+    return !is_v && sp.axis == KVQ_PER_CHANNEL && sp.group > 0;
+  };
+  const bool fused_ok = !one_shot && fused_side(cfg->k, false) && fused_side(cfg->v, true) &&
+                        (Gt == 1 || (Gt % kVBlock == 0 && Gt <= 128));
+  p->unit = fused_ok ? (Gt > kVBlock ? Gt : kVBlock) : 0;
+
+  // token sections: pages of P tokens ([pages][H][P] token rows)
+  if (paged) {
+    const int P = cfg->page_tokens;
+    if (P % kVBlock || P % Gt || P > (1 << 20) || cfg->num_pages < 1) return KVQ_ERR_INVALID_ARG;
+    if (!fused_ok) return KVQ_ERR_INVALID_ARG;   // append-only groups within pages
+    p->paged = 1;
+    p->P = P;
+    p->pages = cfg->num_pages;
+  } else {
+    p->paged = 0;
+    p->P = p->Tc;
+    p->pages = p->B;
+  }
+  const uint64_t rows = (uint64_t)p->pages * p->Hkv * p->P;   // token rows of the token sections
+
   const uint64_t BH = (uint64_t)p->B * p->Hkv;
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) { uint64_t o = off; off = align256(off + bytes); return o; };
   const uint64_t NA = UINT64_MAX;
-  p->k.codes = take(BH * p->Tc * p->k_row_bytes);
+  p->k.codes = take(rows * p->k_row_bytes);
   auto meta_bytes = [&](const SideFmt& f) -> uint64_t {
+    const uint64_t esz = f.meta16 ? 2 : 4;
     if (is_fp8(f.scheme)) return (uint64_t)p->Hkv * 4;
-    return BH * f.meta_rows * f.meta_cols * (f.meta16 ? 2 : 4);
+    if (f.axis == KVQ_PER_CHANNEL && f.group > 0) return rows / f.group * f.meta_cols * esz;
+    if (f.axis == KVQ_PER_TOKEN) return rows * f.meta_cols * esz;
+    return BH * f.meta_rows * f.meta_cols * esz;    // one row per (sequence, head)
   };
   p->k.scale = (p->k.scheme == KVQ_NONE) ? NA : take(meta_bytes(p->k));
   p->k.zero = (p->k.scheme == KVQ_INT_ASYM) ? take(meta_bytes(p->k)) : NA;
-  p->v.codes = take(BH * p->v_nblk * p->v_block_bytes);
+  p->v.codes = take(rows / kVBlock * p->v_block_bytes);
   p->v.scale = (p->v.scheme == KVQ_NONE) ? NA : take(meta_bytes(p->v));
   p->v.zero = (p->v.scheme == KVQ_INT_ASYM) ? take(meta_bytes(p->v)) : NA;
   p->ring_k = p->window ? take(BH * p->Rs * D * 2) : NA;
@@ -195,7 +227,7 @@ using namespace kvq;
 
 extern "C" {
 
-int kvq_abi_version(void) { return 4; }
+int kvq_abi_version(void) { return 5; }
 
 const char* kvq_status_string(int s) {
   switch (s) {
@@ -234,6 +266,8 @@ int kvq_arena_layout(const kvq_config* cfg, kvq_layout* out) {
   out->token_group = p.Gt;
   out->k_meta_cols = p.k.meta_cols;
   out->v_meta_cols = p.v.meta_cols;
+  out->page_tokens = p.P;
+  out->pages = p.pages;
   return KVQ_OK;
 }
 
@@ -260,6 +294,7 @@ int kvq_quantize_append(const kvq_config* cfg, void* arena, int64_t t0, int32_t 
   Plan p;
   int st = make_plan(cfg, &p);
   if (st != KVQ_OK) return st;
+  if (p.paged) return KVQ_ERR_UNSUPPORTED;                // kvq_paged_quantize_append
   if (flags & ~KVQ_CALIBRATE) return KVQ_ERR_INVALID_ARG;
   if (t0 < 0 || n_new < 0) return KVQ_ERR_INVALID_ARG;
   if (t0 + n_new > p.max_tokens) return KVQ_ERR_CAPACITY;
@@ -289,10 +324,17 @@ int kvq_quantize_append(const kvq_config* cfg, void* arena, int64_t t0, int32_t 
       e = launch_fp8_setup(p, arena, k_new, v_new, n_new, k_scale, v_scale,
                            (flags & KVQ_CALIBRATE) != 0, stream);
   }
-  if (q_hi > q_lo && e == hipSuccess)
-    e = launch_quantize_range(p, arena, t0, n_new, q_lo, q_hi, k_new, v_new, stream);
-  if (T_new > w_lo && e == hipSuccess)
-    e = launch_ring_write(p, arena, t0, n_new, w_lo, k_new, v_new, stream);
+  if (p.unit) {
+    // one pass: quantized units and window slots in one launch
+    if ((q_hi > q_lo || T_new > w_lo) && e == hipSuccess)
+      e = launch_append_fused(p, arena, PageMap{nullptr, 0}, nullptr, nullptr, t0, n_new, p.max_tokens,
+                              k_new, v_new, stream);
+  } else {
+    if (q_hi > q_lo && e == hipSuccess)
+      e = launch_quantize_range(p, arena, t0, n_new, q_lo, q_hi, k_new, v_new, stream);
+    if (T_new > w_lo && e == hipSuccess)
+      e = launch_ring_write(p, arena, t0, n_new, w_lo, k_new, v_new, stream);
+  }
   if (e == hipSuccess) e = hipGetLastError();
   return hip_status(e, "kvq_quantize_append");
 }
@@ -317,6 +359,7 @@ int kvq_decode_attention(const kvq_config* cfg, const void* arena, int64_t T, co
   Plan p;
   int st = make_plan(cfg, &p);
   if (st != KVQ_OK) return st;
+  if (p.paged) return KVQ_ERR_UNSUPPORTED;                // the kvq_paged_ entry points
   if (T < 1 || T > p.max_tokens) return KVQ_ERR_CAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_ERR_INVALID_ARG;
   AttnPlan ap;
@@ -342,6 +385,7 @@ int kvq_decode_attention_static(const kvq_config* cfg, const void* arena, int64_
   Plan p;
   int st = make_plan(cfg, &p);
   if (st != KVQ_OK) return st;
+  if (p.paged) return KVQ_ERR_UNSUPPORTED;                // the kvq_paged_ entry points
   if (T < 1 || T > p.max_tokens) return KVQ_ERR_CAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_ERR_INVALID_ARG;
   AttnPlan ap;
@@ -377,6 +421,7 @@ int kvq_decode_step_fused(const kvq_config* cfg, int64_t t0, const kvq_attn_opti
   Plan p;
   int st = make_plan(cfg, &p);
   if (st != KVQ_OK) return st;
+  if (p.paged) return KVQ_ERR_UNSUPPORTED;                // the kvq_paged_ entry points
   if (t0 < 1) return KVQ_ERR_INVALID_ARG;
   if (t0 + 1 > p.max_tokens) return KVQ_ERR_CAPACITY;
   if (p.one_shot) return KVQ_ERR_UNSUPPORTED;
@@ -392,6 +437,7 @@ int kvq_decode_step(const kvq_config* cfg, void* arena, int64_t t0, const void* 
   Plan p;
   int st = make_plan(cfg, &p);
   if (st != KVQ_OK) return st;
+  if (p.paged) return KVQ_ERR_UNSUPPORTED;                // the kvq_paged_ entry points
   if (t0 < 1) return KVQ_ERR_INVALID_ARG;                 // a cache is started by quantize_append
   if (t0 + 1 > p.max_tokens) return KVQ_ERR_CAPACITY;
   if (p.one_shot) return KVQ_ERR_UNSUPPORTED;
@@ -428,6 +474,7 @@ int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T, float* k
   Plan p;
   int st = make_plan(cfg, &p);
   if (st != KVQ_OK) return st;
+  if (p.paged) return KVQ_ERR_UNSUPPORTED;                // the kvq_paged_ entry points
   if (T < 0 || T > p.max_tokens) return KVQ_ERR_CAPACITY;
   if (T == 0 || (!k_out && !v_out)) return KVQ_OK;
   if (!arena) return KVQ_ERR_NULL;
@@ -437,6 +484,140 @@ int kvq_dequantize(const kvq_config* cfg, const void* arena, int64_t T, float* k
   hipError_t e = launch_dequantize(p, arena, T, k_out, v_out, stream);
   if (e == hipSuccess) e = hipGetLastError();
   return hip_status(e, "kvq_dequantize");
+}
+
+// ---- paged caches --------------------------------------------------------------
+
+static int check_paged(const Plan& p, const int32_t* bt, int32_t max_blocks, const int32_t* lens) {
+  if (!p.paged) return KVQ_ERR_UNSUPPORTED;             // the contiguous entry points
+  if (!bt || !lens) return KVQ_ERR_NULL;
+  if (max_blocks < 1) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(bt, 4) || !aligned(lens, 4)) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+int kvq_paged_quantize_append(const kvq_config* cfg, void* arena, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* seq_lens, const int32_t* new_lens,
+                              int32_t n_max, const void* k_new, const void* v_new, const float* k_scale,
+                              const float* v_scale, uint32_t flags, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if ((st = check_paged(p, block_table, max_blocks, seq_lens)) != KVQ_OK) return st;
+  if (flags & ~(KVQ_CALIBRATE | KVQ_INIT)) return KVQ_ERR_INVALID_ARG;
+  if (n_max < 0 || (int64_t)n_max > p.max_tokens) return KVQ_ERR_INVALID_ARG;
+  const bool init = (flags & KVQ_INIT) != 0;
+  const bool fp8 = is_fp8(p.k.scheme) || is_fp8(p.v.scheme);
+  if ((flags & KVQ_CALIBRATE) && (!fp8 || !init)) return KVQ_ERR_INVALID_ARG;
+  if ((k_scale || v_scale) && (!fp8 || !init || (flags & KVQ_CALIBRATE))) return KVQ_ERR_INVALID_ARG;
+  if ((k_scale && p.k.scheme != KVQ_FP8_E4M3) || (v_scale && p.v.scheme != KVQ_FP8_E4M3))
+    return KVQ_ERR_INVALID_ARG;
+  if (!arena) return KVQ_ERR_NULL;
+  if (n_max > 0 && (!k_new || !v_new)) return KVQ_ERR_NULL;
+  if (!aligned(arena, 256) || (k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)) ||
+      (new_lens && !aligned(new_lens, 4)) || (k_scale && !aligned(k_scale, 4)) ||
+      (v_scale && !aligned(v_scale, 4)))
+    return KVQ_ERR_ALIGN;
+  int64_t cap = (int64_t)max_blocks * p.P;
+  if (cap > p.max_tokens) cap = p.max_tokens;
+  if (log_enabled())
+    fprintf(stderr, "[kvq] paged append n_max=%d init=%d cap=%lld\n", n_max, (int)init, (long long)cap);
+  (void)hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (init) {
+    if (p.pre_rope) e = launch_rope_tables(p, arena, stream);
+    if (fp8 && e == hipSuccess)
+      e = launch_fp8_setup(p, arena, k_new, v_new, n_max, k_scale, v_scale, (flags & KVQ_CALIBRATE) != 0,
+                           stream, new_lens ? new_lens : nullptr);
+  }
+  if (n_max > 0 && e == hipSuccess)
+    e = launch_append_fused(p, arena, PageMap{block_table, max_blocks}, seq_lens, new_lens, 0, n_max, cap,
+                            k_new, v_new, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  return hip_status(e, "kvq_paged_quantize_append");
+}
+
+static int paged_attention(const kvq_config* cfg, const void* arena, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* seq_lens, int64_t max_seq_len, int32_t lens_add,
+                           const void* q, void* out, float sm_scale, void* workspace, size_t workspace_bytes,
+                           const kvq_attn_options* opt, hipStream_t stream, const char* where) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if ((st = check_paged(p, block_table, max_blocks, seq_lens)) != KVQ_OK) return st;
+  if (max_seq_len < 1 || max_seq_len > p.max_tokens) return KVQ_ERR_CAPACITY;
+  if (max_seq_len > (int64_t)max_blocks * p.P) return KVQ_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_ERR_INVALID_ARG;
+  AttnPlan ap;
+  st = make_attn_plan(p, max_seq_len, opt, &ap);
+  if (st != KVQ_OK) return st;
+  if (!arena || !q || !out || (ap.workspace_bytes && !workspace)) return KVQ_ERR_NULL;
+  if (!aligned(arena, 256) || !aligned(q, 16) || !aligned(out, 16) ||
+      (workspace && !aligned(workspace, 256)))
+    return KVQ_ERR_ALIGN;
+  if (workspace_bytes < ap.workspace_bytes) return KVQ_ERR_WORKSPACE;
+  if (log_enabled())
+    fprintf(stderr, "[kvq] %s max_T=%lld kernel=%d splits=%d chunk=%lld\n", where, (long long)max_seq_len,
+            ap.kernel, ap.splits, (long long)ap.chunk);
+  (void)hipGetLastError();
+  const Ragged rg{PageMap{block_table, max_blocks}, seq_lens, lens_add};
+  hipError_t e = launch_attention(p, ap, arena, q, out, sm_scale, workspace, stream, nullptr, &rg);
+  if (e == hipSuccess) e = hipGetLastError();
+  return hip_status(e, where);
+}
+
+int kvq_paged_decode_attention(const kvq_config* cfg, const void* arena, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens, int64_t max_seq_len,
+                               const void* q, void* out, float sm_scale, void* workspace,
+                               size_t workspace_bytes, const kvq_attn_options* opt, hipStream_t stream) {
+  return paged_attention(cfg, arena, block_table, max_blocks, seq_lens, max_seq_len, 0, q, out, sm_scale,
+                         workspace, workspace_bytes, opt, stream, "kvq_paged_decode_attention");
+}
+
+int kvq_paged_decode_step(const kvq_config* cfg, void* arena, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, int64_t max_seq_len, const void* k_new, const void* v_new,
+                          const void* q, void* out, float sm_scale, void* workspace, size_t workspace_bytes,
+                          const kvq_attn_options* opt, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if ((st = check_paged(p, block_table, max_blocks, seq_lens)) != KVQ_OK) return st;
+  if (max_seq_len < 1 || max_seq_len > p.max_tokens) return KVQ_ERR_CAPACITY;
+  if (!k_new || !v_new || !q || !out) return KVQ_ERR_NULL;
+  // validate the attention half before anything is launched
+  AttnPlan ap;
+  st = make_attn_plan(p, max_seq_len, opt, &ap);
+  if (st != KVQ_OK) return st;
+  if (max_seq_len > (int64_t)max_blocks * p.P) return KVQ_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_ERR_INVALID_ARG;
+  if (ap.workspace_bytes && !workspace) return KVQ_ERR_NULL;
+  if (workspace_bytes < ap.workspace_bytes) return KVQ_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(out, 16) || (workspace && !aligned(workspace, 256))) return KVQ_ERR_ALIGN;
+  st = kvq_paged_quantize_append(cfg, arena, block_table, max_blocks, seq_lens, nullptr, 1, k_new, v_new,
+                                 nullptr, nullptr, 0, stream);
+  if (st != KVQ_OK) return st;
+  return paged_attention(cfg, arena, block_table, max_blocks, seq_lens, max_seq_len, 1, q, out, sm_scale,
+                         workspace, workspace_bytes, opt, stream, "kvq_paged_decode_step");
+}
+
+int kvq_paged_dequantize(const kvq_config* cfg, const void* arena, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int64_t max_seq_len, float* k_out, float* v_out,
+                         hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, &p);
+  if (st != KVQ_OK) return st;
+  if ((st = check_paged(p, block_table, max_blocks, seq_lens)) != KVQ_OK) return st;
+  if (max_seq_len < 0 || max_seq_len > p.max_tokens) return KVQ_ERR_CAPACITY;
+  if (max_seq_len > (int64_t)max_blocks * p.P) return KVQ_ERR_INVALID_ARG;
+  if (max_seq_len == 0 || (!k_out && !v_out)) return KVQ_OK;
+  if (!arena) return KVQ_ERR_NULL;
+  if (!aligned(arena, 256) || (k_out && !aligned(k_out, 16)) || (v_out && !aligned(v_out, 16)))
+    return KVQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  hipError_t e = launch_dequantize_paged(p, arena, PageMap{block_table, max_blocks}, seq_lens, max_seq_len,
+                                         k_out, v_out, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  return hip_status(e, "kvq_paged_dequantize");
 }
 
 }  // extern "C"

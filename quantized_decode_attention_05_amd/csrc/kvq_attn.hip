@@ -31,7 +31,22 @@ struct AttnArgs {
   int64_t T, Tq, chunk;
   int32_t S;
   float qscale;            // sm_scale * log2(e)
+  // ragged / paged calls: sequence b holds seq_lens[b] + lens_add tokens
+  // (clamped to [0, T]); tokens are read through the block table
+  PageMap pm;
+  const int32_t* seq_lens;
+  int32_t lens_add;
 };
+
+// Tokens of sequence b and how many of them are quantized.
+__device__ __forceinline__ void seq_extent(const Plan& p, const int32_t* seq_lens, int32_t lens_add, int b,
+                                           int64_t T_all, int64_t Tq_all, int64_t* T, int64_t* Tq) {
+  if (!seq_lens) { *T = T_all; *Tq = Tq_all; return; }
+  int64_t t = (int64_t)seq_lens[b] + lens_add;
+  t = t < 0 ? 0 : (t > T_all ? T_all : t);
+  *T = t;
+  *Tq = quantized_tokens(p, t);
+}
 
 // cos/sin of position * theta_i from the two-level table (fine: pos mod 32,
 // coarse: 32 * floor(pos / 32)), combined with the angle-addition formula.
@@ -52,9 +67,11 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int n_rep = p.n_rep;
+  int64_t T, Tq;
+  seq_extent(p, a.seq_lens, a.lens_add, b, a.T, a.Tq, &T, &Tq);
   const int64_t t_begin = (int64_t)split * a.chunk;
   int64_t t_end = t_begin + a.chunk;
-  if (t_end > a.T) t_end = a.T;
+  if (t_end > T) t_end = T;
 
   for (int e = tid; e < n_rep * D; e += 256) {
     const int r = e / D, c = e % D;
@@ -77,8 +94,8 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
       const int64_t t = t0 + tt;
       float k0 = 0.0f, k1 = 0.0f;
       if (t < t_end) {
-        k0 = dequant_elem<SIDE_K>(p, a.arena, b, kvh, t, 2 * pr, a.Tq);
-        k1 = dequant_elem<SIDE_K>(p, a.arena, b, kvh, t, 2 * pr + 1, a.Tq);
+        k0 = dequant_elem<SIDE_K>(p, a.arena, b, kvh, t, 2 * pr, Tq, a.pm);
+        k1 = dequant_elem<SIDE_K>(p, a.arena, b, kvh, t, 2 * pr + 1, Tq, a.pm);
         if (rtab) {
           const float2 cs = rope_cs(p, rtab, t, pr);
           const float r0 = k0 * cs.x - k1 * cs.y;
@@ -122,7 +139,7 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
     for (int e = tid; e < kTile * D; e += 256) {
       const int tt = e / D, c = e % D;
       const int64_t t = t0 + tt;
-      kv_s[tt][c] = (t < t_end) ? dequant_elem<SIDE_V>(p, a.arena, b, kvh, t, c, a.Tq) : 0.0f;
+      kv_s[tt][c] = (t < t_end) ? dequant_elem<SIDE_V>(p, a.arena, b, kvh, t, c, Tq, a.pm) : 0.0f;
     }
     __syncthreads();
     // 5. o = alpha * o + p . V
@@ -205,7 +222,8 @@ __global__ void __launch_bounds__(256) attn_merge(Plan p, const float* ws_o, con
   }
   __syncthreads();
   if (tid < p.D) {
-    const float v = (part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]) / L;
+    // a sequence with no tokens (ragged batches) has no mass: output 0
+    const float v = L > 0.0f ? (part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]) / L : 0.0f;
     const int64_t oi = row * p.D + tid;
     if (p.out_dtype == KVQ_F32) ((float*)out)[oi] = v;
     else if (p.out_dtype == KVQ_F16) ((_Float16*)out)[oi] = (_Float16)v;
@@ -243,6 +261,12 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
   }
   if (splits > max_splits) splits = (int)max_splits;
   if (splits < 1) splits = 1;
+  if (p.paged) {
+    // a split's page ids sit in the MFMA kernel's LDS (kMaxSplitPages entries)
+    // (a chunk of c tokens, rounded up to 64, spans at most c / P + 3 pages)
+    const int64_t need = cdiv(T, (int64_t)(kMaxSplitPages - 4) * p.P);
+    if (splits < need) splits = (int)need;
+  }
   // The workspace is sized for the target split count, which never decreases
   // with T; rounding the chunk to whole 64-token units can only lower the count.
   const int64_t target = splits;
@@ -261,19 +285,23 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
 }
 
 hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                                 float sm_scale, void* ws, hipStream_t s, const StepAppend* app);
+                                 float sm_scale, void* ws, hipStream_t s, const StepAppend* app,
+                                 const Ragged* rg);
 
 hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                            void* out, float sm_scale, void* ws, hipStream_t s, const StepAppend* app) {
+                            void* out, float sm_scale, void* ws, hipStream_t s, const StepAppend* app,
+                            const Ragged* rg) {
   if (app && app->mode != 0 && ap.kernel != 2) return hipErrorInvalidValue;   // MFMA kernel only
+  if (app && app->mode != 0 && rg) return hipErrorInvalidValue;               // contiguous only
   float* ws_o = (float*)((uint8_t*)ws + ap.ws_o);
   float* ws_ml = (float*)((uint8_t*)ws + ap.ws_ml);
   if (ap.kernel == 2) {
-    hipError_t e = launch_attention_mfma(p, ap, arena, q, sm_scale, ws, s, app);
+    hipError_t e = launch_attention_mfma(p, ap, arena, q, sm_scale, ws, s, app, rg);
     if (e != hipSuccess) return e;
   } else {
     AttnArgs a{(const uint8_t*)arena, q, ws_o, ws_ml, ap.T, ap.Tq, ap.chunk, ap.splits,
-               sm_scale * kLog2e};
+               sm_scale * kLog2e, rg ? rg->pm : PageMap{nullptr, 0}, rg ? rg->seq_lens : nullptr,
+               rg ? rg->lens_add : 0};
     dim3 grid(ap.splits, p.Hkv, p.B);
     if (p.D == 128) hipLaunchKernelGGL(attn_generic<128>, grid, dim3(256), 0, s, p, a);
     else hipLaunchKernelGGL(attn_generic<64>, grid, dim3(256), 0, s, p, a);

@@ -84,6 +84,11 @@ struct Args {
   int64_t t_new;
   int32_t app_mode;
   uint8_t* arena_w;   // the arena, writable (decode-step appends only)
+  // ragged / paged calls: sequence b holds seq_lens[b] + lens_add tokens
+  // (clamped to [0, T]), read through the block table
+  PageMap pm;
+  const int32_t* seq_lens;
+  int32_t lens_add;
 };
 
 __device__ __forceinline__ half8 pack8(u32 a, u32 b, u32 c, u32 d) {
@@ -454,7 +459,8 @@ attn_mfma(Plan p, Args a) {
   // table and the reduction scratch), at least 2, and enough to hold the
   // wavefront's O rows after the loop.
   constexpr int LDS_FIXED = QROWS * D * 4 + (ROPE ? 64 * 32 * 8 : 8) + kWaves * QROWS * 2 * 4;
-  constexpr int NB_FIT = (80 * 1024 - 512 - LDS_FIXED) / (kWaves * SLOT);
+  // (1.5 KB kept free: the page table of paged calls is dynamic LDS)
+  constexpr int NB_FIT = (80 * 1024 - 1536 - LDS_FIXED) / (kWaves * SLOT);
   constexpr int NB_DEF = SLOT <= 6144 ? 3 : 2;
   constexpr int NB_LDS = NB_FIT < NB_DEF ? (NB_FIT > 2 ? NB_FIT : 2) : NB_DEF;
   constexpr int NB_O = (QROWS * D * 4 + SLOT - 1) / SLOT;
@@ -470,6 +476,8 @@ attn_mfma(Plan p, Args a) {
   // the rings; after the streaming loop a wavefront's ring holds its O rows
   __shared__ __attribute__((aligned(16))) uint8_t ring_s[kWaves][NB * SLOT];
   __shared__ float red_ml[kWaves][QROWS][2];
+  // page ids of this split's token blocks (paged caches; dynamic LDS)
+  extern __shared__ int32_t page_s[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
@@ -478,6 +486,18 @@ attn_mfma(Plan p, Args a) {
   const int n_rep = p.n_rep;
   const int64_t bh = (int64_t)b * p.Hkv + kvh;
   const uint8_t* arena = a.arena;
+  // tokens of this sequence (ragged batches: from its length)
+  int64_t T = a.T, Tq = a.Tq;
+  if (a.seq_lens) {
+    int64_t tl = (int64_t)a.seq_lens[b] + a.lens_add;
+    tl = tl < 0 ? 0 : (tl > a.T ? a.T : tl);
+    T = tl;
+    Tq = quantized_tokens(p, tl);
+  }
+  const bool paged = a.pm.bt != nullptr;
+  const int64_t lo = (int64_t)split * a.chunk;
+  const int64_t hi = lo + a.chunk < T ? lo + a.chunk : T;
+  const int64_t blk0 = lo / p.P;          // first page-table block of this split
 
   // decode step: append the new token of this (sequence, kv head) first when
   // it falls in this split (threads 0..D-1 write its key, D..2D-1 its value),
@@ -511,6 +531,13 @@ attn_mfma(Plan p, Args a) {
     const int r = e / D, c = e % D;
     q_s[r][c] = load_in(a.q, ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c, p.in_dtype) * a.qscale;
   }
+  if (paged && hi > lo) {
+    const int64_t nblk = (hi - 1) / p.P - blk0 + 1;   // <= kMaxSplitPages (split count)
+    for (int64_t j = tid; j < nblk && j < kMaxSplitPages; j += 256) {
+      const int32_t pg = page_of(p, a.pm, b, (blk0 + j) * p.P);
+      page_s[j] = pg < 0 ? 0 : pg;
+    }
+  }
   if constexpr (ROPE) {
     const float2* tab = (const float2*)(arena + p.rope);
     for (int e = tid; e < 32 * 64; e += 256) {
@@ -521,10 +548,8 @@ attn_mfma(Plan p, Args a) {
   __syncthreads();
 
   // token range of this split and of this wavefront
-  const int64_t lo = (int64_t)split * a.chunk;
-  const int64_t hi = lo + a.chunk < a.T ? lo + a.chunk : a.T;
-  const int64_t q_end = hi < a.Tq ? hi : a.Tq;                 // quantized part [lo, q_end)
-  const int64_t w_beg = lo > a.Tq ? lo : a.Tq;                 // window part [w_beg, hi)
+  const int64_t q_end = hi < Tq ? hi : Tq;                     // quantized part [lo, q_end)
+  const int64_t w_beg = lo > Tq ? lo : Tq;                     // window part [w_beg, hi)
   const int64_t nq = q_end > lo ? (q_end - lo + 31) / 32 : 0;  // quantized steps
   const int64_t s_w0 = w_beg & ~(int64_t)31;
   const int64_t nw = hi > w_beg ? (hi - s_w0 + 31) / 32 : 0;   // window steps
@@ -616,12 +641,24 @@ attn_mfma(Plan p, Args a) {
   const bool vm16 = VINT && p.v.meta16, km16 = KINT && p.k.meta16;
   const int vesz = vm16 ? 2 : 4, kesz = km16 ? 2 : 4;
   auto init_ptrs = [&](int64_t t0, int64_t kgrp) __attribute__((always_inline)) {
-    pk = arena + p.k.codes + (bh * p.Tc + t0) * KROW + 16 * lane;
-    pv = arena + p.v.codes + (bh * p.v_nblk + (t0 >> 5)) * SZ_V + 16 * lane;
+    // token row of t0: through this split's page table, or (b, h)'s own rows
+    int64_t tr;
+    if (paged) {
+      // every issued step lies below the split's end, inside the table; the
+      // clamp only keeps set-up lookups of unused pointers inside the array
+      const int64_t j = t0 / p.P;
+      int64_t jj = j - blk0;
+      jj = jj < 0 ? 0 : (jj > kMaxSplitPages - 1 ? kMaxSplitPages - 1 : jj);
+      tr = ((int64_t)page_s[jj] * p.Hkv + kvh) * p.P + (t0 - j * p.P);
+    } else {
+      tr = bh * p.Tc + t0;
+    }
+    pk = arena + p.k.codes + tr * KROW + 16 * lane;
+    pv = arena + p.v.codes + (tr >> 5) * SZ_V + 16 * lane;
     if constexpr (VINT) {
       // 16-byte granules: 8*VG of scales, then 8*VG of zero-points
-      const uint8_t* vs = arena + p.v.scale + (bh * p.Tc + t0) * VG * vesz;
-      const uint8_t* vz = arena + p.v.zero + (bh * p.Tc + t0) * VG * vesz;
+      const uint8_t* vs = arena + p.v.scale + tr * VG * vesz;
+      const uint8_t* vz = arena + p.v.zero + tr * VG * vesz;
       if (vm16) {
         // 4*VG granules of each fp16 row
         if constexpr (VG == 8) {
@@ -641,7 +678,8 @@ attn_mfma(Plan p, Args a) {
     if constexpr (KINT) {
       // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key
       // group; fp16 rows: lanes 0-15 and 16-31
-      const int64_t mrow = (bh * p.k.meta_rows + kgrp) * D * kesz;
+      (void)kgrp;
+      const int64_t mrow = (tr / p.k.group) * D * kesz;
       if (km16) pkm = lane < 16 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 16);
       else pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * km_pos(lane)
                            : arena + p.k.zero + mrow + 16 * km_pos(lane - 32);
@@ -1015,7 +1053,8 @@ attn_mfma(Plan p, Args a) {
     const int64_t iss_end = lo + qs_end * 32;   // this wavefront's quantized steps only
     init_ptrs(i_grp * kG + i_rem, i_grp);
     auto next_issue = [&](int sl_) __attribute__((always_inline)) {
-      if (i_grp * kG + i_rem < iss_end) issue(sl_);
+      const int64_t pos = i_grp * kG + i_rem;
+      if (pos < iss_end) issue(sl_);
       if constexpr (IL) {
         i_grp += STRIDE;           // kG = 32: one step per group, i_rem stays 0
         advance_ptrs(true);
@@ -1024,6 +1063,11 @@ attn_mfma(Plan p, Args a) {
         const bool ends = i_rem == kG;
         if (ends) { i_rem = 0; ++i_grp; }
         advance_ptrs(ends);
+      }
+      // a paged cache continues on another page: pointers from the page table
+      if (paged) {
+        const int64_t nxt = i_grp * kG + i_rem;
+        if (nxt < iss_end && nxt / p.P != pos / p.P) init_ptrs(nxt, i_grp);
       }
     };
 #pragma unroll
@@ -1170,20 +1214,23 @@ bool mfma_supported(const Plan& p) {
   return p.n_rep == 8 && vgroups(p) == 4 && (kf == INT2 || kf == INT4) && (vf == INT2 || vf == INT4);
 }
 
+// dynamic LDS of a launch: the split's page table for paged calls
+static size_t page_lds(const Args& a) { return a.pm.bt ? kMaxSplitPages * sizeof(int32_t) : 0; }
+
 template <int KF, int VF, int VG>
 static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
   constexpr bool kPV2 = VG == 4 && (KF == INT2 || KF == INT4) && (VF == INT2 || VF == INT4);
   if constexpr (kPV2) {
     if (p.n_rep * VG > 16) {
-      if (p.pre_rope) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, true>), grid, dim3(256), 0, s, p, a);
-      else hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, true>), grid, dim3(256), 0, s, p, a);
+      if (p.pre_rope) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, true>), grid, dim3(256), page_lds(a), s, p, a);
+      else hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, true>), grid, dim3(256), page_lds(a), s, p, a);
       return;
     }
   }
   if (p.pre_rope) {
-    if constexpr (!is_f8(KF)) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, false>), grid, dim3(256), 0, s, p, a);
+    if constexpr (!is_f8(KF)) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, false>), grid, dim3(256), page_lds(a), s, p, a);
   } else {
-    hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, false>), grid, dim3(256), 0, s, p, a);
+    hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, false>), grid, dim3(256), page_lds(a), s, p, a);
   }
 }
 
@@ -1220,11 +1267,13 @@ static void launch_k(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
 }
 
 hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
-                                 float sm_scale, void* ws, hipStream_t s, const StepAppend* app) {
+                                 float sm_scale, void* ws, hipStream_t s, const StepAppend* app,
+                                 const Ragged* rg) {
   Args a{(const uint8_t*)arena, q, (float*)((uint8_t*)ws + ap.ws_o), (float*)((uint8_t*)ws + ap.ws_ml),
          ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e, -1.0f,
          app ? app->k : nullptr, app ? app->v : nullptr, app ? app->t : 0, app ? app->mode : 0,
-         (uint8_t*)arena};
+         (uint8_t*)arena, rg ? rg->pm : PageMap{nullptr, 0}, rg ? rg->seq_lens : nullptr,
+         rg ? rg->lens_add : 0};
   dim3 grid(ap.splits, p.Hkv, p.B);
   switch (kfmt(p)) {
     case INT2: launch_k<INT2>(p, grid, s, a); break;

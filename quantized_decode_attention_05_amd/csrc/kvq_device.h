@@ -37,16 +37,25 @@ __device__ __forceinline__ float src_val(const Plan& p, const Src& s, int b, int
   return p.window ? stage_f16(x) : x;
 }
 
-__device__ __forceinline__ int64_t meta_index(const Plan& p, const SideFmt& f, int b, int h,
-                                              int64_t t, int c) {
-  const int64_t bh = (int64_t)b * p.Hkv + h;
+// Index of the scale / zero-point of channel c of the token in token row tr
+// (row_of) of sequence-head bh = b * Hkv + h.  Per-tensor and whole-axis
+// groups exist only in contiguous caches: one entry / row per (b, h).
+__device__ __forceinline__ int64_t meta_index_row(const Plan& p, const SideFmt& f, int64_t bh, int h,
+                                                  int64_t tr, int c) {
   if (is_fp8(f.scheme)) return h;
   if (f.axis == KVQ_PER_TENSOR) return bh;
   if (f.axis == KVQ_PER_CHANNEL) {
-    const int64_t g = f.group ? t / f.group : 0;
-    return (bh * f.meta_rows + g) * p.D + c;
+    if (f.group) return (tr / f.group) * p.D + c;
+    return bh * p.D + c;
   }
-  return (bh * p.Tc + t) * f.meta_cols + c / f.group;
+  return tr * f.meta_cols + c / f.group;
+}
+
+// The same for token t of a contiguous cache (token row bh * Tc + t).
+__device__ __forceinline__ int64_t meta_index(const Plan& p, const SideFmt& f, int b, int h,
+                                              int64_t t, int c) {
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  return meta_index_row(p, f, bh, h, bh * p.Tc + t, c);
 }
 
 // ---- fp16 scale / zero-point metadata ----------------------------------------
@@ -128,11 +137,55 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return code | sign;
 }
 
+// Scale and zero-point a group with minimum mn and maximum mx (for symmetric
+// groups mx holds the absmax) is stored with, as the fp32 values that codes
+// and dequantization use: fp32 metadata keeps them as computed; fp16 metadata
+// rounds the zero-point down and the scale up (and the symmetric scale up) so
+// the stored grid still spans the group.
+__device__ __forceinline__ void meta_values(const SideFmt& f, float mn, float mx, float* s, float* z) {
+  if (f.scheme == KVQ_INT_ASYM) {
+    if (f.meta16) {
+      const _Float16 zh = f16_directed(mn, false);
+      float sc;
+      asym_params((float)zh, mx, f.bits, &sc);
+      *s = (float)f16_directed(sc, true);
+      *z = (float)zh;
+    } else {
+      asym_params(mn, mx, f.bits, s);
+      *z = mn;
+    }
+  } else {
+    const float sc = fmaxf(mx, 1e-8f) / 127.0f;
+    *s = f.meta16 ? (float)f16_directed(sc, true) : sc;
+    *z = 0.0f;
+  }
+}
+
+// Store the values meta_values gives (exact in the storage type) at index mi.
+__device__ __forceinline__ void store_meta_values(const SideFmt& f, uint8_t* arena, int64_t mi, float s,
+                                                  float z) {
+  if (f.meta16) {
+    ((_Float16*)(arena + f.scale))[mi] = (_Float16)s;
+    if (f.scheme == KVQ_INT_ASYM) ((_Float16*)(arena + f.zero))[mi] = (_Float16)z;
+  } else {
+    ((float*)(arena + f.scale))[mi] = s;
+    if (f.scheme == KVQ_INT_ASYM) ((float*)(arena + f.zero))[mi] = z;
+  }
+}
+
+__device__ __forceinline__ void store_meta(const Plan& p, const SideFmt& f, uint8_t* arena,
+                                           int64_t mi, float mn, float mx) {
+  (void)p;
+  float s, z;
+  meta_values(f, mn, mx, &s, &z);
+  store_meta_values(f, arena, mi, s, z);
+}
+
 // Dequantized value of (t, c) as stored: window tokens from the fp16 ring.
 
 template <int SIDE>
 __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* arena, int b, int h,
-                                              int64_t t, int c, int64_t Tq) {
+                                              int64_t t, int c, int64_t Tq, const PageMap& pm = PageMap{nullptr, 0}) {
   const SideFmt& f = SIDE == SIDE_K ? p.k : p.v;
   const int64_t bh = (int64_t)b * p.Hkv + h;
   if (t >= Tq) {
@@ -140,16 +193,16 @@ __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* aren
     if (SIDE == SIDE_K) return (float)((const _Float16*)(arena + p.ring_k))[(bh * p.Rs + slot) * p.D + c];
     return ring_v_elem(p, arena, bh, slot, c);
   }
+  const int64_t tr = read_row(p, pm, b, h, t);
   uint32_t code;
   if (SIDE == SIDE_K) {
-    const uint8_t* row = arena + f.codes + (bh * p.Tc + t) * p.k_row_bytes;
+    const uint8_t* row = arena + f.codes + tr * p.k_row_bytes;
     const int bit = c * f.bits;
     if (f.bits == 32) code = ((const uint32_t*)row)[c];
     else if (f.bits == 16) code = ((const uint16_t*)row)[c];
     else code = (row[bit >> 3] >> (bit & 7)) & ((1u << f.bits) - 1);
   } else {
-    const uint8_t* wp = arena + f.codes + bh * p.v_nblk * p.v_block_bytes +
-                        vblock_word_byte(t, c, p.D, f.bits, p.v_block_bytes);
+    const uint8_t* wp = arena + f.codes + vblock_word_byte(tr, c, p.D, f.bits, p.v_block_bytes);
     const int k = (int)(t & 7), bit = k * f.bits;
     if (f.bits == 32) code = ((const uint32_t*)wp)[k];
     else if (f.bits == 16) code = ((const uint16_t*)wp)[k];
@@ -159,7 +212,7 @@ __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* aren
     if (f.bits == 16) return (float)__builtin_bit_cast(_Float16, (uint16_t)code);
     return __uint_as_float(code);
   }
-  const int64_t mi = meta_index(p, f, b, h, t, c);
+  const int64_t mi = meta_index_row(p, f, bh, h, tr, c);
   const float s = load_meta(arena + f.scale, mi, f.meta16);
   if (f.scheme == KVQ_FP8_E4M3) return e4m3_decode(code) * s;
   if (f.scheme == KVQ_FP8_E5M2) return e5m2_decode(code) * s;

@@ -45,16 +45,52 @@ struct Plan {
   SideFmt k, v;
   uint64_t ring_k, ring_v, rope, fp8_calib, total;
   int64_t rope_rows;      // coarse rope rows (Tc/32 + 1)
+  // token sections: `pages` pages of P tokens per kv head ([pages][H][P] token
+  // rows); a contiguous cache is one page of Tc tokens per sequence
+  int32_t paged;          // block tables (page_tokens > 0)
+  int64_t P;              // tokens per page (Tc when contiguous)
+  int32_t pages;          // pages of the token sections (B when contiguous)
+  int32_t unit;           // tokens per work-group of the one-pass append kernel
+                          // (max(Gt, 32)); 0 when that kernel does not serve the format
+};
+
+// Block table of a paged call (bt == nullptr: contiguous cache).
+struct PageMap {
+  const int32_t* bt;      // [B][max_blocks]
+  int32_t max_blocks;
 };
 
 // Builds the plan; returns KVQ_OK or an error status.
 int make_plan(const kvq_config* cfg, Plan* p);
 
-inline int64_t quantized_tokens(const Plan& p, int64_t T) {
+__host__ __device__ inline int64_t quantized_tokens(const Plan& p, int64_t T) {
   if (p.one_shot) return T;
   int64_t r = T - p.R;
   if (r < 0) r = 0;
   return (int64_t)p.Gt * (r / p.Gt);
+}
+
+// Page holding token t of sequence b (b itself for a contiguous cache); -1
+// when the block-table entry is past the row or outside the pool.
+__device__ __forceinline__ int32_t page_of(const Plan& p, const PageMap& m, int b, int64_t t) {
+  if (!m.bt) return b;
+  const int64_t j = t / p.P;
+  if (j >= m.max_blocks) return -1;
+  const int32_t pg = m.bt[(int64_t)b * m.max_blocks + j];
+  return (pg >= 0 && pg < p.pages) ? pg : -1;
+}
+
+// Token row of token t of kv head h in page `page`: the index of its row in
+// the [pages][H][P] token sections.
+__device__ __forceinline__ int64_t row_of(const Plan& p, int32_t page, int h, int64_t t) {
+  const int64_t tt = p.paged ? t - (t / p.P) * p.P : t;
+  return ((int64_t)page * p.Hkv + h) * p.P + tt;
+}
+
+// Token row of (b, h, t) for reads: an entry outside the pool reads page 0.
+__device__ __forceinline__ int64_t read_row(const Plan& p, const PageMap& m, int b, int h, int64_t t) {
+  const int32_t pg = page_of(p, m, b, t);
+  return row_of(p, pg < 0 ? 0 : pg, h, t);
 }
 
 // ---- device helpers shared by the kernels ----------------------------------

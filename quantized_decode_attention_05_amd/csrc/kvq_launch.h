@@ -5,6 +5,9 @@
 
 namespace kvq {
 
+// Page ids of one token split that the MFMA kernel keeps in LDS (paged caches).
+constexpr int kMaxSplitPages = 256;
+
 // Plan of one decode-attention call.
 struct AttnPlan {
   int32_t kernel;          // 1 generic, 2 MFMA
@@ -32,15 +35,38 @@ bool mfma_supported(const Plan& p);
 hipError_t launch_rope_tables(const Plan& p, void* arena, hipStream_t s);
 hipError_t launch_fp8_setup(const Plan& p, void* arena, const void* k_new, const void* v_new,
                             int n_new, const float* k_scale, const float* v_scale, bool calibrate,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* new_lens = nullptr);
 hipError_t launch_quantize_range(const Plan& p, void* arena, int64_t t0, int n_new, int64_t q_lo,
                                  int64_t q_hi, const void* k_new, const void* v_new, hipStream_t s);
 hipError_t launch_ring_write(const Plan& p, void* arena, int64_t t0, int n_new, int64_t w_lo,
                              const void* k_new, const void* v_new, hipStream_t s);
 hipError_t launch_dequantize(const Plan& p, const void* arena, int64_t T, float* k_out,
                              float* v_out, hipStream_t s);
+// Per-sequence lengths of a ragged (paged) attention call: sequence b holds
+// seq_lens[b] + lens_add tokens, clamped to [0, AttnPlan::T].
+struct Ragged {
+  PageMap pm;
+  const int32_t* seq_lens;
+  int32_t lens_add;
+};
+
 hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena, const void* q,
                             void* out, float sm_scale, void* ws, hipStream_t s,
-                            const StepAppend* app = nullptr);
+                            const StepAppend* app = nullptr, const Ragged* rg = nullptr);
+
+// One-pass append (kvq_append.hip): tokens [t0_b, t0_b + n_b) of every
+// sequence, t0_b = seq_lens[b] (t0 when seq_lens is null), n_b = new_lens[b]
+// (n when null); quantized units and window slots in one launch.
+bool append_fused_supported(const Plan& p);
+hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, const int32_t* seq_lens,
+                               const int32_t* new_lens, int64_t t0, int n, int64_t cap, const void* k_new,
+                               const void* v_new, hipStream_t s);
+hipError_t launch_fp8_absmax_lens(const Plan& p, const void* k_new, const void* v_new, int n,
+                                  const int32_t* new_lens, uint32_t* amax, hipStream_t s);
+hipError_t launch_fp8_finalize(const Plan& p, void* arena, const float* k_scale, const float* v_scale,
+                               bool calibrate, hipStream_t s);
+hipError_t launch_dequantize_paged(const Plan& p, const void* arena, const PageMap& pm,
+                                   const int32_t* seq_lens, int64_t max_T, float* k_out, float* v_out,
+                                   hipStream_t s);
 
 }  // namespace kvq

@@ -39,29 +39,6 @@ __device__ __forceinline__ uint32_t encode_elem(const Plan& p, const SideFmt& f,
 
 // ---- reductions (scale / zero per group) -------------------------------------
 
-__device__ __forceinline__ void store_meta(const Plan& p, const SideFmt& f, uint8_t* arena,
-                                           int64_t mi, float mn, float mx) {
-  if (f.meta16) {
-    // fp16 storage that still spans the group: zero rounded down, scale up
-    if (f.scheme == KVQ_INT_ASYM) {
-      const _Float16 z = f16_directed(mn, false);
-      float s;
-      asym_params((float)z, mx, f.bits, &s);
-      ((_Float16*)(arena + f.scale))[mi] = f16_directed(s, true);
-      ((_Float16*)(arena + f.zero))[mi] = z;
-    } else {
-      ((_Float16*)(arena + f.scale))[mi] = f16_directed(fmaxf(mx, 1e-8f) / 127.0f, true);
-    }
-  } else if (f.scheme == KVQ_INT_ASYM) {
-    float s;
-    asym_params(mn, mx, f.bits, &s);
-    ((float*)(arena + f.scale))[mi] = s;
-    ((float*)(arena + f.zero))[mi] = mn;
-  } else {  // symmetric: mx holds the absmax
-    ((float*)(arena + f.scale))[mi] = fmaxf(mx, 1e-8f) / 127.0f;
-  }
-}
-
 // Per-channel groups: one block per (group, head, sequence), one thread per
 // channel looping over the group's tokens (loads coalesce across channels).
 template <int SIDE>
@@ -352,21 +329,31 @@ hipError_t launch_rope_tables(const Plan& p, void* arena, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_fp8_finalize(const Plan& p, void* arena, const float* k_scale, const float* v_scale,
+                               bool calibrate, hipStream_t s) {
+  uint32_t* amax = (uint32_t*)((uint8_t*)arena + p.fp8_calib);
+  hipLaunchKernelGGL(fp8_finalize, dim3(1), dim3(64 * ((p.Hkv + 63) / 64)), 0, s, p, (uint8_t*)arena,
+                     (const uint32_t*)amax, k_scale, v_scale, calibrate ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_fp8_setup(const Plan& p, void* arena, const void* k_new, const void* v_new,
                             int n_new, const float* k_scale, const float* v_scale, bool calibrate,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t* new_lens) {
   uint32_t* amax = (uint32_t*)((uint8_t*)arena + p.fp8_calib);
   if (calibrate) {
-    hipLaunchKernelGGL(fp8_zero, dim3(1), dim3(64), 0, s, amax, 2 * p.Hkv);
-    const int64_t nel = (int64_t)p.B * n_new * p.D;
-    unsigned chunks = grid_for(nel, 256);
-    if (chunks > 512) chunks = 512;
-    hipLaunchKernelGGL(fp8_absmax, dim3(chunks, p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+    hipLaunchKernelGGL(fp8_zero, dim3(1), dim3(64 * ((2 * p.Hkv + 63) / 64)), 0, s, amax, 2 * p.Hkv);
+    if (new_lens) {
+      const hipError_t e = launch_fp8_absmax_lens(p, k_new, v_new, n_new, new_lens, amax, s);
+      if (e != hipSuccess) return e;
+    } else {
+      const int64_t nel = (int64_t)p.B * n_new * p.D;
+      unsigned chunks = grid_for(nel, 256);
+      if (chunks > 512) chunks = 512;
+      hipLaunchKernelGGL(fp8_absmax, dim3(chunks, p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+    }
   }
-  const int mode = calibrate ? 1 : 0;
-  hipLaunchKernelGGL(fp8_finalize, dim3(1), dim3(64 * ((p.Hkv + 63) / 64)), 0, s, p, (uint8_t*)arena,
-                     amax, k_scale, v_scale, mode);
-  return hipGetLastError();
+  return launch_fp8_finalize(p, arena, k_scale, v_scale, calibrate, s);
 }
 
 template <int SIDE>
@@ -410,6 +397,36 @@ hipError_t launch_ring_write(const Plan& p, void* arena, int64_t t0, int n_new, 
   const int64_t w_len = t0 + n_new - w_lo;
   const int64_t total = (int64_t)p.B * p.Hkv * w_len * p.D;
   hipLaunchKernelGGL(write_ring_kv, dim3(grid_for(2 * total, 256)), dim3(256), 0, s, p, sk, v_new, w_lo, w_len);
+  return hipGetLastError();
+}
+
+// Paged / ragged: sequence b's first seq_lens[b] tokens (clamped to max_T)
+// into rows [0, seq_lens[b]) of [B][Hkv][max_T][D]; later rows untouched.
+__global__ void dequantize_paged(Plan p, const uint8_t* arena, PageMap pm, const int32_t* seq_lens,
+                                 int64_t max_T, float* kout, float* vout) {
+  const int64_t total = (int64_t)p.B * p.Hkv * max_T * p.D;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % p.D);
+    int64_t r = i / p.D;
+    const int64_t t = r % max_T;
+    r /= max_T;
+    const int h = (int)(r % p.Hkv), b = (int)(r / p.Hkv);
+    int64_t Tb = seq_lens[b];
+    if (Tb > max_T) Tb = max_T;
+    if (t >= Tb) continue;
+    const int64_t Tq = quantized_tokens(p, Tb);
+    if (kout) kout[i] = dequant_elem<SIDE_K>(p, arena, b, h, t, c, Tq, pm);
+    if (vout) vout[i] = dequant_elem<SIDE_V>(p, arena, b, h, t, c, Tq, pm);
+  }
+}
+
+hipError_t launch_dequantize_paged(const Plan& p, const void* arena, const PageMap& pm,
+                                   const int32_t* seq_lens, int64_t max_T, float* k_out, float* v_out,
+                                   hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.Hkv * max_T * p.D;
+  hipLaunchKernelGGL(dequantize_paged, dim3(grid_for(total, 256)), dim3(256), 0, s, p, (const uint8_t*)arena,
+                     pm, seq_lens, max_T, k_out, v_out);
   return hipGetLastError();
 }
 

@@ -224,3 +224,144 @@ def payload_of(values_f32: np.ndarray, dtype: str) -> np.ndarray:
     u = np.ascontiguousarray(values_f32, dtype=np.float32).view(np.uint32)
     assert np.all((u & 0xFFFF) == 0)
     return (u >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# paged caches
+# ---------------------------------------------------------------------------
+
+class PagedCache:
+    """A paged cache on cuda:0: a pool of pages, a block table with pages
+    handed out in a shuffled order, and per-sequence lengths (ragged)."""
+
+    def __init__(self, case: Case, P: int, cap: int, seed: int = 0, spare_pages: int = 3, fill: int = 0x5A):
+        from oracle import paged as OP
+        self.case, self.P, self.cap = case, P, cap
+        self.max_blocks = OP.blocks_of(cap, P)
+        self.pages = case.B * self.max_blocks + spare_pages
+        self.cfg = K.make_config(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv, head_dim=case.D,
+                                 max_tokens=cap, k=case.k, v=case.v, in_dtype=_DT[case.dtype][0],
+                                 out_dtype=K.F32, residual=case.R, pre_rope_k=case.pre_rope,
+                                 rope_base=case.rope_base, meta_dtype=K.F16 if case.meta16 else K.F32,
+                                 page_tokens=P, num_pages=self.pages)
+        self.layout = K.kvq_arena_layout(self.cfg)
+        self.arena = torch.full((self.layout.total_bytes,), fill, dtype=torch.uint8, device="cuda")
+        perm = np.random.default_rng((seed, 91)).permutation(self.pages)[:case.B * self.max_blocks]
+        self.block_table = perm.reshape(case.B, self.max_blocks).astype(np.int32)
+        self.bt = torch.from_numpy(self.block_table).cuda()
+        self.lens = np.zeros(case.B, dtype=np.int64)
+        self.seq_lens = torch.zeros(case.B, dtype=torch.int32, device="cuda")
+
+    def _sync_lens(self):
+        self.seq_lens.copy_(torch.from_numpy(self.lens.astype(np.int32)))
+
+    def append(self, k_payload, v_payload, new_lens, flags=0, k_scale=None, v_scale=None):
+        """k_payload, v_payload: [B, Hkv, n_max, D] device-dtype payloads; sequence
+        b appends its first new_lens[b] rows."""
+        kd, vd = to_dev(k_payload, self.case.dtype), to_dev(v_payload, self.case.dtype)
+        nl = torch.from_numpy(np.asarray(new_lens, dtype=np.int32)).cuda()
+        ks = None if k_scale is None else torch.as_tensor(k_scale, dtype=torch.float32).cuda()
+        vs = None if v_scale is None else torch.as_tensor(v_scale, dtype=torch.float32).cuda()
+        K.kvq_paged_quantize_append(self.cfg, self.arena, self.bt, self.seq_lens, kd, vd, nl, ks, vs, flags)
+        self.lens += np.asarray(new_lens, dtype=np.int64)
+        self._sync_lens()
+
+    def step(self, k_payload, v_payload, q_payload, ws, out, sm=None, kernel=0, num_splits=0):
+        """kvq_paged_decode_step: one token per sequence, attention over lens + 1."""
+        c = self.case
+        sm = 1.0 / math.sqrt(c.D) if sm is None else sm
+        K.kvq_paged_decode_step(self.cfg, self.arena, self.bt, self.seq_lens, int(self.lens.max()) + 1,
+                                to_dev(k_payload, c.dtype), to_dev(v_payload, c.dtype), to_dev(q_payload, c.dtype),
+                                out, sm, ws, kernel, num_splits)
+        self.lens += 1
+        self._sync_lens()
+
+    def attention(self, q_payload, kernel=0, num_splits=0, sm_scale=None):
+        c = self.case
+        maxT = int(self.lens.max())
+        q = to_dev(q_payload, c.dtype)
+        out = torch.full((c.B, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(K.kvq_workspace_bytes(self.cfg, maxT, kernel, num_splits), dtype=torch.uint8,
+                         device="cuda")
+        sm = 1.0 / math.sqrt(c.D) if sm_scale is None else sm_scale
+        K.kvq_paged_decode_attention(self.cfg, self.arena, self.bt, self.seq_lens, maxT, q, out, sm, ws, kernel,
+                                     num_splits)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.isfinite(o).all(), f"paged attention output not finite kernel={kernel} splits={num_splits}"
+        return o
+
+    def dequantize(self):
+        c = self.case
+        maxT = int(self.lens.max())
+        ko = torch.full((c.B, c.Hkv, maxT, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        vo = torch.full_like(ko, float("nan"))
+        K.kvq_paged_dequantize(self.cfg, self.arena, self.bt, self.seq_lens, maxT, ko, vo)
+        torch.cuda.synchronize()
+        return ko.cpu().numpy(), vo.cpu().numpy()
+
+    def section(self, name, per_page_shape, dtype):
+        """A token section as [pages][H][*per_page_shape] (host copy)."""
+        off = getattr(self.layout, name)
+        n = self.pages * self.case.Hkv * int(np.prod(per_page_shape)) * np.dtype(dtype).itemsize
+        return self.arena[off: off + n].cpu().numpy().view(dtype).reshape(
+            (self.pages, self.case.Hkv) + tuple(per_page_shape))
+
+
+def compare_paged_sequence(pc: PagedCache, b: int, st: dict, fp8_scales=None):
+    """Bit-exact comparison of sequence b of a paged cache with the oracle state
+    st of that sequence alone (B = 1): the pages of each token section are
+    gathered into the contiguous order (oracle.paged) and compared as
+    compare_sections does; window slots from the sequence's ring."""
+    from oracle import paged as OP
+    c, lay, P = pc.case, pc.layout, pc.P
+    H, D = c.Hkv, c.D
+    Tq, T = st["Tq"], st["T"]
+    bt = pc.block_table
+
+    def gathered(name, per_page_shape, dtype, count):
+        sec = pc.section(name, per_page_shape, dtype)
+        return OP.gather_pages(sec, bt, b, P, T)[:, :count]
+
+    bits_k = OC.code_bits(OC.Spec(*c.k))
+    rows = gathered("k_codes", (P, lay.k_row_bytes), np.uint8, Tq)
+    assert np.array_equal(rows, OC.pack_rows(st["k"]["codes"][0], bits_k)), f"seq {b}: K code rows differ"
+    bits_v = OC.code_bits(OC.Spec(*c.v))
+    vb = gathered("v_codes", (P // 32, lay.v_block_bytes), np.uint8, -(-Tq // 32))
+    got_v = OC.unpack_vblocks(vb, bits_v, D, Tq)
+    exp_v = OC.unpack_vblocks(OC.pack_vblocks(st["v"]["codes"][0], bits_v), bits_v, D, Tq)
+    assert np.array_equal(got_v, exp_v), f"seq {b}: V code blocks differ"
+    for side, spec in (("k", c.k), ("v", c.v)):
+        part = st[side]
+        if spec[0] in (OC.FP8_E4M3, OC.FP8_E5M2):
+            off = getattr(lay, side + "_scale")
+            s = pc.arena[off: off + 4 * H].cpu().numpy().view(np.float32)
+            exp = np.asarray(part["scale"] if fp8_scales is None else fp8_scales[side], np.float32)
+            assert np.array_equal(s.view(np.uint32), exp.view(np.uint32)), f"{side} fp8 scale differs"
+            continue
+        if spec[0] == OC.NONE:
+            continue
+        mdt, bits_t = (np.float16, np.uint16) if c.meta16 else (np.float32, np.uint32)
+        if spec[2] == OC.PER_CHANNEL:
+            G = spec[3]
+            sc = gathered(side + "_scale", (P // G, D), mdt, Tq // G)
+            zz = gathered(side + "_zero", (P // G, D), mdt, Tq // G) if spec[0] == OC.INT_ASYM else None
+        else:
+            cols = D // (spec[3] or D)
+            sc = gathered(side + "_scale", (P, cols), mdt, Tq)
+            zz = gathered(side + "_zero", (P, cols), mdt, Tq) if spec[0] == OC.INT_ASYM else None
+        exp_s = part["scale"][0].reshape(sc.shape)
+        assert np.array_equal(sc.view(bits_t), exp_s.astype(mdt).view(bits_t)), f"seq {b}: {side} scales differ"
+        if zz is not None:
+            assert np.array_equal(zz.astype(np.float32), part["zero"][0].reshape(zz.shape)), \
+                f"seq {b}: {side} zero-points differ"
+    if T > Tq:
+        Rs = lay.ring_slots
+        slots = OC.window_slots(c.oracle_cfg(), Tq, T)
+        n = Rs * D * 2
+        rk = pc.arena[lay.ring_k + b * H * n: lay.ring_k + (b + 1) * H * n].cpu().numpy().view(np.float16)
+        rk = rk.reshape(H, Rs, D)[:, slots]
+        assert np.array_equal(rk.view(np.uint16), st["k_window"][0].view(np.uint16)), f"seq {b}: ring K differs"
+        rvb = pc.arena[lay.ring_v + b * H * n: lay.ring_v + (b + 1) * H * n].cpu().numpy()
+        rv = OC.unpack_vblocks(rvb.reshape(H, Rs // 32, 32 * D * 2), 16, D, Rs)[:, slots]
+        assert np.array_equal(rv.view(np.uint16), st["v_window"][0].view(np.uint16)), f"seq {b}: ring V differs"

@@ -37,7 +37,8 @@ def test_header_symbols_exported():
 
 
 def test_struct_sizes_match_c_layout():
-    assert C.sizeof(K.Config) == 80
+    assert C.sizeof(K.Config) == 88
+    assert C.sizeof(K.Layout) == 136
     assert C.sizeof(K.TensorSpec) == 16
     assert C.sizeof(K.AttnOptions) == 32
 
@@ -267,7 +268,7 @@ def test_meta_dtype_validation():
     for bad in (2, -1, 7):
         with pytest.raises(K.KvqError):
             K.kvq_arena_bytes(_cfg(meta_dtype=bad))
-    assert K.kvq_abi_version() == 4
+    assert K.kvq_abi_version() == 5
 
 
 def test_plain_c_caller(tmp_path):
@@ -353,7 +354,7 @@ def test_binding_rejects_bad_attention_arguments():
     k1, v1 = t["k"][:, :, :1].contiguous(), t["v"][:, :, :1].contiguous()
     _rejects(st, cfg, t["arena"], 16, t["k"], t["v"], t["q"], t["out"], sm, t["ws"],
              match="a decode step appends 1")
-    _rejects(st, cfg, t["arena"], 16, k1, v1, t["q"].T.contiguous().T, t["out"], sm, t["ws"],
+    _rejects(st, cfg, t["arena"], 16, k1, v1, t["q"].permute(2, 1, 0).contiguous().permute(2, 1, 0), t["out"], sm, t["ws"],
              match="q must be contiguous")
     _rejects(st, cfg, t["arena"], 16, k1, v1, t["q"], t["out"], sm, t["ws"], match="arena must be a GPU tensor")
 
@@ -396,3 +397,77 @@ def test_static_scratch_entry_point_validation():
         c = K.make_config(batch=w["B"], num_q_heads=w["Hq"], num_kv_heads=w["Hkv"], head_dim=128,
                           max_tokens=w["T"] + 64, k=kspec, v=vspec, residual=R, pre_rope_k=pre)
         assert K.kvq_workspace_bytes(c, w["T"] + 1) <= K.STATIC_WORKSPACE_BYTES, name
+
+
+# ---------------------------------------------------------------------------
+# paged caches: configuration rules, layout and host-side validation
+# ---------------------------------------------------------------------------
+
+def _pcfg(**kw):
+    base = dict(page_tokens=64, num_pages=40)
+    base.update(kw)
+    return _cfg(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(page_tokens=48),                                   # not a multiple of 32
+    dict(page_tokens=64, k=(K.INT_ASYM, 4, K.PER_CHANNEL, 128), residual=128),   # P % G != 0
+    dict(num_pages=0),
+    dict(page_tokens=0, num_pages=5),                        # pages without paging
+    dict(page_tokens=-32),
+    dict(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 0), v=(K.INT_ASYM, 4, K.PER_TOKEN, 0), residual=0),  # whole axis
+    dict(k=(K.INT_SYM, 8, K.PER_TENSOR, 0), v=(K.INT_ASYM, 4, K.PER_TOKEN, 0), residual=0),    # per tensor
+    dict(k=(K.INT_ASYM, 4, K.PER_CHANNEL, 256), residual=256, page_tokens=256),  # key group over 128
+])
+def test_paged_invalid_configs(bad):
+    assert K.kvq_validate_config(_pcfg(**bad)) == -1
+
+
+def test_paged_layout_sizes():
+    cfg = _pcfg()                   # INT4 K G32 + INT4 V G32, R 32, B 2, 2 kv heads, D 128
+    lay = K.kvq_arena_layout(cfg)
+    assert (lay.page_tokens, lay.pages) == (64, 40)
+    rows = 40 * 2 * 64
+    assert lay.k_scale - lay.k_codes >= rows * 64
+    assert lay.k_zero - lay.k_scale >= rows // 32 * 128 * 4
+    assert lay.v_codes - lay.k_zero >= rows // 32 * 128 * 4
+    assert lay.v_scale - lay.v_codes >= rows // 32 * (32 * 128 * 4 // 8)
+    assert lay.v_zero - lay.v_scale >= rows * 4 * 4          # 4 value groups of 32 channels per token
+    c = K.kvq_arena_layout(_cfg())
+    assert (c.page_tokens, c.pages) == (c.token_capacity, 2)
+
+
+def test_paged_entry_point_validation():
+    raw = _lib.raw
+    pc, cc = _pcfg(), _cfg()
+    bt, sl, arena, kn, q, out, ws = 0x500000, 0x600000, 0x100000, 0x200000, 0x300000, 0x380000, 0x400000
+    opt = K.AttnOptions()
+    wsb = K.kvq_workspace_bytes(pc, 640)
+
+    def app(c=pc, bt_=bt, mb=10, sl_=sl, nl=None, n=4, flags=0, a=arena):
+        return raw.kvq_paged_quantize_append(C.byref(c), a, bt_, mb, sl_, nl, n, kn, kn, None, None, flags, None)
+
+    def att(c=pc, bt_=bt, mb=10, sl_=sl, T=640, w=wsb):
+        return raw.kvq_paged_decode_attention(C.byref(c), arena, bt_, mb, sl_, T, q, out, 0.088, ws, w,
+                                              C.byref(opt), None)
+
+    assert app(c=cc) == -2                       # contiguous cache: the contiguous calls
+    assert att(c=cc) == -2
+    assert app(bt_=None) == -5 and att(sl_=None) == -5
+    assert app(bt_=0x500002) == -4
+    assert app(mb=0) == -1
+    assert app(flags=K.CALIBRATE) == -1           # calibrate only when starting (and FP8)
+    assert app(flags=16) == -1
+    assert app(a=0x100010) == -4
+    assert att(T=641) == -1                        # past max_blocks * P
+    assert att(T=1025) == -3                       # past max_tokens
+    assert att(w=wsb - 1) == -6
+    # the contiguous entry points refuse a paged cache
+    assert _append(pc) == -2
+    assert raw.kvq_decode_attention(C.byref(pc), arena, 100, q, out, 0.088, ws, wsb, C.byref(opt), None) == -2
+    assert raw.kvq_dequantize(C.byref(pc), arena, 100, 0x200000, None, None) == -2
+    # paged workspace: a split's pages fit the attention kernel's table
+    small = _pcfg(page_tokens=32, num_pages=4000, max_tokens=65536)
+    for T in (1, 1000, 8192, 65536):
+        b = K.kvq_workspace_bytes(small, T)
+        assert b >= K.kvq_workspace_bytes(small, max(1, T // 2))

@@ -111,3 +111,15 @@ def test_timed_window_without_a_window_is_empty():
     from oracle import cache as OC
     cfg = OC.Cfg(1, 4, 1, 128, OC.Spec(3, 8, 0, 0), OC.Spec(3, 8, 0, 0), R=0)
     assert bench.timed_window(lambda T: OC.quantized_tokens(cfg, T), 8192, 5, 20, 1) == (0, [])
+
+
+def test_ragged_algorithmic_bytes_sum_the_sequences():
+    """A ragged batch moves each sequence's own bytes: the total is the sum of
+    batch-1 totals minus the per-call q / out of the other sequences."""
+    w, fmt = W.WORKLOADS["c5_int2_kivi_prerope_32k"], bench.FORMATS["c5_int2_kivi_prerope_32k"]
+    lens = [32769 - (1021 * b) % 8192 for b in range(w["B"])]
+    total, _ = bench.algorithmic_bytes(w, fmt, 0, lens=lens)
+    one = dict(w, B=1)
+    qo = w["Hq"] * 128 * (2 + 4)
+    assert total == sum(bench.algorithmic_bytes(one, fmt, t)[0] - qo for t in lens) + w["B"] * qo
+    assert bench.algorithmic_bytes(w, fmt, 32769, lens=[32769] * w["B"]) == bench.algorithmic_bytes(w, fmt, 32769)

@@ -273,3 +273,17 @@ def test_window_slot_bugs_are_caught(monkeypatch):
     monkeypatch.setattr(C, "window_slots", lambda cfg, Tq, T: (np.arange(Tq, T) % max(orig(cfg), 1)) if
                         orig(cfg) == 0 else (np.arange(Tq, T) - Tq) % orig(cfg))
     assert _fails(P.test_window_slots_hand_values_and_no_collisions)
+
+
+def test_gather_pages_bugs_are_caught(monkeypatch):
+    """Pages taken in table order but from the wrong sequence's row, or the
+    table read column-major, fail the hand-value pin."""
+    import oracle.paged as OP
+    orig = OP.gather_pages
+    monkeypatch.setattr(OP, "gather_pages", lambda sec, bt, b, P, T: orig(sec, bt[::-1], b, P, T))
+    assert _fails(P.test_gather_pages_hand_values)
+    monkeypatch.setattr(OP, "gather_pages",
+                        lambda sec, bt, b, P, T: np.concatenate([sec[int(bt.T.reshape(-1)[b * OP.blocks_of(T, P) + j])]
+                                                                 for j in range(OP.blocks_of(T, P))], axis=1)
+                        if OP.blocks_of(T, P) else orig(sec, bt, b, P, T))
+    assert _fails(P.test_gather_pages_hand_values)

@@ -570,3 +570,39 @@ def test_rel_l2_zero_reference():
     z = np.zeros(4)
     assert A.rel_l2(z, z) == 0.0
     assert A.rel_l2(np.ones(4), z) == np.inf
+
+
+# ---------------------------------------------------------------------------
+# paged layout: gathering pages back into the contiguous order
+# ---------------------------------------------------------------------------
+
+def test_gather_pages_hand_values():
+    """Pages of P = 2 tokens, 1 head, rows tagged by hand: page k holds rows
+    [10k, 10k + 1]; sequence 0 owns pages (2, 0), sequence 1 owns (1, 3, 4)."""
+    from oracle import paged as OP
+    sec = np.array([[[10 * k, 10 * k + 1]] for k in range(5)])            # [pages=5][H=1][rows=2]
+    bt = np.array([[2, 0, -1], [1, 3, 4]])
+    assert OP.gather_pages(sec, bt, 0, 2, 3).tolist() == [[20, 21, 0, 1]]
+    assert OP.gather_pages(sec, bt, 1, 2, 5).tolist() == [[10, 11, 30, 31, 40, 41]]
+    assert OP.gather_pages(sec, bt, 1, 2, 2).tolist() == [[10, 11]]
+    assert OP.gather_pages(sec, bt, 0, 2, 0).shape == (1, 0)
+    assert OP.blocks_of(0, 32) == 0 and OP.blocks_of(32, 32) == 1 and OP.blocks_of(33, 32) == 2
+
+
+def test_gather_scatter_round_trip_and_contiguous_special_case():
+    """A contiguous cache is the paged layout with one page of Tc tokens per
+    sequence (block_table[b] = [b]); scatter then gather is the identity."""
+    from oracle import paged as OP
+    rng = np.random.default_rng(5)
+    B, H, Tc = 3, 2, 8
+    contig = rng.integers(0, 255, size=(B, H, Tc, 4))
+    ident = np.arange(B).reshape(B, 1)
+    for b in range(B):
+        assert np.array_equal(OP.gather_pages(contig, ident, b, Tc, Tc), contig[b])
+    P, pages = 2, 13
+    perm = rng.permutation(pages)[:B * (Tc // P)].reshape(B, Tc // P)
+    pool = np.zeros((pages, H, P, 4), dtype=contig.dtype)
+    for b in range(B):
+        OP.scatter_pages(contig[b], perm, b, pool)
+    for b in range(B):
+        assert np.array_equal(OP.gather_pages(pool, perm, b, P, Tc), contig[b])
