@@ -184,32 +184,35 @@ def summarize_counters(workload, fetch_dir, write_dir, copy_bytes, command):
     import csv
     import glob
 
-    def per_kernel(d, counter):
+    def per_dispatch(d, counter):
         acc = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] != counter:
                     continue
-                key = (r["Kernel_Name"], r.get("Dispatch_Id", ""))
+                key = (r["Kernel_Name"], int(r.get("Dispatch_Id") or 0))
                 acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
-        by_name = {}
-        for (kname, _), v in acc.items():
-            by_name.setdefault(kname, []).append(v)
-        return {k: sum(v) / len(v) for k, v in by_name.items()}
+        return acc
 
-    def pick(table, needle):
-        hits = [(k, v) for k, v in table.items() if needle in k]
-        if not hits:
+    def mean_of(table, needle, after=-1):
+        vals = [(k, v) for (k, i), v in table.items() if needle in k and i > after]
+        if not vals:
             raise SystemExit(f"no dispatch of a kernel matching {needle!r}")
-        return hits[0]
+        return vals[0][0], sum(v for _, v in vals) / len(vals)
 
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    _, f_copy = pick(fetch, "copyBuffer")
-    _, w_copy = pick(write, "copyBuffer")
-    k1, f_attn = pick(fetch, "attn_mfma")
-    _, f_merge = pick(fetch, "attn_merge")
-    _, w_attn = pick(write, "attn_mfma")
-    _, w_merge = pick(write, "attn_merge")
+    def probe(table):
+        # the copy probe runs after the timed region: only copies issued after
+        # the last attention launch count (set-up copies, such as the arena
+        # copies of a rotating-arena run, are excluded)
+        last = max(i for (k, i) in table if "attn_mfma" in k)
+        return mean_of(table, "copyBuffer", after=last)[1]
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    f_copy, w_copy = probe(fetch), probe(write)
+    k1, f_attn = mean_of(fetch, "attn_mfma")
+    _, f_merge = mean_of(fetch, "attn_merge")
+    _, w_attn = mean_of(write, "attn_mfma")
+    _, w_merge = mean_of(write, "attn_merge")
     cf, cw = copy_bytes / (f_copy * 1024.0), copy_bytes / (w_copy * 1024.0)
     fetched = (f_attn + f_merge) * 1024.0 * cf
     written = (w_attn + w_merge) * 1024.0 * cw
@@ -260,6 +263,10 @@ def gpu_clock_record():
     """Clock and power of the GPU as rocm-smi reports them (sampled while
     attention launches are queued), or the reason there is none."""
     import subprocess
+    # under a profiler the tool's preloaded library would initialise the GPU in
+    # rocm-smi's own process too, which then re-executes its interpreter
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return {"error": "not sampled under a profiler"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
                            text=True, timeout=20)
@@ -365,19 +372,19 @@ def main():
     steps_total = a.warmup + extra + a.steps + (period if period > 1 else 0)
     cap = T0 + n_new * (steps_total + 1) + 64
     cfg = make_cfg(cap, paged=a.paged > 0)
-    # paged caches: lengths base[b] + s after s decode steps (s = T - T0 for
+    # paged caches: lengths lens0[b] + s after s decode steps (s = T - T0 for
     # the uniform-length bookkeeping below), one device array per s prepared
     # up front so the timed steps launch nothing else
-    base = np.array([T0 - (1021 * b) % 8192 for b in range(B)] if a.ragged else [T0] * B, dtype=np.int64)
+    lens0 = np.array([T0 - (1021 * b) % 8192 for b in range(B)] if a.ragged else [T0] * B, dtype=np.int64)
     if a.paged:
         pages = K.kvq_arena_layout(cfg).pages
         nblk = -(-cap // a.paged)
         perm = np.random.default_rng(1234).permutation(pages)[:B * nblk].astype(np.int32)
         bt = torch.from_numpy(perm.reshape(B, nblk)).to(dev)
-        lens_dev = [torch.from_numpy((base + i).astype(np.int32)).to(dev) for i in range(steps_total + 3)]
+        lens_dev = [torch.from_numpy((lens0 + i).astype(np.int32)).to(dev) for i in range(steps_total + 3)]
 
     def lens_at(T):
-        return base + (T - T0)
+        return lens0 + (T - T0)
     print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
     kp = torch.from_numpy(W.full_prefill(name, "k").view(np.int16)).view(torch.bfloat16).to(dev)
     vp = torch.from_numpy(W.full_prefill(name, "v").view(np.int16)).view(torch.bfloat16).to(dev)
@@ -540,7 +547,7 @@ def main():
             "untimed_positioning_steps": extra,
             "folds_in_timed_steps": len(folds_in_window),
             "layout": (f"paged, {a.paged}-token pages in a shuffled order" if a.paged else "contiguous"),
-            "lengths": ("ragged " + f"{int(base.min())}..{int(base.max())} at the start" if a.ragged
+            "lengths": ("ragged " + f"{int(lens0.min())}..{int(lens0.max())} at the start" if a.ragged
                         else "uniform"),
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 2),

@@ -123,3 +123,34 @@ def test_ragged_algorithmic_bytes_sum_the_sequences():
     qo = w["Hq"] * 128 * (2 + 4)
     assert total == sum(bench.algorithmic_bytes(one, fmt, t)[0] - qo for t in lens) + w["B"] * qo
     assert bench.algorithmic_bytes(w, fmt, 32769, lens=[32769] * w["B"]) == bench.algorithmic_bytes(w, fmt, 32769)
+
+
+def test_counter_summary_calibrates_on_the_probe_copies_only(tmp_path, monkeypatch):
+    """Copies issued before the attention launches (a rotating-arena run copies
+    its arena) must not enter the calibration: only the probe copies issued
+    after the last attention launch do."""
+    import csv
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "attention_source_hash", lambda: "h")
+    copy = "__amd_rocclr_copyBuffer"
+    attn = "void kvq::attn_mfma<4, 4, false, 1, false, false>(kvq::Plan, kvq::mf::Args)"
+    merge = "kvq::attn_merge(kvq::Plan, float const*, float const*, int, float*)"
+    probe_kib = {"FETCH_SIZE": 1048576.0, "WRITE_SIZE": 2097152.0}     # 2 GiB each way
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = tmp_path / counter
+        d.mkdir()
+        rows = [(1, copy, 70000.0), (2, copy, 70000.0),                 # set-up copies
+                (3, attn, 1000.0), (4, merge, 10.0), (5, attn, 1000.0), (6, merge, 10.0),
+                (7, copy, probe_kib[counter]), (8, copy, probe_kib[counter])]
+        with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+            w = csv.writer(fh)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            for i, k, v in rows:
+                w.writerow([i, k, counter, v])
+    bench.summarize_counters("c4_int4_llama70b_128k", str(tmp_path / "FETCH_SIZE"),
+                             str(tmp_path / "WRITE_SIZE"), 2 << 30, "cmd")
+    out = json.load(open(tmp_path / "profiles" / "traffic_c4_int4_llama70b_128k.json"))
+    assert out["calibration"] == {"fetch": 2.0, "write": 1.0}
+    assert out["fetch_bytes_per_launch"] == round(1010.0 * 1024 * 2)
+    assert out["write_bytes_per_launch"] == round(1010.0 * 1024)
