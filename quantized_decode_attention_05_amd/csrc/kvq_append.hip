@@ -54,6 +54,7 @@ struct AppendArgs {
   int64_t cap;               // a sequence's range must end at or before this
   int32_t units_q;           // work-groups per (sequence, head) that take quantize units
   int32_t phases;            // bit 0: quantize units run, bit 1: ring units run
+  float one;                 // 1.0f (an operand the compiler cannot fold)
 };
 
 constexpr int kAppendThreads = 256;
@@ -129,6 +130,71 @@ __device__ __forceinline__ float rint_quot(float d, float s, float rs, float m) 
   return __builtin_rintf(d / s);
 }
 
+// Keys and values of N granules (channels c0 .. c0 + 7 of tokens t1 + ts i,
+// i < N), all from the input (t1 >= t0), staged as load_granule stages them.
+// Every load is issued before any value is used, so the memory latency is
+// waited for once per batch, not once per granule.
+template <int D, int N>
+__device__ __forceinline__ void load_kv_granules(const Plan& p, const AppendArgs& a, int b, int h, int64_t t1, int ts,
+                                                 int64_t t0, int c0, float (&xk)[N][8], float (&xv)[N][8]) {
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  const int64_t e0 = (bh * a.n + (t1 - t0)) * D + c0;
+  if (p.in_dtype == KVQ_F32) {
+    const float4* kp = (const float4*)a.k_in + e0 / 4;
+    const float4* vp = (const float4*)a.v_in + e0 / 4;
+    float4 fk[2 * N], fv[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int64_t o = (int64_t)i * ts * (D / 4);
+      fk[2 * i] = kp[o]; fk[2 * i + 1] = kp[o + 1];
+      fv[2 * i] = vp[o]; fv[2 * i + 1] = vp[o + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float ck[8] = {fk[2 * i].x, fk[2 * i].y, fk[2 * i].z, fk[2 * i].w,
+                           fk[2 * i + 1].x, fk[2 * i + 1].y, fk[2 * i + 1].z, fk[2 * i + 1].w};
+      const float cv[8] = {fv[2 * i].x, fv[2 * i].y, fv[2 * i].z, fv[2 * i].w,
+                           fv[2 * i + 1].x, fv[2 * i + 1].y, fv[2 * i + 1].z, fv[2 * i + 1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { xk[i][j] = ck[j]; xv[i][j] = cv[j]; }
+    }
+  } else {
+    const uint4* kp = (const uint4*)a.k_in + e0 / 8;
+    const uint4* vp = (const uint4*)a.v_in + e0 / 8;
+    uint4 rk[N], rv[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int64_t o = (int64_t)i * ts * (D / 8);
+      rk[i] = kp[o];
+      rv[i] = vp[o];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t wk[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w}, wv[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (p.in_dtype == KVQ_F16) {
+          xk[i][2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wk[j] & 0xFFFFu));
+          xk[i][2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wk[j] >> 16));
+          xv[i][2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wv[j] & 0xFFFFu));
+          xv[i][2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wv[j] >> 16));
+        } else {
+          xk[i][2 * j] = __uint_as_float(wk[j] << 16);
+          xk[i][2 * j + 1] = __uint_as_float(wk[j] & 0xFFFF0000u);
+          xv[i][2 * j] = __uint_as_float(wv[j] << 16);
+          xv[i][2 * j + 1] = __uint_as_float(wv[j] & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+  if (p.window) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { xk[i][j] = stage_f16(xk[i][j]); xv[i][j] = stage_f16(xv[i][j]); }
+  }
+}
+
 // Code field (masked to the format's bits) of value x under scale s (rs =
 // recip_or_nan(s)) and zero z; S >= 0 fixes the scheme at compile time.
 template <int S>
@@ -186,6 +252,61 @@ __device__ __forceinline__ void write_k_granule(uint8_t* row, int cb, int bits, 
   }
 }
 
+// Store a value word (8 codes of `bits` bits, tokens 0..7 of the word in
+// lo | hi) at wp; codes of tokens outside `valid` keep the bits already there.
+__device__ __forceinline__ void store_vword(uint8_t* wp, int bits, uint32_t valid, uint32_t lo, uint32_t hi) {
+  if (bits == 2) {
+    if (valid != 0xFFu) {
+      uint32_t keep = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) if (!((valid >> i) & 1u)) keep |= 3u << (2 * i);
+      lo |= (uint32_t)*(const uint16_t*)wp & keep;
+    }
+    *(uint16_t*)wp = (uint16_t)lo;
+  } else if (bits == 4) {
+    if (valid != 0xFFu) {
+      uint32_t keep = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) if (!((valid >> i) & 1u)) keep |= 15u << (4 * i);
+      lo |= *(const uint32_t*)wp & keep;
+    }
+    *(uint32_t*)wp = lo;
+  } else {
+    if (valid != 0xFFu) {
+      const uint2 old = *(const uint2*)wp;
+      uint32_t klo = 0, khi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!((valid >> i) & 1u)) klo |= 0xFFu << (8 * i);
+        if (!((valid >> (i + 4)) & 1u)) khi |= 0xFFu << (8 * i);
+      }
+      lo |= old.x & klo;
+      hi |= old.y & khi;
+    }
+    *(uint2*)wp = make_uint2(lo, hi);
+  }
+}
+
+// A 16-byte granule of a 16-bit input (8 values) as fp32, staged as
+// load_granule stages it.
+__device__ __forceinline__ void unpack16(const Plan& p, const uint4& r, float (&x)[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (p.in_dtype == KVQ_F16) {
+      x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
+      x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+    } else {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  if (p.window) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = stage_f16(x[j]);
+  }
+}
+
 template <int D>
 struct AppendShared {
   float red_mn[4][D], red_mx[4][D];   // per-wavefront partial min / max of key channels
@@ -205,17 +326,38 @@ __device__ __forceinline__ void quantize_unit(const Plan& p, const AppendArgs& a
   const bool k_int = fk.scheme == KVQ_INT_ASYM || fk.scheme == KVQ_INT_SYM;
   const bool k_sym = fk.scheme == KVQ_INT_SYM;
 
+  // A whole unit of new tokens of a 16-bit input (every unit of such a
+  // prefill) issues all its key and value loads at once; the value granules
+  // are the same tokens as the key granules (value block sb, granule i is
+  // key granule sb * (32 / TPP) + i) and wait as raw words.
+  constexpr int NG = U / TPP;              // granules per thread
+  const bool batch = u0 >= t0 && v_lo == u0 && v_hi == u0 + U && p.in_dtype != KVQ_F32;
+  uint4 rv[NG];
+
   // ---- keys --------------------------------------------------------------------
   {
-    constexpr int NG = U / TPP;            // granules per thread
     float x[NG][8];
+    if (batch) {
+      const int64_t e0 = (bh * a.n + (u0 + tq - t0)) * D + 8 * cb;
+      const uint4* kp = (const uint4*)a.k_in + e0 / 8;
+      const uint4* vp = (const uint4*)a.v_in + e0 / 8;
+      uint4 rk[NG];
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int64_t t = u0 + tq + TPP * i;
-      if (t >= v_lo && t < v_hi) load_granule<SIDE_K, D>(p, a, b, h, t, t0, 8 * cb, x[i]);
-      else {
+      for (int i = 0; i < NG; ++i) {
+        rk[i] = kp[(int64_t)i * TPP * (D / 8)];
+        rv[i] = vp[(int64_t)i * TPP * (D / 8)];
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
+      for (int i = 0; i < NG; ++i) unpack16(p, rk[i], x[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int64_t t = u0 + tq + TPP * i;
+        if (t >= v_lo && t < v_hi) load_granule<SIDE_K, D>(p, a, b, h, t, t0, 8 * cb, x[i]);
+        else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
+        }
       }
     }
     const bool per_channel = k_int && fk.axis == KVQ_PER_CHANNEL;
@@ -311,7 +453,8 @@ __device__ __forceinline__ void quantize_unit(const Plan& p, const AppendArgs& a
       const int64_t t = ts + tk;
       const bool ok = t >= v_lo && t < v_hi;
       float x[8];
-      if (ok) load_granule<SIDE_V, D>(p, a, b, h, t, t0, 8 * cb, x);
+      if (batch) unpack16(p, rv[sb * NVG + i], x);
+      else if (ok) load_granule<SIDE_V, D>(p, a, b, h, t, t0, 8 * cb, x);
       else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = 0.0f;
@@ -499,6 +642,39 @@ __device__ __forceinline__ void token_groups(const SideFmt& f, const float (&x)[
   }
 }
 
+// Window tokens of one 32-token block (ring unit xr of (b, h)) into their
+// ring slots: lane (cb, r) moves channels 8 cb .. 8 cb + 7 of tokens 8 r ..
+// 8 r + 7 of the block.
+__device__ __forceinline__ void wave_ring_block(const Plan& p, const AppendArgs& a, int b, int h, int64_t t0,
+                                                int64_t nb, int64_t q_hi, int64_t xr, int cb, int r) {
+  constexpr int D = 128;
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  const int64_t w_lo = q_hi > t0 ? q_hi : t0, w_hi = t0 + nb;
+  const int64_t blk = (w_lo & ~(int64_t)31) + 32 * xr;
+  if (w_hi <= w_lo || blk >= w_hi) return;
+  const int rblock = kVBlock * D * 2;
+  uint8_t* vbase = a.arena + p.ring_v + (uint64_t)bh * (p.Rs / kVBlock) * rblock;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t t = blk + 8 * r + i;
+    if (t < w_lo || t >= w_hi) continue;
+    const int64_t slot = t % p.Rs;
+    float xk[8], xv[8];
+    load_granule<SIDE_K, D>(p, a, b, h, t, t0, 8 * cb, xk);
+    load_granule<SIDE_V, D>(p, a, b, h, t, t0, 8 * cb, xv);
+    uint32_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)xk[2 * j], hi = (_Float16)xk[2 * j + 1];
+      u[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *(uint4*)(a.arena + p.ring_k + ((bh * p.Rs + slot) * D + 8 * cb) * 2) = make_uint4(u[0], u[1], u[2], u[3]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ((_Float16*)(vbase + vblock_word_byte(slot, 8 * cb + j, D, 16, rblock)))[slot & 7] = (_Float16)xv[j];
+  }
+}
+
 // KS / VS >= 0 fix the key / value scheme and KAX >= 0 the key axis at
 // compile time, so that an instance holds only its own encoder (the whole
 // unrolled body then stays in the instruction cache).
@@ -519,32 +695,7 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
   const int64_t bh = (int64_t)b * p.Hkv + h;
 
   if (x >= a.units_q) {
-    // window tokens of one 32-token block into their ring slots
-    if (!(a.phases & 2)) return;
-    const int64_t w_lo = q_hi > t0 ? q_hi : t0, w_hi = t0 + nb;
-    const int64_t blk = (w_lo & ~(int64_t)31) + 32 * (x - a.units_q);
-    if (w_hi <= w_lo || blk >= w_hi) return;
-    const int rblock = kVBlock * D * 2;
-    uint8_t* vbase = a.arena + p.ring_v + (uint64_t)bh * (p.Rs / kVBlock) * rblock;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t t = blk + 8 * r + i;
-      if (t < w_lo || t >= w_hi) continue;
-      const int64_t slot = t % p.Rs;
-      float xk[8], xv[8];
-      load_granule<SIDE_K, D>(p, a, b, h, t, t0, 8 * cb, xk);
-      load_granule<SIDE_V, D>(p, a, b, h, t, t0, 8 * cb, xv);
-      uint32_t u[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const _Float16 lo = (_Float16)xk[2 * j], hi = (_Float16)xk[2 * j + 1];
-        u[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      *(uint4*)(a.arena + p.ring_k + ((bh * p.Rs + slot) * D + 8 * cb) * 2) = make_uint4(u[0], u[1], u[2], u[3]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        ((_Float16*)(vbase + vblock_word_byte(slot, 8 * cb + j, D, 16, rblock)))[slot & 7] = (_Float16)xv[j];
-    }
+    if (a.phases & 2) wave_ring_block(p, a, b, h, t0, nb, q_hi, x - a.units_q, cb, r);
     return;
   }
   if (!(a.phases & 1) || x >= n_qu) return;
@@ -553,16 +704,23 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
   const int32_t pg = page_of(p, a.pm, b, u0);     // the unit's page (units never straddle pages)
   bool ok[8];
   float xk[8][8], xv[8][8];
+  if (u0 >= t0 && v_lo == u0 && v_hi == u0 + 32) {
+    // a whole unit of new tokens (every unit of a prefill)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t t = u0 + 8 * r + i;
-    ok[i] = t >= v_lo && t < v_hi;
-    if (ok[i]) {
-      load_granule<SIDE_K, D>(p, a, b, h, t, t0, 8 * cb, xk[i]);
-      load_granule<SIDE_V, D>(p, a, b, h, t, t0, 8 * cb, xv[i]);
-    } else {
+    for (int i = 0; i < 8; ++i) ok[i] = true;
+    load_kv_granules<D, 8>(p, a, b, h, u0 + 8 * r, 1, t0, 8 * cb, xk, xv);
+  } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { xk[i][j] = 0.0f; xv[i][j] = 0.0f; }
+    for (int i = 0; i < 8; ++i) {
+      const int64_t t = u0 + 8 * r + i;
+      ok[i] = t >= v_lo && t < v_hi;
+      if (ok[i]) {
+        load_granule<SIDE_K, D>(p, a, b, h, t, t0, 8 * cb, xk[i]);
+        load_granule<SIDE_V, D>(p, a, b, h, t, t0, 8 * cb, xv[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { xk[i][j] = 0.0f; xv[i][j] = 0.0f; }
+      }
     }
   }
 
@@ -659,36 +817,289 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
       if (bit < 32) lo |= code << bit;
       else hi |= code << (bit - 32);
     }
-    if (bits == 2) {
-      if (valid != 0xFFu) {
-        uint32_t keep = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) if (!((valid >> i) & 1u)) keep |= 3u << (2 * i);
-        lo |= (uint32_t)*(const uint16_t*)wp & keep;
-      }
-      *(uint16_t*)wp = (uint16_t)lo;
-    } else if (bits == 4) {
-      if (valid != 0xFFu) {
-        uint32_t keep = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) if (!((valid >> i) & 1u)) keep |= 15u << (4 * i);
-        lo |= *(const uint32_t*)wp & keep;
-      }
-      *(uint32_t*)wp = lo;
+    store_vword(wp, bits, valid, lo, hi);
+  }
+}
+
+// ---- fp16-staged caches: keys per channel, values per token ------------------
+// When every value is rounded to fp16 before it is quantized (caches with an
+// fp16 window, or fp16 inputs), a wavefront holds its unit as packed fp16
+// pairs: half the registers of fp32 values, so twice the wavefronts fit per
+// SIMD, and min / max take one packed instruction per two values.  x - z is
+// taken from the fp16 value by one mixed-precision FMA (x * 1 - z rounds
+// once, as the subtraction does), and the correctly rounded quotient comes
+// from a correctly rounded reciprocal and one FMA correction (asym_codes8_h).
+// Same lane layout, work split and outputs as append_wave.
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t pk_h(float lo, float hi) {
+  const h2_t v = {(_Float16)lo, (_Float16)hi};
+  return as_u32(v);
+}
+
+// Channels c0 .. c0 + 7 of token t as four fp16 pairs: from the ring for
+// tokens appended by earlier calls (t < t0), else the input rounded to fp16.
+template <int SIDE>
+__device__ __forceinline__ void load_granule_h(const Plan& p, const AppendArgs& a, int b, int h, int64_t t,
+                                               int64_t t0, int c0, uint32_t (&w)[4]) {
+  constexpr int D = 128;
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  if (t < t0) {
+    const int64_t slot = t % p.Rs;
+    if (SIDE == SIDE_K) {
+      const uint4 r = *(const uint4*)(a.arena + p.ring_k + ((bh * p.Rs + slot) * D + c0) * 2);
+      w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
     } else {
-      if (valid != 0xFFu) {
-        const uint2 old = *(const uint2*)wp;
-        uint32_t klo = 0, khi = 0;
+      const int rblock = kVBlock * D * 2;
+      const uint8_t* base = a.arena + p.ring_v + (uint64_t)bh * (p.Rs / kVBlock) * rblock;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!((valid >> i) & 1u)) klo |= 0xFFu << (8 * i);
-          if (!((valid >> (i + 4)) & 1u)) khi |= 0xFFu << (8 * i);
-        }
-        lo |= old.x & klo;
-        hi |= old.y & khi;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = ((const uint16_t*)(base + vblock_word_byte(slot, c0 + 2 * j, D, 16, rblock)))[slot & 7];
+        const uint32_t hi = ((const uint16_t*)(base + vblock_word_byte(slot, c0 + 2 * j + 1, D, 16, rblock)))[slot & 7];
+        w[j] = lo | (hi << 16);
       }
-      *(uint2*)wp = make_uint2(lo, hi);
     }
+    return;
+  }
+  const void* in = SIDE == SIDE_K ? a.k_in : a.v_in;
+  const int64_t e = (bh * a.n + (t - t0)) * D + c0;
+  if (p.in_dtype == KVQ_F16) {
+    const uint4 r = ((const uint4*)in)[e / 8];
+    w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+  } else if (p.in_dtype == KVQ_F32) {
+    const float4 u = ((const float4*)in)[e / 4], v = ((const float4*)in)[e / 4 + 1];
+    w[0] = pk_h(u.x, u.y); w[1] = pk_h(u.z, u.w); w[2] = pk_h(v.x, v.y); w[3] = pk_h(v.z, v.w);
+  } else {
+    const uint4 r = ((const uint4*)in)[e / 8];
+    const uint32_t q[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pk_h(__uint_as_float(q[j] << 16), __uint_as_float(q[j] & 0xFFFF0000u));
+  }
+}
+
+// Tokens u0 + 8 r + i (i = 0..7), channels 8 cb .. 8 cb + 7, all from the
+// input (u0 >= t0), as fp16 pairs.  Every load is issued before any value is
+// used, so a wavefront waits for its unit's memory once, not once per granule.
+__device__ __forceinline__ void load_unit_h(const Plan& p, const AppendArgs& a, int b, int h, int64_t u0, int64_t t0,
+                                            int cb, int r, uint32_t (&hk)[8][4], uint32_t (&hv)[8][4]) {
+  constexpr int D = 128;
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  const int64_t e0 = (bh * a.n + (u0 + 8 * r - t0)) * D + 8 * cb;   // element of (token u0 + 8 r, channel 8 cb)
+  if (p.in_dtype == KVQ_F32) {
+    // two 16-byte loads per granule: keys, then values
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+      const float4* src = (const float4*)(side ? a.v_in : a.k_in) + e0 / 4;
+      float4 f[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { f[2 * i] = src[i * (D / 4)]; f[2 * i + 1] = src[i * (D / 4) + 1]; }
+      uint32_t (&w)[8][4] = side ? hv : hk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[i][0] = pk_h(f[2 * i].x, f[2 * i].y);
+        w[i][1] = pk_h(f[2 * i].z, f[2 * i].w);
+        w[i][2] = pk_h(f[2 * i + 1].x, f[2 * i + 1].y);
+        w[i][3] = pk_h(f[2 * i + 1].z, f[2 * i + 1].w);
+      }
+    }
+    return;
+  }
+  const uint4* ks = (const uint4*)a.k_in + e0 / 8;
+  const uint4* vs = (const uint4*)a.v_in + e0 / 8;
+  uint4 rk[8], rv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { rk[i] = ks[i * (D / 8)]; rv[i] = vs[i * (D / 8)]; }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t qk[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w}, qv[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (p.in_dtype == KVQ_F16) {
+        hk[i][j] = qk[j];
+        hv[i][j] = qv[j];
+      } else {
+        hk[i][j] = pk_h(__uint_as_float(qk[j] << 16), __uint_as_float(qk[j] & 0xFFFF0000u));
+        hv[i][j] = pk_h(__uint_as_float(qv[j] << 16), __uint_as_float(qv[j] & 0xFFFF0000u));
+      }
+    }
+  }
+}
+
+// Asymmetric codes of eight fp16 values xh[k] under scales s[k] and zero-
+// points z[k], given ys[k] = 1 / s[k] rounded once (the IEEE division).
+// d = x - z is one mixed-precision FMA from the fp16 value (one = 1.0 from the
+// host, kept opaque so that the FMA is not turned back into a conversion and
+// a subtraction); both rounding steps of the quotient are exact-rounding
+// steps: q0 = d * y, r = d - s q0 (exact by FMA), q = q0 + r y rounded once is
+// the correctly rounded d / s (the correction step of Markstein's division,
+// valid for a correctly rounded reciprocal).  For fp16-staged groups d is 0
+// or at least 2^-24, s lies in [1e-8 / 255, 2^16] and d = 0 whenever s is at
+// the floor, so no step leaves the normal range.  No branch, no division per
+// element.
+__device__ __forceinline__ void asym_codes8_h(const _Float16 (&xh)[8], const float (&s)[8], const float (&ys)[8],
+                                              const float (&z)[8], float one, float qmax, uint32_t (&c)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float d = __builtin_fmaf((float)xh[k], one, -z[k]);
+    const float q0 = d * ys[k];
+    const float r = __builtin_fmaf(-q0, s[k], d);
+    const float q = __builtin_fmaf(r, ys[k], q0);
+    c[k] = (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(q), 0.0f, qmax);
+  }
+}
+
+__device__ __forceinline__ void rows_minmax_h(uint32_t& mn, uint32_t& mx) {
+  auto r = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
+  mn = as_u32(__builtin_elementwise_min(as_h2(r[0]), as_h2(r[1])));
+  r = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+  mx = as_u32(__builtin_elementwise_max(as_h2(r[0]), as_h2(r[1])));
+  r = __builtin_amdgcn_permlane32_swap(mn, mn, false, false);
+  mn = as_u32(__builtin_elementwise_min(as_h2(r[0]), as_h2(r[1])));
+  r = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+  mx = as_u32(__builtin_elementwise_max(as_h2(r[0]), as_h2(r[1])));
+}
+
+__global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int cb = lane & 15, r = lane >> 4;        // channels 8 cb.., tokens 8 r..
+  const int64_t t0 = a.seq_lens ? (int64_t)a.seq_lens[b] : a.t0;
+  int64_t nb = a.new_lens ? (int64_t)a.new_lens[b] : (int64_t)a.n;
+  if (nb > a.n) nb = a.n;
+  if (t0 < 0 || nb <= 0 || t0 + nb > a.cap) return;
+  const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + nb);
+  const int64_t u_first = q_lo & ~(int64_t)31;
+  const int64_t n_qu = q_hi > q_lo ? (q_hi - u_first + 31) / 32 : 0;
+  const int64_t x = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t bh = (int64_t)b * p.Hkv + h;
+  if (x >= a.units_q) {
+    if (a.phases & 2) wave_ring_block(p, a, b, h, t0, nb, q_hi, x - a.units_q, cb, r);
+    return;
+  }
+  if (!(a.phases & 1) || x >= n_qu) return;
+  const int64_t u0 = u_first + 32 * x;
+  const int64_t v_lo = u0 > q_lo ? u0 : q_lo, v_hi = u0 + 32 < q_hi ? u0 + 32 : q_hi;
+  const int32_t pg = page_of(p, a.pm, b, u0);     // the unit's page (units never straddle pages)
+  bool ok[8];
+  uint32_t hk[8][4], hv[8][4];
+  if (u0 >= t0 && v_lo == u0 && v_hi == u0 + 32) {
+    // a whole unit of new tokens (every unit of a prefill)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ok[i] = true;
+    load_unit_h(p, a, b, h, u0, t0, cb, r, hk, hv);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t t = u0 + 8 * r + i;
+      ok[i] = t >= v_lo && t < v_hi;
+      if (ok[i]) {
+        load_granule_h<SIDE_K>(p, a, b, h, t, t0, 8 * cb, hk[i]);
+        load_granule_h<SIDE_V>(p, a, b, h, t, t0, 8 * cb, hv[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { hk[i][j] = 0u; hv[i][j] = 0u; }
+      }
+    }
+  }
+  const float one = a.one;
+
+  // ---- keys: one whole key group of 32 tokens (every token valid) ----
+  {
+    const SideFmt& fk = p.k;
+    const float qmax = (float)((1 << fk.bits) - 1);
+    float sc[8], zc[8], rc[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      h2_t mn = as_h2(hk[0][m]), mx = mn;
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = __builtin_elementwise_min(mn, as_h2(hk[i][m]));
+        mx = __builtin_elementwise_max(mx, as_h2(hk[i][m]));
+      }
+      uint32_t umn = as_u32(mn), umx = as_u32(mx);
+      rows_minmax_h(umn, umx);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int j = 2 * m + e;
+        meta_values(fk, (float)as_h2(umn)[e], (float)as_h2(umx)[e], &sc[j], &zc[j]);
+        rc[j] = 1.0f / sc[j];
+      }
+    }
+    if (pg >= 0) {
+      if (r == 0) {
+        const int64_t mi = meta_index_row(p, fk, bh, h, row_of(p, pg, h, u0), 8 * cb);   // 8 consecutive entries
+        if (fk.meta16) {
+          *(uint4*)((_Float16*)(a.arena + fk.scale) + mi) =
+              make_uint4(pk_h(sc[0], sc[1]), pk_h(sc[2], sc[3]), pk_h(sc[4], sc[5]), pk_h(sc[6], sc[7]));
+          *(uint4*)((_Float16*)(a.arena + fk.zero) + mi) =
+              make_uint4(pk_h(zc[0], zc[1]), pk_h(zc[2], zc[3]), pk_h(zc[4], zc[5]), pk_h(zc[6], zc[7]));
+        } else {
+          float4* ps = (float4*)((float*)(a.arena + fk.scale) + mi);
+          float4* pz = (float4*)((float*)(a.arena + fk.zero) + mi);
+          ps[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+          ps[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+          pz[0] = make_float4(zc[0], zc[1], zc[2], zc[3]);
+          pz[1] = make_float4(zc[4], zc[5], zc[6], zc[7]);
+        }
+      }
+      uint8_t* krow0 = a.arena + fk.codes + row_of(p, pg, h, u0 + 8 * r) * p.k_row_bytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        _Float16 xh[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xh[j] = as_h2(hk[i][j >> 1])[j & 1];
+        uint32_t c[8];
+        asym_codes8_h(xh, sc, rc, zc, one, qmax, c);
+        write_k_granule(krow0 + i * p.k_row_bytes, cb, fk.bits, c);
+      }
+    }
+  }
+
+  // ---- values: per-token groups of Gc channels, words of 8 tokens formed in the lane ----
+  const SideFmt& fv = p.v;
+  const float qmax = (float)((1 << fv.bits) - 1);
+  float vs[8], vz[8], vr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h2_t mn = __builtin_elementwise_min(__builtin_elementwise_min(as_h2(hv[i][0]), as_h2(hv[i][1])),
+                                        __builtin_elementwise_min(as_h2(hv[i][2]), as_h2(hv[i][3])));
+    h2_t mx = __builtin_elementwise_max(__builtin_elementwise_max(as_h2(hv[i][0]), as_h2(hv[i][1])),
+                                        __builtin_elementwise_max(as_h2(hv[i][2]), as_h2(hv[i][3])));
+    float fmn = fminf((float)mn[0], (float)mn[1]), fmx = fmaxf((float)mx[0], (float)mx[1]);
+    lane_minmax(fmn, fmx, 1, fv.group / 8);
+    meta_values(fv, fmn, fmx, &vs[i], &vz[i]);
+    vr[i] = 1.0f / vs[i];
+    if (ok[i] && pg >= 0 && (cb % (fv.group / 8)) == 0)
+      store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, u0 + 8 * r + i), 8 * cb),
+                        vs[i], vz[i]);
+  }
+  if (pg < 0) return;
+  uint32_t valid = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) valid |= (ok[i] ? 1u : 0u) << i;
+  if (!valid) return;
+  const int bits = fv.bits;
+  uint8_t* blk = a.arena + fv.codes + (row_of(p, pg, h, u0) >> 5) * p.v_block_bytes;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 8 * cb + j, n = c & 15, iw = c >> 4;
+    uint8_t* wp = blk + (int64_t)((16 * r + n) * (D / 16) + iw) * bits;
+    _Float16 xh[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xh[i] = as_h2(hv[i][j >> 1])[j & 1];
+    uint32_t code[8];
+    asym_codes8_h(xh, vs, vr, vz, one, qmax, code);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int bit = i * bits;
+      if (bit < 32) lo |= code[i] << bit;
+      else hi |= code[i] << (bit - 32);
+    }
+    store_vword(wp, bits, valid, lo, hi);
   }
 }
 
@@ -698,18 +1109,15 @@ __global__ void __launch_bounds__(256) fp8_absmax_lens(Plan p, const void* kin, 
                                                         const int32_t* new_lens, uint32_t* amax) {
   const int h = blockIdx.y, side = blockIdx.z;
   const void* in = side ? vin : kin;
+  // each sequence's first new_lens[b] tokens (n * D values per run, 16-byte aligned)
   const int64_t per_seq = (int64_t)n * p.D;
-  const int64_t nel = per_seq * p.B;
-  float m = 0.0f;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nel;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = i / per_seq, r = i % per_seq;
-    const int32_t nl = new_lens ? new_lens[b] : n;
-    if (r / p.D >= nl) continue;
-    float x = load_in(in, (b * p.Hkv + h) * per_seq + r, p.in_dtype);
-    if (p.window) x = stage_f16(x);
-    m = fmaxf(m, fabsf(x));
-  }
+  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+  const int D = p.D;
+  float m = absmax_runs(in, p.B, p.Hkv, h, per_seq, p.in_dtype, p.window != 0, gid, stride, [=](int b) {
+    int64_t nl = new_lens ? (int64_t)new_lens[b] : n;
+    nl = nl < 0 ? 0 : (nl > n ? n : nl);
+    return nl * D;
+  });
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float sm[4];
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
@@ -735,6 +1143,7 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
   a.t0 = t0;
   a.n = n;
   a.cap = cap;
+  a.one = 1.0f;
   // quantize units a sequence can need: the call's tokens plus the window it
   // already held (< Rs), from a group-aligned start; ring units: one per
   // 32-token block of window tokens
@@ -761,7 +1170,9 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
   auto go = [&](int phases) {
     a.phases = phases;
     if (wave_units) {
-      if (kivi)
+      if (kivi && (p.window || p.in_dtype == KVQ_F16))
+        hipLaunchKernelGGL(append_kivi_h, grid_w, blk, 0, s, p, a);
+      else if (kivi)
         hipLaunchKernelGGL((append_wave<KVQ_INT_ASYM, KVQ_INT_ASYM, KVQ_PER_CHANNEL>), grid_w, blk, 0, s, p, a);
       else if (p.k.scheme == KVQ_FP8_E4M3 && p.v.scheme == KVQ_FP8_E4M3)
         hipLaunchKernelGGL((append_wave<KVQ_FP8_E4M3, KVQ_FP8_E4M3, -1>), grid_w, blk, 0, s, p, a);
@@ -792,12 +1203,8 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
 
 hipError_t launch_fp8_absmax_lens(const Plan& p, const void* k_new, const void* v_new, int n,
                                   const int32_t* new_lens, uint32_t* amax, hipStream_t s) {
-  const int64_t nel = (int64_t)p.B * n * p.D;
-  int64_t chunks = (nel + 255) / 256;
-  if (chunks > 512) chunks = 512;
-  if (chunks < 1) chunks = 1;
-  hipLaunchKernelGGL(fp8_absmax_lens, dim3((unsigned)chunks, p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new, n,
-                     new_lens, amax);
+  hipLaunchKernelGGL(fp8_absmax_lens, dim3(fp8_absmax_blocks(p, n), p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new,
+                     n, new_lens, amax);
   return hipGetLastError();
 }
 

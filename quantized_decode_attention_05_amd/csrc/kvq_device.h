@@ -222,4 +222,68 @@ __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* aren
   return prod + z;
 }
 
+// Largest |x| of the values staged from 16 bytes of input (8 values of a
+// 16-bit type, 4 of fp32), as the quantizers stage them (through fp16 when the
+// cache keeps a window).
+__device__ __forceinline__ float absmax16(const uint4& w, int dtype, bool window) {
+  float m = 0.0f;
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float a, b;
+    if (dtype == KVQ_F32) {
+      a = __uint_as_float(q[j]);
+      b = 0.0f;
+    } else if (dtype == KVQ_F16) {
+      a = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[j] & 0xFFFFu));
+      b = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[j] >> 16));
+    } else {
+      a = bf16_to_f32((uint16_t)(q[j] & 0xFFFFu));
+      b = bf16_to_f32((uint16_t)(q[j] >> 16));
+    }
+    if (window) { a = stage_f16(a); b = stage_f16(b); }
+    m = fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
+  }
+  return m;
+}
+
+// absmax over the values of kv head h of every sequence b < B (run b holds
+// lens(b) values from base + (b * Hkv + h) * per_seq elements; per_seq and
+// every lens(b) a multiple of the values per 16 bytes, runs 16-byte
+// aligned), by the threads of a grid-stride (gid, stride).  Each round issues
+// sixteen 16-byte loads (four sequences, four strides) before using any.
+template <typename Lens>
+__device__ __forceinline__ float absmax_runs(const void* base, int B, int Hkv, int h, int64_t per_seq, int dtype,
+                                             bool window, int64_t gid, int64_t stride, Lens lens) {
+  const int per = dtype == KVQ_F32 ? 4 : 8;
+  const int esz = dtype == KVQ_F32 ? 4 : 2;
+  float m = 0.0f;
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    const uint4* v[4];
+    int64_t nv[4], nmax = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = b0 + u < B ? b0 + u : b0;
+      v[u] = (const uint4*)((const uint8_t*)base + ((int64_t)b * Hkv + h) * per_seq * esz);
+      nv[u] = b0 + u < B ? lens(b) / per : 0;
+      nmax = nv[u] > nmax ? nv[u] : nmax;
+    }
+    for (int64_t i = gid; i < nmax; i += 4 * stride) {
+      uint4 w[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = i + k * stride;
+          w[u][k] = e < nv[u] ? v[u][e] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = fmaxf(m, absmax16(w[u][k], dtype, window));
+    }
+  }
+  return m;
+}
+
 }  // namespace kvq

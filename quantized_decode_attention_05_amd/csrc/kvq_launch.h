@@ -61,6 +61,15 @@ bool append_fused_supported(const Plan& p);
 hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, const int32_t* seq_lens,
                                const int32_t* new_lens, int64_t t0, int n, int64_t cap, const void* k_new,
                                const void* v_new, hipStream_t s);
+// Work-groups per (kv head, side) of the FP8 calibration kernels: each lane
+// takes about four 16-byte loads of every sequence (n tokens of D values).
+inline unsigned fp8_absmax_blocks(const Plan& p, int64_t n) {
+  const int64_t per = p.in_dtype == KVQ_F32 ? 4 : 8;
+  int64_t blocks = (n * p.D / per + 4 * 256 - 1) / (4 * 256);
+  if (blocks > 512) blocks = 512;
+  if (blocks < 1) blocks = 1;
+  return (unsigned)blocks;
+}
 hipError_t launch_fp8_absmax_lens(const Plan& p, const void* k_new, const void* v_new, int n,
                                   const int32_t* new_lens, uint32_t* amax, hipStream_t s);
 hipError_t launch_fp8_finalize(const Plan& p, void* arena, const float* k_scale, const float* v_scale,

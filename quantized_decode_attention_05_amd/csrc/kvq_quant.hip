@@ -238,16 +238,11 @@ __global__ void __launch_bounds__(256) fp8_absmax(Plan p, const void* kin, const
                                                    uint32_t* amax) {
   const int h = blockIdx.y, side = blockIdx.z;
   const void* in = side ? vin : kin;
+  // each sequence's run of n * D values (a multiple of 8, 16-byte aligned)
   const int64_t per_seq = (int64_t)n * p.D;
-  const int64_t nel = per_seq * p.B;
-  float m = 0.0f;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nel;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = i / per_seq, r = i % per_seq;
-    float x = load_in(in, (b * p.Hkv + h) * per_seq + r, p.in_dtype);
-    if (p.window) x = stage_f16(x);
-    m = fmaxf(m, fabsf(x));
-  }
+  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+  float m = absmax_runs(in, p.B, p.Hkv, h, per_seq, p.in_dtype, p.window != 0, gid, stride,
+                        [=](int) { return per_seq; });
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float sm[4];
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
@@ -347,10 +342,8 @@ hipError_t launch_fp8_setup(const Plan& p, void* arena, const void* k_new, const
       const hipError_t e = launch_fp8_absmax_lens(p, k_new, v_new, n_new, new_lens, amax, s);
       if (e != hipSuccess) return e;
     } else {
-      const int64_t nel = (int64_t)p.B * n_new * p.D;
-      unsigned chunks = grid_for(nel, 256);
-      if (chunks > 512) chunks = 512;
-      hipLaunchKernelGGL(fp8_absmax, dim3(chunks, p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+      hipLaunchKernelGGL(fp8_absmax, dim3(fp8_absmax_blocks(p, n_new), p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new,
+                         n_new, amax);
     }
   }
   return launch_fp8_finalize(p, arena, k_scale, v_scale, calibrate, s);

@@ -1,0 +1,110 @@
+"""The two ways the quantize kernels obtain rint of the correctly rounded fp32
+quotient (x - z) / s without an IEEE division per element, checked against
+correctly rounded division (numpy's float32 division: the float64 quotient
+rounded to float32, which is correctly rounded because 53 >= 2 * 24 + 2).
+
+1. Correction step (fp16-staged caches): y = RN(1 / s), q0 = RN(d y),
+   r = d - s q0 (exact by FMA), q = RN(q0 + r y) equals RN(d / s).
+2. Reciprocal and test (fp32-staged caches): q = RN(d rcp(s)) with rcp within
+   one ulp; unless |q - rint(q)| >= 1/2 - (qmax + 1) 2^-20, rint(q) equals
+   rint(RN(d / s)) after clamping to the code range.
+
+Inputs: random quotients over the code ranges, quotients planted at
+half-integers and their neighbours a few ulps away, and the values of real
+groups (x at a group's exact midpoints, scale = RN(range / qmax)).
+"""
+from fractions import Fraction
+
+import numpy as np
+
+F32, F64 = np.float32, np.float64
+
+
+def _rn32(fr: Fraction) -> float:
+    """Round a positive Fraction to the nearest fp32 (ties to even; normal range)."""
+    if fr == 0:
+        return 0.0
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    while Fraction(2) ** e > fr:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= fr:
+        e += 1
+    scaled = fr / Fraction(2) ** (e - 23)
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+def _correction_step(d, s):
+    """q of rule 1, with every fp32 operation emulated in float64 and each
+    float64 result either exact or rechecked exactly near an fp32 midpoint."""
+    y = (F64(1) / s.astype(F64)).astype(F32)
+    q0 = (d.astype(F64) * y.astype(F64)).astype(F32)                      # product exact in f64
+    r = (d.astype(F64) - s.astype(F64) * q0.astype(F64)).astype(F32)      # exact difference in f64
+    t = q0.astype(F64) + r.astype(F64) * y.astype(F64)
+    q = t.astype(F32)
+    # t may be rounded in float64: recheck exactly where it lies near an fp32 midpoint
+    u = np.abs(np.nextafter(q, F32(np.inf)).astype(F64) - q.astype(F64))
+    dist = np.minimum(np.abs(t - (q.astype(F64) + u / 2)), np.abs(t - (q.astype(F64) - u / 2)))
+    for i in np.nonzero(dist <= 8 * np.abs(t) * 2.0 ** -52)[0]:
+        exact = Fraction(float(q0[i])) + Fraction(float(r[i])) * Fraction(float(y[i]))
+        q[i] = F32(_rn32(exact))
+    return q
+
+
+def _cases(rng, qmax, n):
+    s = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(-30, 16, n)).astype(F32)
+    yield (s.astype(F64) * rng.uniform(0, qmax + 1, n)).astype(F32), s
+    k = rng.integers(0, qmax + 1, n)
+    base = ((k + 0.5) * s.astype(F64)).astype(F32)
+    for step in (-3, -2, -1, 0, 1, 2, 3):
+        d = base.copy()
+        for _ in range(abs(step)):
+            d = np.nextafter(d, F32(np.inf if step > 0 else -np.inf))
+        yield d, s
+    rng_v = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(-12, 12, n)).astype(F32)
+    sc = (rng_v.astype(F64) / qmax).astype(F32)
+    j = rng.integers(0, 2 * qmax + 1, n)
+    yield (rng_v.astype(F64) * j / (2 * qmax)).astype(F32), sc
+
+
+def test_correction_step_is_correctly_rounded_division():
+    rng = np.random.default_rng(11)
+    for qmax in (3, 15, 255):
+        for d, s in _cases(rng, qmax, 1 << 16):
+            ref = (d.astype(F64) / s.astype(F64)).astype(F32)
+            q = _correction_step(d, s)
+            assert np.array_equal(q, ref), (qmax, int(np.count_nonzero(q != ref)))
+
+
+def test_reciprocal_and_test_rule_gives_the_same_codes():
+    rng = np.random.default_rng(12)
+    for qmax in (3, 15, 255):
+        m = F32((qmax + 1) * 2.0 ** -20)
+        for case, (d, s) in enumerate(_cases(rng, qmax, 1 << 16)):
+            ref = np.clip(np.rint((d.astype(F64) / s.astype(F64)).astype(F32)), 0, qmax)
+            for ulp in (-1, 0, 1):                      # a reciprocal within one ulp either way
+                rs = (F64(1) / s.astype(F64)).astype(F32)
+                if ulp:
+                    rs = np.nextafter(rs, F32(np.inf if ulp > 0 else -np.inf))
+                q = (d.astype(F64) * rs.astype(F64)).astype(F32)
+                r = np.rint(q)
+                ok = np.abs((q - r).astype(F32)) < F32(0.5) - m
+                got = np.where(ok, np.clip(r, 0, qmax), ref)     # rejected codes take the division
+                assert np.array_equal(got, ref), (qmax, ulp)
+                if case == 0:                            # random quotients: the test rarely rejects
+                    assert ok.mean() > 0.99
+
+
+def test_planted_mistake_fails():
+    """Dropping the correction (q = RN(d y)) is not correctly rounded: the
+    check above would catch a kernel that skipped it."""
+    rng = np.random.default_rng(13)
+    wrong = 0
+    for d, s in _cases(rng, 15, 1 << 14):
+        y = (F64(1) / s.astype(F64)).astype(F32)
+        q0 = (d.astype(F64) * y.astype(F64)).astype(F32)
+        wrong += int(np.count_nonzero(q0 != (d.astype(F64) / s.astype(F64)).astype(F32)))
+    assert wrong > 0
