@@ -54,6 +54,7 @@ struct AppendArgs {
   int64_t cap;               // a sequence's range must end at or before this
   int32_t units_q;           // work-groups per (sequence, head) that take quantize units
   int32_t phases;            // bit 0: quantize units run, bit 1: ring units run
+  int32_t x0;                // unit index of the launch's first work item (a launch of ring units only starts at units_q)
   float one;                 // 1.0f (an operand the compiler cannot fold)
 };
 
@@ -195,16 +196,42 @@ __device__ __forceinline__ void load_kv_granules(const Plan& p, const AppendArgs
   }
 }
 
+// 1 / s rounded once for an FP8 per-head scale s in [2^-80, 2^80], else NaN
+// (then fp8_quot divides).
+__device__ __forceinline__ float fp8_recip(float s) {
+  return fabsf(s) >= 0x1p-80f && fabsf(s) <= 0x1p80f ? 1.0f / s : __builtin_nanf("");
+}
+
+// x / s rounded once, given ys = fp8_recip(s): x is first clamped to
+// +-2^17 s (exact; every FP8 code saturates beyond 2^17), then q0 = x ys,
+// r = x - s q0 (exact by FMA) and q0 + r ys rounded once is the correctly
+// rounded quotient (the correction step of Markstein's division).  With s in
+// [2^-80, 2^80] every step stays in the normal range wherever the quotient
+// reaches an FP8 rounding boundary (|x / s| >= 2^-17); below that the code
+// is a signed zero whatever the last bits.  The correction never changes the
+// quotient's sign, but for x = -0 it yields +0 (r = +0, +0 + -0 = +0), so the
+// sign is taken from x: FP8 codes keep the sign of zero.  ys = NaN (a scale
+// outside that range, uniform per head) divides.
+__device__ __forceinline__ float fp8_quot(float x, float s, float ys) {
+  if (ys != ys) return x / s;
+  const float lim = s * 0x1p17f;
+  const float xc = fminf(fmaxf(x, -lim), lim);
+  const float q0 = xc * ys;
+  const float r = __builtin_fmaf(-q0, s, xc);
+  return __builtin_copysignf(__builtin_fmaf(r, ys, q0), xc);
+}
+
 // Code field (masked to the format's bits) of value x under scale s (rs =
-// recip_or_nan(s)) and zero z; S >= 0 fixes the scheme at compile time.
+// recip_or_nan(s) for INT schemes, fp8_recip(s) for FP8) and zero z; S >= 0
+// fixes the scheme at compile time.
 template <int S>
 __device__ __forceinline__ uint32_t code_t(const SideFmt& f, float x, float s, float rs, float z) {
   switch (S >= 0 ? S : f.scheme) {
     case KVQ_NONE:
       if (f.bits == 16) { const _Float16 hv = (_Float16)x; return (uint32_t)__builtin_bit_cast(uint16_t, hv); }
       return __float_as_uint(x);
-    case KVQ_FP8_E4M3: return e4m3_encode(x / s);
-    case KVQ_FP8_E5M2: return e5m2_encode(x / s);
+    case KVQ_FP8_E4M3: return e4m3_encode(fp8_quot(x, s, rs));
+    case KVQ_FP8_E5M2: return e5m2_encode(fp8_quot(x, s, rs));
     case KVQ_INT_SYM: {
       const float r = fminf(fmaxf(rint_quot(x, s, rs, 128.0f * 0x1p-20f), -127.0f), 127.0f);
       return (uint32_t)(int32_t)r & 0xFFu;
@@ -396,6 +423,7 @@ __device__ __forceinline__ void quantize_unit(const Plan& p, const AppendArgs& a
       __syncthreads();
     }
     const float fp8s = is_fp8(fk.scheme) ? ((const float*)(a.arena + fk.scale))[h] : 1.0f;
+    const float fp8r = fp8_recip(fp8s);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int64_t t = u0 + tq + TPP * i;
@@ -424,7 +452,7 @@ __device__ __forceinline__ void quantize_unit(const Plan& p, const AppendArgs& a
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { s[j] = fp8s; z[j] = 0.0f; rs[j] = 1.0f; }
+        for (int j = 0; j < 8; ++j) { s[j] = fp8s; z[j] = 0.0f; rs[j] = fp8r; }
       }
       if (!ok) continue;
       const int32_t pg = page_of(p, a.pm, b, t);
@@ -474,7 +502,7 @@ __device__ __forceinline__ void quantize_unit(const Plan& p, const AppendArgs& a
           if (pg >= 0) store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, t), 8 * cb), sv, zv);
         }
       }
-      const float rv = v_int ? recip_or_nan(sv) : 1.0f;
+      const float rv = v_int ? recip_or_nan(sv) : fp8_recip(sv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) sh.vt[8 * cb + j][tk] = ok ? (code_t<-1>(fv, x[j], sv, rv, zv) & vmask) : 0u;
     }
@@ -584,7 +612,7 @@ __global__ void __launch_bounds__(kAppendThreads) append_units(Plan p, AppendArg
   const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + nb);
   const int64_t u_first = (q_lo / U) * U;
   const int64_t n_qu = q_hi > q_lo ? (q_hi - u_first + U - 1) / U : 0;
-  const int64_t x = blockIdx.x;
+  const int64_t x = (int64_t)blockIdx.x + a.x0;
   if (x < a.units_q) {
     if (x >= n_qu || !(a.phases & 1)) return;
     const int64_t u0 = u_first + x * U;
@@ -691,7 +719,7 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
   const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + nb);
   const int64_t u_first = q_lo & ~(int64_t)31;
   const int64_t n_qu = q_hi > q_lo ? (q_hi - u_first + 31) / 32 : 0;
-  const int64_t x = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t x = (int64_t)blockIdx.x * 4 + wave + a.x0;
   const int64_t bh = (int64_t)b * p.Hkv + h;
 
   if (x >= a.units_q) {
@@ -762,8 +790,9 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
       token_groups<KS>(fk, xk, st, zt, rt);
     } else {
       const float s8 = is_fp8(ksch) ? ((const float*)(a.arena + fk.scale))[h] : 1.0f;
+      const float r8 = fp8_recip(s8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { st[i] = s8; zt[i] = 0.0f; rt[i] = 1.0f; }
+      for (int i = 0; i < 8; ++i) { st[i] = s8; zt[i] = 0.0f; rt[i] = r8; }
     }
     if (pg >= 0) {
 #pragma unroll
@@ -794,8 +823,9 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
                           vs[i], vz[i]);
   } else {
     const float s8 = is_fp8(vsch) ? ((const float*)(a.arena + fv.scale))[h] : 1.0f;
+    const float r8 = fp8_recip(s8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { vs[i] = s8; vz[i] = 0.0f; vr[i] = 1.0f; }
+    for (int i = 0; i < 8; ++i) { vs[i] = s8; vz[i] = 0.0f; vr[i] = r8; }
   }
   if (pg < 0) return;
   uint32_t valid = 0;
@@ -973,7 +1003,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + nb);
   const int64_t u_first = q_lo & ~(int64_t)31;
   const int64_t n_qu = q_hi > q_lo ? (q_hi - u_first + 31) / 32 : 0;
-  const int64_t x = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t x = (int64_t)blockIdx.x * 4 + wave + a.x0;
   const int64_t bh = (int64_t)b * p.Hkv + h;
   if (x >= a.units_q) {
     if (a.phases & 2) wave_ring_block(p, a, b, h, t0, nb, q_hi, x - a.units_q, cb, r);
@@ -1151,7 +1181,6 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
   const int64_t w = p.Rs > 0 ? p.Rs : 0;
   a.units_q = (int32_t)((n + w + U - 1) / U + 2);
   const int64_t units_r = p.window ? ((n < w ? n : w) + 31) / 32 + 1 : 0;
-  const dim3 grid((unsigned)(a.units_q + units_r), p.Hkv, p.B);
   const dim3 blk(kAppendThreads);
   // A fold reads window tokens [q_lo, t0) from the ring while the call writes
   // its own window tokens [w_lo, t0 + n) into slots t mod Rs.  Two such tokens
@@ -1163,12 +1192,17 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
   // one wavefront per 32-token unit where the format allows (D = 128, value
   // codes of at most 8 bits): four units per work-group
   const bool wave_units = U == 32 && p.D == 128 && p.v.bits <= 8;
-  const dim3 grid_w((unsigned)((a.units_q + units_r + 3) / 4), p.Hkv, p.B);
   // keys per channel and values per token, both asymmetric integers (the
   // recipe of the "Different Axes" page)
   const bool kivi = p.k.scheme == KVQ_INT_ASYM && p.k.axis == KVQ_PER_CHANNEL && p.v.scheme == KVQ_INT_ASYM;
+  // a launch of one phase covers only that phase's units
   auto go = [&](int phases) {
     a.phases = phases;
+    const int64_t first = phases == 2 ? a.units_q : 0;
+    const int64_t last = phases == 1 ? a.units_q : a.units_q + units_r;
+    a.x0 = (int32_t)first;
+    const dim3 grid((unsigned)(last - first), p.Hkv, p.B);
+    const dim3 grid_w((unsigned)((last - first + 3) / 4), p.Hkv, p.B);
     if (wave_units) {
       if (kivi && (p.window || p.in_dtype == KVQ_F16))
         hipLaunchKernelGGL(append_kivi_h, grid_w, blk, 0, s, p, a);

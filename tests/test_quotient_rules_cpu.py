@@ -108,3 +108,40 @@ def test_planted_mistake_fails():
         q0 = (d.astype(F64) * y.astype(F64)).astype(F32)
         wrong += int(np.count_nonzero(q0 != (d.astype(F64) / s.astype(F64)).astype(F32)))
     assert wrong > 0
+
+
+def test_correction_step_over_the_fp8_scale_range():
+    """The FP8 encoders take x / s through the same correction step, with
+    per-head scales s in [2^-80, 2^80], quotients of either sign in
+    [2^-17, 2^17] (below, every code is a signed zero; above, x is clamped to
+    2^17 s first, where every code saturates)."""
+    rng = np.random.default_rng(14)
+    n = 1 << 16
+    for lo, hi in ((-80, -40), (-40, 0), (0, 40), (40, 80)):
+        s = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(lo, hi, n)).astype(F32)
+        q = rng.choice([-1.0, 1.0], n) * 2.0 ** rng.uniform(-17, 17, n)
+        x = (s.astype(F64) * q).astype(F32)
+        sign = np.sign(x)
+        got = _correction_step(np.abs(x), s) * sign.astype(F32)
+        ref = (x.astype(F64) / s.astype(F64)).astype(F32)
+        assert np.array_equal(got, ref), (lo, hi)
+
+
+def test_correction_step_loses_the_sign_of_zero_and_copysign_restores_it():
+    """For x = -0 the correction step gives +0 (q0 = -0, r = -0 - s * -0 = +0,
+    q = +0 * y + -0 = +0), while -0 / s = -0 and FP8 keeps the sign of zero
+    (the E4M3 / E5M2 code of -0 is 0x80): the kernels take the sign from x."""
+    s = F32(0.0105)
+    y = F32(1) / s
+    x = F32(-0.0)
+    q0 = F32(x * y)
+    r = F32(x - F32(s * q0))
+    q = F32(q0 + F32(r * y))
+    assert np.signbit(F32(x / s)) and not np.signbit(q)
+    assert np.signbit(np.copysign(q, x))
+    # copysign changes nothing for nonzero quotients: the correction never crosses zero
+    rng = np.random.default_rng(15)
+    xs = (rng.standard_normal(1 << 16) * 10.0 ** rng.uniform(-3, 3, 1 << 16)).astype(F32)
+    ss = np.full(xs.shape, s, F32)
+    q = _correction_step(np.abs(xs), ss) * np.sign(xs).astype(F32)
+    assert np.array_equal(np.signbit(q), np.signbit(xs))
