@@ -304,6 +304,8 @@ __device__ __forceinline__ u32 key_code_reg(const u32* w, int r) {
   } else if constexpr (KF == INT4) {
     const u32 x = w[r >> 2];
     return fp8_pair(r & 1 ? (x >> 4) & 0x0F0F0F0Fu : x & 0x0F0F0F0Fu, r >> 1);
+  } else if constexpr (is_f8(KF)) {
+    return f8_pair<KF>(w[r >> 1], r & 1);   // channels 2r, 2r + 1: bytes (0, 1) or (2, 3)
   } else {
     const u32 src = w[r >> 1];
     const int sh = 16 * (r & 1);
@@ -448,7 +450,8 @@ attn_mfma(Plan p, Args a) {
   // rows and (pre-RoPE keys) the step's coarse cos/sin row.
   constexpr int KROW = D * KB / 8;
   constexpr int SZ_K = 32 * KROW, SZ_V = 32 * D * VB / 8;
-  constexpr int SZ_VM = VINT ? 2 * 32 * VG * 4 : 0, SZ_KM = KINT ? 2 * D * 4 : 0, SZ_KT = ROPE ? 64 * 8 : 0;
+  // (pre-RoPE FP8 keys: no key metadata, but the region holds the step's pair coefficients)
+  constexpr int SZ_VM = VINT ? 2 * 32 * VG * 4 : 0, SZ_KM = (KINT || ROPE) ? 2 * D * 4 : 0, SZ_KT = ROPE ? 64 * 8 : 0;
   constexpr int OFF_V = SZ_K, OFF_VM = OFF_V + SZ_V, OFF_KM = OFF_VM + SZ_VM, OFF_KT = OFF_KM + SZ_KM;
   constexpr int SLOT = OFF_KT + SZ_KT;
   // query rows: up to 16 heads per kv head with one value group (the PV rows
@@ -720,7 +723,7 @@ attn_mfma(Plan p, Args a) {
       if constexpr (VG == 8) pvm1 += 32 * VG * vesz;
     }
     if constexpr (KINT) { if (group_ends) pkm += D * kesz; }
-    if constexpr (ROPE) prp += 64 * 8;
+    if constexpr (ROPE) prp += 64 * 8 * STRIDE;
   };
   // Registers of a quantized step from its LDS slot.
   auto read_slot = [&](int sl, StepData<KDW, VDW, VINT ? 8 : 1>& d) __attribute__((always_inline)) {
@@ -1097,8 +1100,13 @@ attn_mfma(Plan p, Args a) {
         uint8_t* st_l = ring + sl * SLOT;
         const float2 cs2 = ((const float2*)(st_l + OFF_KT))[lane];
         const int mo = 16 * km_pos(lane >> 1) + 8 * (lane & 1);
-        float2 s2 = *(const float2*)(st_l + OFF_KM + mo);
-        float2 z2 = *(const float2*)(st_l + OFF_KM + 4 * D + mo);
+        // FP8 keys: codes are the values (s = 1, z = 0); the per-head scale
+        // sits in the query operand
+        float2 s2 = make_float2(1.0f, 1.0f), z2 = make_float2(0.0f, 0.0f);
+        if constexpr (KINT) {
+          s2 = *(const float2*)(st_l + OFF_KM + mo);
+          z2 = *(const float2*)(st_l + OFF_KM + 4 * D + mo);
+        }
         asm volatile("" ::: "memory");   // every lane's reads before any lane's writes
         if constexpr (KF == INT2) {
           // codes arrive as 1 + c 2^(p - 10): x = s c + z = (s f) h + (z - s f), f = 2^(10 - p)
@@ -1205,7 +1213,6 @@ bool mfma_supported(const Plan& p) {
   if (p.D != 128 || p.n_rep > 16) return false;
   const int kf = kfmt(p), vf = vfmt(p);
   if (kf < 0 || vf < 0) return false;
-  if (p.pre_rope && is_f8(kf)) return false;
   // E5M2 pairs only with FP8 values / keys (other mixes run the generic kernel)
   if ((kf == BF8 || vf == BF8) && !(is_f8(kf) && is_f8(vf))) return false;
   // PV rows are (value group, head) pairs: 16 in one A operand, or 32 in two
@@ -1228,7 +1235,7 @@ static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
     }
   }
   if (p.pre_rope) {
-    if constexpr (!is_f8(KF)) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, false>), grid, dim3(256), page_lds(a), s, p, a);
+    hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, false>), grid, dim3(256), page_lds(a), s, p, a);
   } else {
     hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, false>), grid, dim3(256), page_lds(a), s, p, a);
   }

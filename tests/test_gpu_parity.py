@@ -36,6 +36,11 @@ FORMATS = [
     ("prerope_int2ch32_int2tok32_R32", dict(k=(A, 2, CH, 32), v=(A, 2, TOK, 32), R=32, pre_rope=True)),
     ("prerope_int4ch128_R128", dict(k=(A, 4, CH, 128), v=(A, 4, TOK, 0), R=128, pre_rope=True,
                                     rope_base=500.0)),
+    # FP8 keys cached before RoPE: both FP8 (wavefronts take every fourth step),
+    # FP8 keys with INT values and a window, and E5M2
+    ("prerope_fp8_fp8", dict(k=(F8, 8, 0, 0), v=(F8, 8, 0, 0), R=0, pre_rope=True)),
+    ("prerope_fp8_int4tok32_R32", dict(k=(F8, 8, 0, 0), v=(A, 4, TOK, 32), R=32, pre_rope=True)),
+    ("prerope_e5m2_e5m2_R32", dict(k=(E5, 8, 0, 0), v=(E5, 8, 0, 0), R=32, pre_rope=True)),
 ]
 ONE_SHOT = [
     ("sym8ten_sym8ten", dict(k=(S, 8, TEN, 0), v=(S, 8, TEN, 0))),
