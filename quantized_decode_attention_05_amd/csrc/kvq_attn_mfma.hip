@@ -1213,8 +1213,6 @@ bool mfma_supported(const Plan& p) {
   if (p.D != 128 || p.n_rep > 16) return false;
   const int kf = kfmt(p), vf = vfmt(p);
   if (kf < 0 || vf < 0) return false;
-  // E5M2 pairs only with FP8 values / keys (other mixes run the generic kernel)
-  if ((kf == BF8 || vf == BF8) && !(is_f8(kf) && is_f8(vf))) return false;
   // PV rows are (value group, head) pairs: 16 in one A operand, or 32 in two
   // (8 heads x 4 value groups, INT2 / INT4 codes)
   if (p.n_rep * vgroups(p) <= 16) return true;
@@ -1257,19 +1255,12 @@ static void launch_kv(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
 
 template <int KF>
 static void launch_k(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
-  if constexpr (KF == BF8) {            // E5M2 keys: FP8-class values only
-    if (vfmt(p) == BF8) launch_kv<KF, BF8>(p, grid, s, a);
-    else launch_kv<KF, FP8>(p, grid, s, a);
-  } else {
-    switch (vfmt(p)) {
-      case INT2: launch_kv<KF, INT2>(p, grid, s, a); break;
-      case INT4: launch_kv<KF, INT4>(p, grid, s, a); break;
-      case INT8: launch_kv<KF, INT8>(p, grid, s, a); break;
-      case BF8:
-        if constexpr (KF == FP8) launch_kv<KF, BF8>(p, grid, s, a);
-        break;
-      default: launch_kv<KF, FP8>(p, grid, s, a); break;
-    }
+  switch (vfmt(p)) {
+    case INT2: launch_kv<KF, INT2>(p, grid, s, a); break;
+    case INT4: launch_kv<KF, INT4>(p, grid, s, a); break;
+    case INT8: launch_kv<KF, INT8>(p, grid, s, a); break;
+    case BF8: launch_kv<KF, BF8>(p, grid, s, a); break;
+    default: launch_kv<KF, FP8>(p, grid, s, a); break;
   }
 }
 
