@@ -54,7 +54,7 @@ struct AppendArgs {
   int64_t cap;               // a sequence's range must end at or before this
   int32_t units_q;           // work-groups per (sequence, head) that take quantize units
   int32_t phases;            // bit 0: quantize units run, bit 1: ring units run
-  int32_t x0;                // unit index of the launch's first work item (a launch of ring units only starts at units_q)
+  int32_t x0;                // index of the launch's first work item (unit, or wavefront slot of append_kivi_h)
   float one;                 // 1.0f (an operand the compiler cannot fold)
 };
 
@@ -991,40 +991,53 @@ __device__ __forceinline__ void rows_minmax_h(uint32_t& mn, uint32_t& mx) {
   mx = as_u32(__builtin_elementwise_max(as_h2(r[0]), as_h2(r[1])));
 }
 
+// W = Gt / 32 wavefronts share one key group (unit) of Gt tokens; wavefront
+// s of a unit takes its tokens 32 s .. 32 s + 31.  With W > 1 the key
+// channels' min / max combine across the unit's wavefronts through LDS, and
+// every wavefront of the work-group (ring units and idle ones too) reaches
+// that one barrier.  Launch slots count wavefronts: units_q * W quantize
+// slots, then one slot per ring unit.
+template <int W>
 __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   constexpr int D = 128;
+  static_assert(W == 1 || W == 2 || W == 4, "units of 32, 64 or 128 tokens");
+  __shared__ uint32_t red[W > 1 ? 4 : 1][2][64];   // per wavefront: channel-pair min / max (packed fp16)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.y, b = blockIdx.z;
   const int cb = lane & 15, r = lane >> 4;        // channels 8 cb.., tokens 8 r..
   const int64_t t0 = a.seq_lens ? (int64_t)a.seq_lens[b] : a.t0;
   int64_t nb = a.new_lens ? (int64_t)a.new_lens[b] : (int64_t)a.n;
   if (nb > a.n) nb = a.n;
-  if (t0 < 0 || nb <= 0 || t0 + nb > a.cap) return;
+  if (t0 < 0 || nb <= 0 || t0 + nb > a.cap) return;   // uniform over the work-group
+  const int64_t U = 32 * W;
   const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + nb);
-  const int64_t u_first = q_lo & ~(int64_t)31;
-  const int64_t n_qu = q_hi > q_lo ? (q_hi - u_first + 31) / 32 : 0;
-  const int64_t x = (int64_t)blockIdx.x * 4 + wave + a.x0;
+  const int64_t u_first = (q_lo / U) * U;
+  const int64_t n_qu = q_hi > q_lo ? (q_hi - u_first + U - 1) / U : 0;
+  const int64_t slot = (int64_t)blockIdx.x * 4 + wave + a.x0;
+  const int64_t q_slots = (int64_t)a.units_q * W;
   const int64_t bh = (int64_t)b * p.Hkv + h;
-  if (x >= a.units_q) {
-    if (a.phases & 2) wave_ring_block(p, a, b, h, t0, nb, q_hi, x - a.units_q, cb, r);
-    return;
-  }
-  if (!(a.phases & 1) || x >= n_qu) return;
-  const int64_t u0 = u_first + 32 * x;
-  const int64_t v_lo = u0 > q_lo ? u0 : q_lo, v_hi = u0 + 32 < q_hi ? u0 + 32 : q_hi;
-  const int32_t pg = page_of(p, a.pm, b, u0);     // the unit's page (units never straddle pages)
+  const bool ring = slot >= q_slots;
+  const int64_t x = slot / W;                      // unit
+  const int s = (int)(slot % W);                   // the wavefront's 32 tokens in it
+  const bool active = !ring && (a.phases & 1) && x < n_qu;
+  if (ring && (a.phases & 2)) wave_ring_block(p, a, b, h, t0, nb, q_hi, slot - q_slots, cb, r);
+  if (W == 1 && !active) return;
+  const int64_t u0 = u_first + U * x;              // the unit (key group)
+  const int64_t us = u0 + 32 * s;                  // this wavefront's tokens
+  const int64_t v_lo = us > q_lo ? us : q_lo, v_hi = us + 32 < q_hi ? us + 32 : q_hi;
+  const int32_t pg = active ? page_of(p, a.pm, b, u0) : -1;   // units never straddle pages
   bool ok[8];
   uint32_t hk[8][4], hv[8][4];
-  if (u0 >= t0 && v_lo == u0 && v_hi == u0 + 32) {
-    // a whole unit of new tokens (every unit of a prefill)
+  if (active && us >= t0 && v_lo == us && v_hi == us + 32) {
+    // 32 new tokens (every wavefront of a prefill)
 #pragma unroll
     for (int i = 0; i < 8; ++i) ok[i] = true;
-    load_unit_h(p, a, b, h, u0, t0, cb, r, hk, hv);
+    load_unit_h(p, a, b, h, us, t0, cb, r, hk, hv);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t t = u0 + 8 * r + i;
-      ok[i] = t >= v_lo && t < v_hi;
+      const int64_t t = us + 8 * r + i;
+      ok[i] = active && t >= v_lo && t < v_hi;
       if (ok[i]) {
         load_granule_h<SIDE_K>(p, a, b, h, t, t0, 8 * cb, hk[i]);
         load_granule_h<SIDE_V>(p, a, b, h, t, t0, 8 * cb, hv[i]);
@@ -1036,11 +1049,11 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   }
   const float one = a.one;
 
-  // ---- keys: one whole key group of 32 tokens (every token valid) ----
+  // ---- keys: one whole key group of U tokens (every token valid) ----
   {
     const SideFmt& fk = p.k;
     const float qmax = (float)((1 << fk.bits) - 1);
-    float sc[8], zc[8], rc[8];
+    uint32_t umn[4], umx[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       h2_t mn = as_h2(hk[0][m]), mx = mn;
@@ -1049,17 +1062,42 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
         mn = __builtin_elementwise_min(mn, as_h2(hk[i][m]));
         mx = __builtin_elementwise_max(mx, as_h2(hk[i][m]));
       }
-      uint32_t umn = as_u32(mn), umx = as_u32(mx);
-      rows_minmax_h(umn, umx);
+      umn[m] = as_u32(mn);
+      umx[m] = as_u32(mx);
+      rows_minmax_h(umn[m], umx[m]);
+    }
+    if constexpr (W > 1) {
+      if (r == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { red[wave][0][4 * cb + m] = umn[m]; red[wave][1][4 * cb + m] = umx[m]; }
+      }
+      __syncthreads();
+      if (!active) return;
+      const int w0 = (wave / W) * W;               // the unit's first wavefront in the work-group
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        h2_t mn = as_h2(red[w0][0][4 * cb + m]), mx = as_h2(red[w0][1][4 * cb + m]);
+#pragma unroll
+        for (int k = 1; k < W; ++k) {
+          mn = __builtin_elementwise_min(mn, as_h2(red[w0 + k][0][4 * cb + m]));
+          mx = __builtin_elementwise_max(mx, as_h2(red[w0 + k][1][4 * cb + m]));
+        }
+        umn[m] = as_u32(mn);
+        umx[m] = as_u32(mx);
+      }
+    }
+    float sc[8], zc[8], rc[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int j = 2 * m + e;
-        meta_values(fk, (float)as_h2(umn)[e], (float)as_h2(umx)[e], &sc[j], &zc[j]);
+        meta_values(fk, (float)as_h2(umn[m])[e], (float)as_h2(umx[m])[e], &sc[j], &zc[j]);
         rc[j] = 1.0f / sc[j];
       }
     }
     if (pg >= 0) {
-      if (r == 0) {
+      if (r == 0 && s == 0) {
         const int64_t mi = meta_index_row(p, fk, bh, h, row_of(p, pg, h, u0), 8 * cb);   // 8 consecutive entries
         if (fk.meta16) {
           *(uint4*)((_Float16*)(a.arena + fk.scale) + mi) =
@@ -1075,7 +1113,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
           pz[1] = make_float4(zc[4], zc[5], zc[6], zc[7]);
         }
       }
-      uint8_t* krow0 = a.arena + fk.codes + row_of(p, pg, h, u0 + 8 * r) * p.k_row_bytes;
+      uint8_t* krow0 = a.arena + fk.codes + row_of(p, pg, h, us + 8 * r) * p.k_row_bytes;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         _Float16 xh[8];
@@ -1103,7 +1141,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
     meta_values(fv, fmn, fmx, &vs[i], &vz[i]);
     vr[i] = 1.0f / vs[i];
     if (ok[i] && pg >= 0 && (cb % (fv.group / 8)) == 0)
-      store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, u0 + 8 * r + i), 8 * cb),
+      store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, us + 8 * r + i), 8 * cb),
                         vs[i], vz[i]);
   }
   if (pg < 0) return;
@@ -1112,7 +1150,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   for (int i = 0; i < 8; ++i) valid |= (ok[i] ? 1u : 0u) << i;
   if (!valid) return;
   const int bits = fv.bits;
-  uint8_t* blk = a.arena + fv.codes + (row_of(p, pg, h, u0) >> 5) * p.v_block_bytes;
+  uint8_t* blk = a.arena + fv.codes + (row_of(p, pg, h, us) >> 5) * p.v_block_bytes;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = 8 * cb + j, n = c & 15, iw = c >> 4;
@@ -1195,18 +1233,31 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
   // keys per channel and values per token, both asymmetric integers (the
   // recipe of the "Different Axes" page)
   const bool kivi = p.k.scheme == KVQ_INT_ASYM && p.k.axis == KVQ_PER_CHANNEL && p.v.scheme == KVQ_INT_ASYM;
-  // a launch of one phase covers only that phase's units
+  // fp16-staged caches of that recipe: W = U / 32 wavefronts per unit
+  const bool kivi_h = kivi && (p.window || p.in_dtype == KVQ_F16) && p.D == 128 && p.v.bits <= 8 &&
+                      (U == 32 || U == 64 || U == 128);
+  // a launch of one phase covers only that phase's units (work items: units,
+  // or wavefront slots for the fp16-staged kernel)
   auto go = [&](int phases) {
     a.phases = phases;
+    if (kivi_h) {
+      const int64_t W = U / 32, q_slots = a.units_q * W;
+      const int64_t first = phases == 2 ? q_slots : 0;
+      const int64_t last = phases == 1 ? q_slots : q_slots + units_r;
+      a.x0 = (int32_t)first;
+      const dim3 grid_s((unsigned)((last - first + 3) / 4), p.Hkv, p.B);
+      if (W == 4) hipLaunchKernelGGL(append_kivi_h<4>, grid_s, blk, 0, s, p, a);
+      else if (W == 2) hipLaunchKernelGGL(append_kivi_h<2>, grid_s, blk, 0, s, p, a);
+      else hipLaunchKernelGGL(append_kivi_h<1>, grid_s, blk, 0, s, p, a);
+      return;
+    }
     const int64_t first = phases == 2 ? a.units_q : 0;
     const int64_t last = phases == 1 ? a.units_q : a.units_q + units_r;
     a.x0 = (int32_t)first;
     const dim3 grid((unsigned)(last - first), p.Hkv, p.B);
     const dim3 grid_w((unsigned)((last - first + 3) / 4), p.Hkv, p.B);
     if (wave_units) {
-      if (kivi && (p.window || p.in_dtype == KVQ_F16))
-        hipLaunchKernelGGL(append_kivi_h, grid_w, blk, 0, s, p, a);
-      else if (kivi)
+      if (kivi)
         hipLaunchKernelGGL((append_wave<KVQ_INT_ASYM, KVQ_INT_ASYM, KVQ_PER_CHANNEL>), grid_w, blk, 0, s, p, a);
       else if (p.k.scheme == KVQ_FP8_E4M3 && p.v.scheme == KVQ_FP8_E4M3)
         hipLaunchKernelGGL((append_wave<KVQ_FP8_E4M3, KVQ_FP8_E4M3, -1>), grid_w, blk, 0, s, p, a);

@@ -643,6 +643,9 @@ attn_mfma(Plan p, Args a) {
   // below from them once the stage has landed
   const bool vm16 = VINT && p.v.meta16, km16 = KINT && p.k.meta16;
   const int vesz = vm16 ? 2 : 4, kesz = km16 ? 2 : 4;
+  // first token past the page the issue side is in (paged caches): the step
+  // loop compares against it instead of dividing by P every step
+  int64_t page_end = 0;
   auto init_ptrs = [&](int64_t t0, int64_t kgrp) __attribute__((always_inline)) {
     // token row of t0: through this split's page table, or (b, h)'s own rows
     int64_t tr;
@@ -650,6 +653,7 @@ attn_mfma(Plan p, Args a) {
       // every issued step lies below the split's end, inside the table; the
       // clamp only keeps set-up lookups of unused pointers inside the array
       const int64_t j = t0 / p.P;
+      page_end = (j + 1) * p.P;
       int64_t jj = j - blk0;
       jj = jj < 0 ? 0 : (jj > kMaxSplitPages - 1 ? kMaxSplitPages - 1 : jj);
       tr = ((int64_t)page_s[jj] * p.Hkv + kvh) * p.P + (t0 - j * p.P);
@@ -1068,9 +1072,10 @@ attn_mfma(Plan p, Args a) {
         advance_ptrs(ends);
       }
       // a paged cache continues on another page: pointers from the page table
+      // (steps only move forward, so leaving the page means passing its end)
       if (paged) {
         const int64_t nxt = i_grp * kG + i_rem;
-        if (nxt < iss_end && nxt / p.P != pos / p.P) init_ptrs(nxt, i_grp);
+        if (nxt < iss_end && nxt >= page_end) init_ptrs(nxt, i_grp);
       }
     };
 #pragma unroll
