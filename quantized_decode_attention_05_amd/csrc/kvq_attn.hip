@@ -174,56 +174,64 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
   }
 }
 
-// Pass 2: one work-group of four wavefronts per (query head, sequence).  Each
-// wavefront reduces M = max_s m_s and L = sum_s 2^(m_s - M) l_s over all
-// splits with cross-lane shuffles (no barriers); wavefront w then accumulates
-// the splits s = w (mod 4) for every channel (two per lane when D = 128), with
-// several splits' loads in flight, and the four partial sums meet in LDS.
-__device__ __forceinline__ float merge_wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float merge_wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
+// Pass 2: one work-group of four wavefronts per (query head, sequence).
+// Wavefront w takes the splits s = w (mod 4) in one pass over their partials,
+// keeping a running maximum m, mass l and weighted sum (two channels per lane
+// when D = 128) that it rescales whenever the maximum rises, with several
+// splits' loads in flight; the four wavefronts' states meet in LDS, rescaled
+// to the common maximum.  (Each partial is read once: no separate passes for
+// the maximum and the mass.)
 __global__ void __launch_bounds__(256) attn_merge(Plan p, const float* ws_o, const float* ws_ml, int S,
                                                   void* out) {
   __shared__ float part[4][128];
+  __shared__ float wml[4][2];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int64_t row = (int64_t)b * p.Hq + hq;
   const float* ml = ws_ml + row * S * 2;
-  float M = kNegBig;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = merge_wave_max(M);
-  float L = 0.0f;
-  for (int s = lane; s < S; s += 64) L += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
-  L = merge_wave_sum(L);
   const float* o = ws_o + row * S * p.D;
-  float a0 = 0.0f, a1 = 0.0f;
-  if (p.D == 128) {
+  const bool d128 = p.D == 128;
+  float m = kNegBig, l = 0.0f, a0 = 0.0f, a1 = 0.0f;
 #pragma unroll 4
-    for (int s = w; s < S; s += 4) {
-      const float wt = exp2f(ml[2 * s] - M);
+  for (int s = w; s < S; s += 4) {
+    const float ms = ml[2 * s], ls = ml[2 * s + 1];
+    float v0, v1 = 0.0f;
+    if (d128) {
       const float2 v = ((const float2*)(o + (int64_t)s * 128))[lane];
-      a0 += wt * v.x;
-      a1 += wt * v.y;
+      v0 = v.x;
+      v1 = v.y;
+    } else {   // D = 64: one channel per lane
+      v0 = o[(int64_t)s * 64 + lane];
     }
+    const float mn = fmaxf(m, ms);
+    const float f0 = exp2f(m - mn), f1 = exp2f(ms - mn);
+    l = l * f0 + ls * f1;
+    a0 = a0 * f0 + v0 * f1;
+    a1 = a1 * f0 + v1 * f1;
+    m = mn;
+  }
+  if (d128) {
     part[w][2 * lane] = a0;
     part[w][2 * lane + 1] = a1;
-  } else {   // D = 64: one channel per lane
-#pragma unroll 4
-    for (int s = w; s < S; s += 4) a0 += exp2f(ml[2 * s] - M) * o[(int64_t)s * 64 + lane];
+  } else {
     part[w][lane] = a0;
+  }
+  if (lane == 0) {
+    wml[w][0] = m;
+    wml[w][1] = l;
   }
   __syncthreads();
   if (tid < p.D) {
+    const float M = fmaxf(fmaxf(wml[0][0], wml[1][0]), fmaxf(wml[2][0], wml[3][0]));
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float f = exp2f(wml[k][0] - M);
+      L += wml[k][1] * f;
+      acc += part[k][tid] * f;
+    }
     // a sequence with no tokens (ragged batches) has no mass: output 0
-    const float v = L > 0.0f ? (part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]) / L : 0.0f;
+    const float v = L > 0.0f ? acc / L : 0.0f;
     const int64_t oi = row * p.D + tid;
     if (p.out_dtype == KVQ_F32) ((float*)out)[oi] = v;
     else if (p.out_dtype == KVQ_F16) ((_Float16*)out)[oi] = (_Float16)v;
