@@ -19,21 +19,26 @@
 //    Cache Quantization...", section "Should you quantize keys pre-RoPE or
 //    post-RoPE?").
 //
-// Work split.  One work-group of 256 threads per (unit, kv head, sequence):
-// a quantize unit is one key group (U = Gt tokens; 32 when keys have no token
-// groups), a ring unit is up to 32 window tokens.  Each sequence's range comes
-// from device data (the lengths of a ragged batch) or from the call's uniform
-// t0, so units a sequence does not need exit at once.  A thread owns 16-byte
-// granules of 8 consecutive channels of one token, loaded with 128-bit loads.
-//  - per-channel key groups: min / max over the granules a thread holds, then
-//    over the lanes holding the same channels (cross-lane shuffles), then over
-//    the four wavefronts (LDS); the group's scale / zero-point rows are
-//    written and every thread encodes its elements against them and writes
-//    its part of each packed key row (D * b / 8 bytes per token);
-//  - per-token value groups: min / max over the lanes holding one group's
-//    channels (shuffles); codes go through LDS so that each thread assembles
-//    whole words of the 32-token value block layout (8 tokens of one channel
-//    per word) and no two threads write one byte.
+// Work split.  A quantize unit is one key group of one (sequence, kv head)
+// (U = Gt tokens; 32 when keys have no token groups), a ring unit is up to 32
+// window tokens.  Each sequence's range comes from device data (the lengths
+// of a ragged batch) or from the call's uniform t0, so units a sequence does
+// not need exit at once.  Three kernels share the work items and outputs:
+//  - append_kivi_h<W> (fp16-staged caches, per-channel INT keys, per-token
+//    INT values, D = 128): W = U / 32 wavefronts per unit, each holding 32
+//    tokens as packed fp16 pairs (lane: 8 channels of 8 tokens), key-channel
+//    min / max across the lane's tokens, the token rows (permlane swaps) and,
+//    for W > 1, the unit's wavefronts (LDS); value groups within the lane's
+//    channels and its neighbours; codes by a division-free exact rule;
+//  - append_wave<KS, VS, KAX> (32-token units of other formats, D = 128): the
+//    same lane layout in fp32, one instance per scheme;
+//  - append_units<D, U> (everything else): one 256-thread work-group per
+//    unit, a thread owning 16-byte granules; key channels reduce across the
+//    four wavefronts through LDS, value codes go through LDS so that each
+//    thread assembles whole words of the 32-token value block layout.
+// In every kernel a value word (8 tokens of one channel) has one writer, so
+// no two threads write one byte; whole units of new tokens issue all their
+// loads before using any.
 //
 // Built with -ffp-contract=off: every step rounds once, in the listings' order.
 #include "kvq_internal.h"
