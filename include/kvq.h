@@ -99,7 +99,7 @@ typedef struct kvq_tensor_spec {
 typedef struct kvq_config {
   int32_t batch;          /* B: sequences                                        */
   int32_t num_q_heads;    /* Hq                                                  */
-  int32_t num_kv_heads;   /* Hkv, Hq % Hkv == 0                                  */
+  int32_t num_kv_heads;   /* Hkv, Hq % Hkv == 0, Hq / Hkv <= 256                 */
   int32_t head_dim;       /* D: 64 or 128                                        */
   int64_t max_tokens;     /* capacity per sequence                               */
   int32_t in_dtype;       /* dtype of k_new, v_new and q (enum kvq_dtype)       */

@@ -83,7 +83,7 @@ int make_plan(const kvq_config* cfg, Plan* p) {
   const int D = cfg->head_dim;
   if (cfg->batch < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads < cfg->num_kv_heads) return KVQ_ERR_INVALID_ARG;
   if (cfg->num_q_heads % cfg->num_kv_heads) return KVQ_ERR_INVALID_ARG;
-  if (cfg->num_q_heads / cfg->num_kv_heads > 16) return KVQ_ERR_INVALID_ARG;
+  if (cfg->num_q_heads / cfg->num_kv_heads > kMaxHeadsPerKv) return KVQ_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KVQ_ERR_INVALID_ARG;
   if (cfg->max_tokens < 1 || cfg->max_tokens > ((int64_t)1 << 31)) return KVQ_ERR_INVALID_ARG;
   if (cfg->in_dtype < KVQ_F32 || cfg->in_dtype > KVQ_BF16) return KVQ_ERR_INVALID_ARG;
@@ -410,7 +410,9 @@ int kvq_decode_attention_static(const kvq_config* cfg, const void* arena, int64_
 // launch, 0 = a separate append first (a fold, or a shape the MFMA kernel
 // does not serve).
 static int step_mode(const Plan& p, const AttnPlan& ap, int64_t t0) {
-  if (ap.kernel != 2) return 0;
+  // the appending work-group must be the only reader of its (b, kv head)'s
+  // split: not with several head groups
+  if (ap.kernel != 2 || ap.ngroups != 1) return 0;
   const int64_t q_lo = quantized_tokens(p, t0), q_hi = quantized_tokens(p, t0 + 1);
   if (q_hi == q_lo) return 1;
   if (is_fp8(p.k.scheme) && is_fp8(p.v.scheme) && !p.window && q_hi == q_lo + 1) return 2;

@@ -36,6 +36,9 @@ struct AttnArgs {
   PageMap pm;
   const int32_t* seq_lens;
   int32_t lens_add;
+  // query heads in groups of hg (at most 16) per work-group, ngroups per kv
+  // head (grid y = kv head * ngroups + group)
+  int32_t hg, ngroups;
 };
 
 // Tokens of sequence b and how many of them are quantized.
@@ -65,8 +68,11 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
   __shared__ float m_s[16], l_s[16], alpha_s[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int n_rep = p.n_rep;
+  const int split = blockIdx.x, kvh = blockIdx.y / a.ngroups, b = blockIdx.z;
+  // this work-group's query heads: hb .. hb + n_rep - 1 of the kv head's p.n_rep
+  const int hb = (blockIdx.y - kvh * a.ngroups) * a.hg;
+  const int n_rep = a.hg < p.n_rep - hb ? a.hg : p.n_rep - hb;
+  const int64_t hq0 = (int64_t)b * p.Hq + (int64_t)kvh * p.n_rep + hb;   // first query head
   int64_t T, Tq;
   seq_extent(p, a.seq_lens, a.lens_add, b, a.T, a.Tq, &T, &Tq);
   const int64_t t_begin = (int64_t)split * a.chunk;
@@ -75,7 +81,7 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
 
   for (int e = tid; e < n_rep * D; e += 256) {
     const int r = e / D, c = e % D;
-    const int64_t qi = ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c;
+    const int64_t qi = (hq0 + r) * D + c;
     q_s[r][c] = load_in(a.q, qi, p.in_dtype) * a.qscale;
   }
   if (tid < 16) { m_s[tid] = kNegBig; l_s[tid] = 0.0f; }
@@ -163,12 +169,12 @@ __global__ void __launch_bounds__(256) attn_generic(Plan p, AttnArgs a) {
     const int e = tid + 256 * j;
     const int r = e / D, c = e % D;
     if (r < n_rep) {
-      const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + r;
+      const int64_t hq = hq0 + r;
       a.ws_o[(hq * a.S + split) * D + c] = o_acc[j];
     }
   }
   if (tid < n_rep) {
-    const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + tid;
+    const int64_t hq = hq0 + tid;
     a.ws_ml[(hq * a.S + split) * 2 + 0] = m_s[tid];
     a.ws_ml[(hq * a.S + split) * 2 + 1] = l_s[tid];
   }
@@ -258,10 +264,17 @@ int make_attn_plan(const Plan& p, int64_t T, const kvq_attn_options* opt, AttnPl
   if (kernel == 0) kernel = mfma_supported(p) ? 2 : 1;
   const int64_t unit = 64;
   const int64_t max_splits = cdiv(T, unit);
+  if (kernel == 2) {
+    ap->hg = mfma_head_group(p);
+  } else {   // the generic kernel holds up to 16 query rows
+    const int ng = (int)cdiv(p.n_rep, 16);
+    ap->hg = (int)cdiv(p.n_rep, ng);
+  }
+  ap->ngroups = (int32_t)cdiv(p.n_rep, ap->hg);
   if (splits == 0) {
     // about two work-groups per CU (the MFMA kernel runs at two waves per
     // SIMD), each with a long run of tokens per wavefront
-    const int64_t bh = (int64_t)p.B * p.Hkv;
+    const int64_t bh = (int64_t)p.B * p.Hkv * ap->ngroups;
     const int64_t want = cdiv(kernel == 2 ? 512 : 1024, bh);
     const int64_t min_tokens = (kernel == 2) ? 512 : 128;
     const int64_t by_len = cdiv(T, min_tokens);
@@ -301,6 +314,7 @@ hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena
                             const Ragged* rg) {
   if (app && app->mode != 0 && ap.kernel != 2) return hipErrorInvalidValue;   // MFMA kernel only
   if (app && app->mode != 0 && rg) return hipErrorInvalidValue;               // contiguous only
+  if (app && app->mode != 0 && ap.ngroups != 1) return hipErrorInvalidValue;   // one writer per (b, kv head)
   float* ws_o = (float*)((uint8_t*)ws + ap.ws_o);
   float* ws_ml = (float*)((uint8_t*)ws + ap.ws_ml);
   if (ap.kernel == 2) {
@@ -309,8 +323,8 @@ hipError_t launch_attention(const Plan& p, const AttnPlan& ap, const void* arena
   } else {
     AttnArgs a{(const uint8_t*)arena, q, ws_o, ws_ml, ap.T, ap.Tq, ap.chunk, ap.splits,
                sm_scale * kLog2e, rg ? rg->pm : PageMap{nullptr, 0}, rg ? rg->seq_lens : nullptr,
-               rg ? rg->lens_add : 0};
-    dim3 grid(ap.splits, p.Hkv, p.B);
+               rg ? rg->lens_add : 0, ap.hg, ap.ngroups};
+    dim3 grid(ap.splits, p.Hkv * ap.ngroups, p.B);
     if (p.D == 128) hipLaunchKernelGGL(attn_generic<128>, grid, dim3(256), 0, s, p, a);
     else hipLaunchKernelGGL(attn_generic<64>, grid, dim3(256), 0, s, p, a);
   }

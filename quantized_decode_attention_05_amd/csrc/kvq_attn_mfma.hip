@@ -89,6 +89,9 @@ struct Args {
   PageMap pm;
   const int32_t* seq_lens;
   int32_t lens_add;
+  // query heads in groups of hg per work-group, ngroups groups per kv head
+  // (grid y = kv head * ngroups + group)
+  int32_t hg, ngroups;
 };
 
 __device__ __forceinline__ half8 pack8(u32 a, u32 b, u32 c, u32 d) {
@@ -485,8 +488,11 @@ attn_mfma(Plan p, Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int n_rep = p.n_rep;
+  const int split = blockIdx.x, kvh = blockIdx.y / a.ngroups, b = blockIdx.z;
+  // this work-group's query heads: hb .. hb + n_rep - 1 of the kv head's p.n_rep
+  const int hb = (blockIdx.y - kvh * a.ngroups) * a.hg;
+  const int n_rep = a.hg < p.n_rep - hb ? a.hg : p.n_rep - hb;
+  const int64_t hq0 = (int64_t)b * p.Hq + (int64_t)kvh * p.n_rep + hb;   // first query head
   const int64_t bh = (int64_t)b * p.Hkv + kvh;
   const uint8_t* arena = a.arena;
   // tokens of this sequence (ragged batches: from its length)
@@ -532,7 +538,7 @@ attn_mfma(Plan p, Args a) {
   }
   for (int e = tid; e < n_rep * D; e += 256) {
     const int r = e / D, c = e % D;
-    q_s[r][c] = load_in(a.q, ((int64_t)b * p.Hq + kvh * n_rep + r) * D + c, p.in_dtype) * a.qscale;
+    q_s[r][c] = load_in(a.q, (hq0 + r) * D + c, p.in_dtype) * a.qscale;
   }
   if (paged && hi > lo) {
     const int64_t nblk = (hi - 1) / p.P - blk0 + 1;   // <= kMaxSplitPages (split count)
@@ -1186,7 +1192,7 @@ attn_mfma(Plan p, Args a) {
       L += f * red_ml[w][r][1];
       acc += f * ((const float (*)[D])ring_s[w])[r][c];
     }
-    const int64_t hq = (int64_t)b * p.Hq + kvh * n_rep + r;
+    const int64_t hq = hq0 + r;
     a.ws_o[(hq * a.S + split) * D + c] = acc;
     if (c == 0) {
       a.ws_ml[(hq * a.S + split) * 2 + 0] = M;
@@ -1214,14 +1220,23 @@ static int vfmt(const Plan& p) {
 static int vgroups(const Plan& p) { return is_fp8(p.v.scheme) ? 1 : 128 / p.v.group; }
 
 bool mfma_supported(const Plan& p) {
-  // n_rep > 8 only with one value group (checked below: n_rep * groups <= 16)
-  if (p.D != 128 || p.n_rep > 16) return false;
+  // any number of query heads per kv head: they are split into groups that
+  // fit the PV rows (mfma_head_group), one work-group per group
+  return p.D == 128 && kfmt(p) >= 0 && vfmt(p) >= 0;
+}
+
+// PV rows are (value group, head) pairs: 16 in one A operand, or 32 in two
+// (8 heads x 4 value groups with INT2 / INT4 codes on both sides).  The heads
+// of a kv head are split into the fewest groups that fit, of near-equal size.
+static bool pv2_formats(const Plan& p) {
   const int kf = kfmt(p), vf = vfmt(p);
-  if (kf < 0 || vf < 0) return false;
-  // PV rows are (value group, head) pairs: 16 in one A operand, or 32 in two
-  // (8 heads x 4 value groups, INT2 / INT4 codes)
-  if (p.n_rep * vgroups(p) <= 16) return true;
-  return p.n_rep == 8 && vgroups(p) == 4 && (kf == INT2 || kf == INT4) && (vf == INT2 || vf == INT4);
+  return vgroups(p) == 4 && (kf == INT2 || kf == INT4) && (vf == INT2 || vf == INT4);
+}
+int mfma_head_group(const Plan& p) {
+  if (pv2_formats(p) && p.n_rep % 8 == 0) return 8;
+  const int cap = 16 / vgroups(p);
+  const int ng = (p.n_rep + cap - 1) / cap;
+  return (p.n_rep + ng - 1) / ng;
 }
 
 // dynamic LDS of a launch: the split's page table for paged calls
@@ -1231,7 +1246,7 @@ template <int KF, int VF, int VG>
 static void launch_kvg(const Plan& p, dim3 grid, hipStream_t s, const Args& a) {
   constexpr bool kPV2 = VG == 4 && (KF == INT2 || KF == INT4) && (VF == INT2 || VF == INT4);
   if constexpr (kPV2) {
-    if (p.n_rep * VG > 16) {
+    if (a.hg * VG > 16) {
       if (p.pre_rope) hipLaunchKernelGGL((attn_mfma<KF, VF, true, VG, true, true>), grid, dim3(256), page_lds(a), s, p, a);
       else hipLaunchKernelGGL((attn_mfma<KF, VF, false, VG, false, true>), grid, dim3(256), page_lds(a), s, p, a);
       return;
@@ -1276,8 +1291,8 @@ hipError_t launch_attention_mfma(const Plan& p, const AttnPlan& ap, const void* 
          ap.T, ap.Tq, ap.chunk, ap.splits, sm_scale * kLog2e, -1.0f,
          app ? app->k : nullptr, app ? app->v : nullptr, app ? app->t : 0, app ? app->mode : 0,
          (uint8_t*)arena, rg ? rg->pm : PageMap{nullptr, 0}, rg ? rg->seq_lens : nullptr,
-         rg ? rg->lens_add : 0};
-  dim3 grid(ap.splits, p.Hkv, p.B);
+         rg ? rg->lens_add : 0, ap.hg, ap.ngroups};
+  dim3 grid(ap.splits, p.Hkv * ap.ngroups, p.B);
   switch (kfmt(p)) {
     case INT2: launch_k<INT2>(p, grid, s, a); break;
     case INT4: launch_k<INT4>(p, grid, s, a); break;

@@ -10,6 +10,7 @@ namespace kvq {
 
 constexpr int kVBlock = 32;      // tokens per V code block
 constexpr int kRingAlign = 32;   // ring slots are a multiple of this
+constexpr int kMaxHeadsPerKv = 256;   // query heads per kv head (Hq / Hkv)
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE5M2Max = 57344.0f;
 

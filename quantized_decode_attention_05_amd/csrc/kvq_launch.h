@@ -12,6 +12,9 @@ constexpr int kMaxSplitPages = 256;
 struct AttnPlan {
   int32_t kernel;          // 1 generic, 2 MFMA
   int32_t splits;          // token splits per (b, kv head)
+  // MFMA kernel: the query heads of a kv head are taken in groups of hg by
+  // ngroups work-groups per (b, kv head, split) (the last group may be short)
+  int32_t hg, ngroups;
   int64_t chunk;           // tokens per split (multiple of 64)
   int64_t T, Tq;
   uint64_t ws_o, ws_ml;    // workspace offsets: o [B][Hq][S][D], (m, l) [B][Hq][S][2]
@@ -31,6 +34,9 @@ struct StepAppend {
   int32_t mode;    // 0: none
 };
 bool mfma_supported(const Plan& p);
+// query heads per MFMA work-group (the kernel's PV rows hold at most 16
+// (value group, head) pairs, or 32 with two A operands)
+int mfma_head_group(const Plan& p);
 
 hipError_t launch_rope_tables(const Plan& p, void* arena, hipStream_t s);
 hipError_t launch_fp8_setup(const Plan& p, void* arena, const void* k_new, const void* v_new,

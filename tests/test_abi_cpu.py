@@ -50,7 +50,7 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("bad", [
-    dict(head_dim=96), dict(num_q_heads=7), dict(num_kv_heads=0), dict(num_q_heads=64, num_kv_heads=2),
+    dict(head_dim=96), dict(num_q_heads=7), dict(num_kv_heads=0), dict(num_q_heads=514, num_kv_heads=2),
     dict(k=(K.INT_ASYM, 3, K.PER_CHANNEL, 32)), dict(k=(K.INT_SYM, 4, K.PER_CHANNEL, 0)),
     dict(v=(K.INT_ASYM, 4, K.PER_TOKEN, 24)), dict(v=(K.INT_ASYM, 4, K.PER_TOKEN, 4)),
     dict(k=(K.NONE, 8, 0, 0)), dict(k=(K.FP8_E4M3, 4, 0, 0)), dict(k=(7, 8, 0, 0)),
@@ -203,6 +203,24 @@ def test_workspace_monotone_in_T(fmt):
                 ws = K.kvq_workspace_bytes(cfg, T, kern)
                 assert ws >= prev
                 prev = ws
+
+
+@pytest.mark.parametrize("Hq,Hkv,fmt", [
+    (64, 2, dict()),                                                             # 32 per kv head
+    (33, 1, dict(k=(K.FP8_E4M3, 8, 0, 0), v=(K.FP8_E4M3, 8, 0, 0), residual=0)),  # multi-query
+    (512, 2, dict()),                                                            # the limit, 256
+    (8, 2, dict(v=(K.INT_ASYM, 4, K.PER_TOKEN, 16))),                            # 4 x 8 value groups
+])
+def test_any_heads_per_kv_head_run_on_both_kernels(Hq, Hkv, fmt):
+    """Host-only: query heads beyond one work-group's rows are split into head
+    groups on both kernels, so every such config is accepted and sized, and a
+    decode step with several groups appends before the launch."""
+    cfg = _cfg(num_q_heads=Hq, num_kv_heads=Hkv, **fmt)
+    for kern in (K.KERNEL_GENERIC, K.KERNEL_MFMA):
+        ws = K.kvq_workspace_bytes(cfg, 1000, kern, 3)
+        assert ws >= cfg.batch * Hq * 3 * 128 * 4      # one fp32 row per (sequence, head, split)
+    # every case here has more than one MFMA head group: no step appends in the launch
+    assert not any(K.kvq_decode_step_fused(cfg, t) for t in range(64, 140))
 
 
 def test_decode_step_fusion_query_and_validation():
