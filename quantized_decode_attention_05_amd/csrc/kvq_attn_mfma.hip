@@ -208,11 +208,6 @@ template <int F> struct Bits { static constexpr int v = is_f8(F) ? 8 : F; };
 // the row use it too.
 __device__ __forceinline__ int km_pos(int q) { return q ^ (((q >> 3) & 3) << 1); }
 
-// LDS positions of a channel pair's coefficients (pre-RoPE keys): the 16-byte
-// (u, v) entry and the 8-byte w entry of pair p, which lane group p / 16
-// reads; XOR-ing with the group spreads the four groups over bank groups.
-__device__ __forceinline__ int pc_pos(int p) { return p ^ (((p >> 4) & 3) << 1); }
-__device__ __forceinline__ int pcw_pos(int p) { return 2 * km_pos(p >> 1) + (p & 1); }
 
 // LDS position of the 16-byte granule of token t (its four group scales, or
 // zero-points) when values have four channel groups: lane group g reads tokens
@@ -652,7 +647,7 @@ attn_mfma(Plan p, Args a) {
   // first token past the page the issue side is in (paged caches): the step
   // loop compares against it instead of dividing by P every step
   int64_t page_end = 0;
-  auto init_ptrs = [&](int64_t t0, int64_t kgrp) __attribute__((always_inline)) {
+  auto init_ptrs = [&](int64_t t0) __attribute__((always_inline)) {
     // token row of t0: through this split's page table, or (b, h)'s own rows
     int64_t tr;
     if (paged) {
@@ -691,7 +686,6 @@ attn_mfma(Plan p, Args a) {
     if constexpr (KINT) {
       // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key
       // group; fp16 rows: lanes 0-15 and 16-31
-      (void)kgrp;
       const int64_t mrow = (tr / p.k.group) * D * kesz;
       if (km16) pkm = lane < 16 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 16);
       else pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * km_pos(lane)
@@ -804,6 +798,12 @@ attn_mfma(Plan p, Args a) {
     floatx4 S[2];
     if constexpr (ROPE) {
       const float2* crow = (const float2*)(arena + p.rope) + (32 + (t0 >> 5)) * 64 + 16 * g;
+      // the coefficients of this lane group's 16 pairs in the step's slot, in
+      // pair order: one base per step, each pair's read an immediate offset
+      // from it (lane group g reads pairs 16g..16g+15; the 16 lanes of a group
+      // read one address, a broadcast)
+      const float4* uvb = (const float4*)(ring + cur_slot * SLOT + OFF_KM) + 16 * g;
+      const float2* wvb = (const float2*)(ring + cur_slot * SLOT + OFF_KT) + 16 * g;
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -820,10 +820,9 @@ attn_mfma(Plan p, Args a) {
         float2 wv[4], cc[4];
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-          const int pp = 16 * g + (cp[pr] >> 1);
           if constexpr (!RING) {
-            uv[pr] = ((const float4*)(ring + cur_slot * SLOT + OFF_KM))[pc_pos(pp)];
-            wv[pr] = ((const float2*)(ring + cur_slot * SLOT + OFF_KT))[pcw_pos(pp)];
+            uv[pr] = uvb[cp[pr] >> 1];
+            wv[pr] = wvb[cp[pr] >> 1];
           } else {
             cc[pr] = crow[cp[pr] >> 1];
           }
@@ -1056,32 +1055,31 @@ attn_mfma(Plan p, Args a) {
     // for, read into registers), the next stage is issued into the slot freed
     // by the previous step, then the step is computed.
     // Key groups are tracked incrementally (one division up front): the
-    // issue side (i_grp, i_rem) and the compute side (c_rem) each advance by
-    // one 32-token step per iteration.
+    // issue side (position i_pos, offset i_rem in its key group) and the
+    // compute side (c_rem) each advance by one 32-token step per iteration.
     const int64_t qs_beg = st_beg < qs_end ? st_beg : qs_end;
-    const int64_t kG = KINT ? p.k.group : 32;
-    int64_t i_grp = (lo + qs_beg * 32) / kG;
-    int64_t i_rem = (lo + qs_beg * 32) - i_grp * kG;
-    int64_t c_rem = i_rem;
+    const int kG = KINT ? p.k.group : 32;
+    int64_t i_pos = lo + qs_beg * 32;
+    int i_rem = (int)(i_pos % kG);
+    int c_rem = i_rem;
     const int64_t iss_end = lo + qs_end * 32;   // this wavefront's quantized steps only
-    init_ptrs(i_grp * kG + i_rem, i_grp);
+    init_ptrs(i_pos);
     auto next_issue = [&](int sl_) __attribute__((always_inline)) {
-      const int64_t pos = i_grp * kG + i_rem;
-      if (pos < iss_end) issue(sl_);
+      if (i_pos < iss_end) issue(sl_);
       if constexpr (IL) {
-        i_grp += STRIDE;           // kG = 32: one step per group, i_rem stays 0
+        i_pos += 32 * STRIDE;      // kG = 32: one step per group, i_rem stays 0
         advance_ptrs(true);
       } else {
+        i_pos += 32;
         i_rem += 32;
         const bool ends = i_rem == kG;
-        if (ends) { i_rem = 0; ++i_grp; }
+        if (ends) i_rem = 0;
         advance_ptrs(ends);
       }
       // a paged cache continues on another page: pointers from the page table
       // (steps only move forward, so leaving the page means passing its end)
       if (paged) {
-        const int64_t nxt = i_grp * kG + i_rem;
-        if (nxt < iss_end && nxt >= page_end) init_ptrs(nxt, i_grp);
+        if (i_pos < iss_end && i_pos >= page_end) init_ptrs(i_pos);
       }
     };
 #pragma unroll
@@ -1126,8 +1124,8 @@ attn_mfma(Plan p, Args a) {
           z2.x -= s2.x;
           z2.y -= s2.y;
         }
-        ((float4*)(st_l + OFF_KM))[pc_pos(lane)] = make_float4(s2.x * cs2.x, s2.x * cs2.y, -s2.y * cs2.y, s2.y * cs2.x);
-        ((float2*)(st_l + OFF_KT))[pcw_pos(lane)] =
+        ((float4*)(st_l + OFF_KM))[lane] = make_float4(s2.x * cs2.x, s2.x * cs2.y, -s2.y * cs2.y, s2.y * cs2.x);
+        ((float2*)(st_l + OFF_KT))[lane] =
             make_float2(cs2.x * z2.x - cs2.y * z2.y, cs2.y * z2.x + cs2.x * z2.y);
       }
       next_issue(sl == 0 ? NB - 1 : sl - 1);
