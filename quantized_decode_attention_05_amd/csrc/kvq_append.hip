@@ -226,6 +226,35 @@ __device__ __forceinline__ float fp8_quot(float x, float s, float ys) {
   return __builtin_copysignf(__builtin_fmaf(r, ys, q0), xc);
 }
 
+// FP8 codes of four values x0..x3 under a per-head scale s whose reciprocal
+// ys = fp8_recip(s) is finite, packed in one dword (value k in byte k): the
+// quotient of fp8_quot without its division fallback, saturated at the
+// format's largest finite value by a median (which keeps the sign, also of
+// zero), then converted two at a time by the instruction that rounds to
+// nearest, ties to even (the rounding of e4m3_encode / e5m2_encode).
+template <bool E5>
+__device__ __forceinline__ float fp8_sat_quot(float x, float s, float ys) {
+  const float lim = s * 0x1p17f;
+  const float xc = __builtin_amdgcn_fmed3f(x, -lim, lim);
+  const float q0 = xc * ys;
+  const float r = __builtin_fmaf(-q0, s, xc);
+  const float q = __builtin_copysignf(__builtin_fmaf(r, ys, q0), xc);
+  const float mx = E5 ? kE5M2Max : kE4M3Max;
+  return __builtin_amdgcn_fmed3f(q, -mx, mx);
+}
+template <bool E5>
+__device__ __forceinline__ uint32_t fp8_pack4(float x0, float x1, float x2, float x3, float s, float ys) {
+  const float q0 = fp8_sat_quot<E5>(x0, s, ys), q1 = fp8_sat_quot<E5>(x1, s, ys);
+  const float q2 = fp8_sat_quot<E5>(x2, s, ys), q3 = fp8_sat_quot<E5>(x3, s, ys);
+  if constexpr (E5) {
+    const int w = __builtin_amdgcn_cvt_pk_bf8_f32(q0, q1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(q2, q3, w, true);
+  } else {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+  }
+}
+
 // Code field (masked to the format's bits) of value x under scale s (rs =
 // recip_or_nan(s) for INT schemes, fp8_recip(s) for FP8) and zero z; S >= 0
 // fixes the scheme at compile time.
@@ -711,6 +740,36 @@ __device__ __forceinline__ void wave_ring_block(const Plan& p, const AppendArgs&
 // KS / VS >= 0 fix the key / value scheme and KAX >= 0 the key axis at
 // compile time, so that an instance holds only its own encoder (the whole
 // unrolled body then stays in the instruction cache).
+// FP8 key rows of a wavefront's unit: token 8 r + i of lane (cb, r), channels
+// 8 cb .. 8 cb + 7 (byte j of the row's 8-byte granule cb is channel 8 cb + j).
+template <bool E5>
+__device__ __forceinline__ void fp8_rows(const float (&x)[8][8], const bool (&ok)[8], float s, float ys,
+                                         uint8_t* row0, int64_t row_bytes, int cb) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (!ok[i]) continue;
+    const uint32_t lo = fp8_pack4<E5>(x[i][0], x[i][1], x[i][2], x[i][3], s, ys);
+    const uint32_t hi = fp8_pack4<E5>(x[i][4], x[i][5], x[i][6], x[i][7], s, ys);
+    ((uint2*)(row0 + i * row_bytes))[cb] = make_uint2(lo, hi);
+  }
+}
+
+// FP8 value words of a wavefront's unit: channel 8 cb + j of tokens 8 r ..
+// 8 r + 7 (byte i of the word is token 8 r + i), in the 32-token block layout
+// (store_vword keeps the bytes of tokens outside `valid`).
+template <bool E5, int D>
+__device__ __forceinline__ void fp8_vwords(const float (&x)[8][8], uint32_t valid, float s, float ys, uint8_t* blk,
+                                           int cb, int r) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 8 * cb + j, n = c & 15, iw = c >> 4;
+    uint8_t* wp = blk + (int64_t)((16 * r + n) * (D / 16) + iw) * 8;
+    const uint32_t lo = fp8_pack4<E5>(x[0][j], x[1][j], x[2][j], x[3][j], s, ys);
+    const uint32_t hi = fp8_pack4<E5>(x[4][j], x[5][j], x[6][j], x[7][j], s, ys);
+    store_vword(wp, 8, valid, lo, hi);
+  }
+}
+
 template <int KS, int VS, int KAX>
 __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
   constexpr int D = 128;
@@ -799,7 +858,12 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) { st[i] = s8; zt[i] = 0.0f; rt[i] = r8; }
     }
-    if (pg >= 0) {
+    if (pg >= 0 && is_fp8(ksch) && rt[0] == rt[0]) {
+      // FP8 under an in-range scale (uniform per head): eight codes per token
+      // row from four conversions, no division
+      if (ksch == KVQ_FP8_E5M2) fp8_rows<true>(xk, ok, st[0], rt[0], krow0, p.k_row_bytes, cb);
+      else fp8_rows<false>(xk, ok, st[0], rt[0], krow0, p.k_row_bytes, cb);
+    } else if (pg >= 0) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (!ok[i]) continue;
@@ -840,6 +904,12 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
   const int bits = fv.bits;
   const uint32_t mask = (1u << bits) - 1;
   uint8_t* blk = a.arena + fv.codes + (row_of(p, pg, h, u0) >> 5) * p.v_block_bytes;
+  if (is_fp8(vsch) && vr[0] == vr[0]) {
+    // FP8 under an in-range scale: a word of eight tokens from four conversions
+    if (vsch == KVQ_FP8_E5M2) fp8_vwords<true, D>(xv, valid, vs[0], vr[0], blk, cb, r);
+    else fp8_vwords<false, D>(xv, valid, vs[0], vr[0], blk, cb, r);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = 8 * cb + j, n = c & 15, iw = c >> 4;

@@ -104,37 +104,22 @@ __device__ __forceinline__ uint32_t sym_code(float x, float s) {
   return (uint32_t)(int32_t)r & 0xFFu;
 }
 
-// E5M2 encode with saturation: nearest representable, ties to even (the
-// code's parity is its last mantissa bit's).
+// FP8 encodes with saturation: the magnitude is clamped to the largest finite
+// value (so NaN and infinity give the largest code, and the sign, also of
+// zero, is kept), then gfx950's conversion instruction rounds to the nearest
+// representable value, ties to even, subnormals included.  For inputs within
+// the range this is the same rounding as encoding by exponent and mantissa
+// (checked over every fp32 bit pattern from 0 to a little past the maximum
+// of each format); the instruction converts two values, the low byte of the
+// result is the first.
 __device__ __forceinline__ uint32_t e5m2_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), kE5M2Max);
-  uint32_t code;
-  if (a < 6.103515625e-05f) {                // below 2^-14: quantum 2^-16
-    code = (uint32_t)__builtin_rintf(a * 65536.0f);   // 0..4 (4 is the smallest normal)
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
-    uint32_t m = (uint32_t)__builtin_rintf(ldexpf(a, 2 - e));   // 4..8
-    if (m == 8) { m = 4; e += 1; }
-    code = ((uint32_t)(e + 15) << 2) | (m - 4);
-  }
-  return code | sign;
+  const float c = __builtin_copysignf(fminf(fabsf(y), kE5M2Max), y);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, c, 0, false) & 0xFFu;
 }
 
-// E4M3FN encode with saturation: nearest representable, ties to even.
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), kE4M3Max);
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: quantum 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 is the smallest normal)
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
-    uint32_t m = (uint32_t)__builtin_rintf(ldexpf(a, 3 - e));   // 8..16
-    if (m == 16) { m = 8; e += 1; }
-    code = ((uint32_t)(e + 7) << 3) | (m - 8);
-  }
-  return code | sign;
+  const float c = __builtin_copysignf(fminf(fabsf(y), kE4M3Max), y);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
 // Scale and zero-point a group with minimum mn and maximum mx (for symmetric

@@ -457,3 +457,53 @@ def test_quantizer_edge_cases(name, fmt, bits, big, sched):
         assert s_k[0] == np.float32(np.float32(1e-8) / np.float32(2 ** bits - 1)) or fmt.get("meta16")
         codes = st["k"]["codes"][0, 0, :32, 3]
         assert set(codes.tolist()) <= set(range(2 ** bits)) and (codes % 2 == 0).sum() > (codes % 2 == 1).sum()
+
+
+def _fp8_grid(e_bits, m_bits, vmax):
+    """Positive finite values of an FP8 format (bias 2^(e_bits-1) - 1,
+    subnormals below the first binade), up to vmax, from its definition."""
+    bias = 2 ** (e_bits - 1) - 1
+    vals = set()
+    for e in range(0, 2 ** e_bits):
+        for m in range(2 ** m_bits):
+            v = (m / 2 ** m_bits) * 2.0 ** (1 - bias) if e == 0 else (1 + m / 2 ** m_bits) * 2.0 ** (e - bias)
+            if v <= vmax:
+                vals.add(v)
+    return np.array(sorted(vals), np.float64)
+
+
+@pytest.mark.parametrize("fmt8", ["e4m3", "e5m2"])
+def test_fp8_codes_at_every_value_and_tie(fmt8):
+    """With a unit scale the encoder sees every representable value, every
+    midpoint between neighbours (ties go to the even code), the fp32 values
+    either side of each midpoint, zeros of both signs, the saturation region
+    past the largest value and the negatives of all of them: the codes must
+    equal the oracle's bit for bit."""
+    e_bits, m_bits, vmax = (4, 3, 448.0) if fmt8 == "e4m3" else (5, 2, 57344.0)
+    g = _fp8_grid(e_bits, m_bits, vmax)
+    mids = ((g[:-1] + g[1:]) / 2).astype(np.float32)
+    vals = [g.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)),
+            np.nextafter(mids, np.float32(-np.inf)),
+            np.array([0.0, vmax * 1.03, vmax * 1.0625, vmax * 4, 1e30], np.float32)]
+    pos = np.concatenate(vals).astype(np.float32)
+    x = np.concatenate([pos, -pos]).astype(np.float32)
+    D, Hkv = 128, 2
+    T = -(-x.size // (D * Hkv))
+    flat = np.zeros(Hkv * T * D, np.float32)
+    flat[:x.size] = x
+    flat[x.size:] = -0.0
+    Kf = flat.reshape(1, Hkv, T, D)
+    Vf = Kf[:, ::-1].copy()          # the same values, the other head first
+    spec = (F8, 8, 0, 0) if fmt8 == "e4m3" else (E5, 8, 0, 0)
+    case = Case(B=1, Hq=2, Hkv=Hkv, D=D, dtype="f32", k=spec, v=spec, R=0)
+    gc = GpuCache(case, cap=T)
+    one = np.ones(Hkv, np.float32)
+    if fmt8 == "e4m3":
+        gc.append(Kf, Vf, 0, one, one)
+        st = OC.quantize_cache(case.oracle_cfg(), Kf, Vf, T, k_scale=one, v_scale=one)
+    else:
+        gc.append(Kf, Vf, 0)
+        st = OC.quantize_cache(case.oracle_cfg(), Kf, Vf, T)
+    compare_sections(gc, st)
+    codes = np.asarray(st["k"]["codes"]).ravel()
+    assert (codes == 0x80).any() and (codes == 0x00).any()          # both zeros reached the encoder
