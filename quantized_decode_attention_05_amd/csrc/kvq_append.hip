@@ -1248,6 +1248,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
 
 // FP8 calibration over the valid tokens of every sequence (new_lens), for
 // paged calls: absmax per (kv head, side) into amax (u32 bit patterns).
+template <int DT, bool WIN>
 __global__ void __launch_bounds__(256) fp8_absmax_lens(Plan p, const void* kin, const void* vin, int n,
                                                         const int32_t* new_lens, uint32_t* amax) {
   const int h = blockIdx.y, side = blockIdx.z;
@@ -1256,7 +1257,7 @@ __global__ void __launch_bounds__(256) fp8_absmax_lens(Plan p, const void* kin, 
   const int64_t per_seq = (int64_t)n * p.D;
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
   const int D = p.D;
-  float m = absmax_runs(in, p.B, p.Hkv, h, per_seq, p.in_dtype, p.window != 0, gid, stride, [=](int b) {
+  float m = absmax_runs<DT, WIN>(in, p.B, p.Hkv, h, per_seq, gid, stride, [=](int b) {
     int64_t nl = new_lens ? (int64_t)new_lens[b] : n;
     nl = nl < 0 ? 0 : (nl > n ? n : nl);
     return nl * D;
@@ -1363,8 +1364,14 @@ hipError_t launch_append_fused(const Plan& p, void* arena, const PageMap& pm, co
 
 hipError_t launch_fp8_absmax_lens(const Plan& p, const void* k_new, const void* v_new, int n,
                                   const int32_t* new_lens, uint32_t* amax, hipStream_t s) {
-  hipLaunchKernelGGL(fp8_absmax_lens, dim3(fp8_absmax_blocks(p, n), p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new,
-                     n, new_lens, amax);
+  const dim3 grid(fp8_absmax_blocks(p, n), p.Hkv, 2);
+  const bool win = p.window != 0;
+#define KVQ_ABSMAX_LENS(DT, W) \
+  hipLaunchKernelGGL((fp8_absmax_lens<DT, W>), grid, dim3(256), 0, s, p, k_new, v_new, n, new_lens, amax)
+  if (p.in_dtype == KVQ_F32) { if (win) KVQ_ABSMAX_LENS(KVQ_F32, true); else KVQ_ABSMAX_LENS(KVQ_F32, false); }
+  else if (p.in_dtype == KVQ_F16) { if (win) KVQ_ABSMAX_LENS(KVQ_F16, true); else KVQ_ABSMAX_LENS(KVQ_F16, false); }
+  else { if (win) KVQ_ABSMAX_LENS(KVQ_BF16, true); else KVQ_ABSMAX_LENS(KVQ_BF16, false); }
+#undef KVQ_ABSMAX_LENS
   return hipGetLastError();
 }
 

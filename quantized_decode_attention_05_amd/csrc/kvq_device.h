@@ -210,23 +210,24 @@ __device__ __forceinline__ float dequant_elem(const Plan& p, const uint8_t* aren
 // Largest |x| of the values staged from 16 bytes of input (8 values of a
 // 16-bit type, 4 of fp32), as the quantizers stage them (through fp16 when the
 // cache keeps a window).
-__device__ __forceinline__ float absmax16(const uint4& w, int dtype, bool window) {
+template <int DT, bool WIN>
+__device__ __forceinline__ float absmax16(const uint4& w) {
   float m = 0.0f;
   const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float a, b;
-    if (dtype == KVQ_F32) {
+    if constexpr (DT == KVQ_F32) {
       a = __uint_as_float(q[j]);
       b = 0.0f;
-    } else if (dtype == KVQ_F16) {
+    } else if constexpr (DT == KVQ_F16) {
       a = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[j] & 0xFFFFu));
       b = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[j] >> 16));
     } else {
       a = bf16_to_f32((uint16_t)(q[j] & 0xFFFFu));
       b = bf16_to_f32((uint16_t)(q[j] >> 16));
     }
-    if (window) { a = stage_f16(a); b = stage_f16(b); }
+    if constexpr (WIN) { a = stage_f16(a); b = stage_f16(b); }
     m = fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
   }
   return m;
@@ -235,13 +236,17 @@ __device__ __forceinline__ float absmax16(const uint4& w, int dtype, bool window
 // absmax over the values of kv head h of every sequence b < B (run b holds
 // lens(b) values from base + (b * Hkv + h) * per_seq elements; per_seq and
 // every lens(b) a multiple of the values per 16 bytes, runs 16-byte
-// aligned), by the threads of a grid-stride (gid, stride).  Each round issues
-// sixteen 16-byte loads (four sequences, four strides) before using any.
-template <typename Lens>
-__device__ __forceinline__ float absmax_runs(const void* base, int B, int Hkv, int h, int64_t per_seq, int dtype,
-                                             bool window, int64_t gid, int64_t stride, Lens lens) {
-  const int per = dtype == KVQ_F32 ? 4 : 8;
-  const int esz = dtype == KVQ_F32 ? 4 : 2;
+// aligned), by the threads of a grid-stride (gid, stride), for input dtype DT
+// (staged through fp16 when WIN).  Each round issues sixteen 16-byte loads
+// (four sequences, four strides) before using any; a load past its run's end
+// reads the run's first granule (every run of a launch with a nonempty run
+// holds per_seq >= lens values) and its result is dropped, so no load sits
+// behind a branch.
+template <int DT, bool WIN, typename Lens>
+__device__ __forceinline__ float absmax_runs(const void* base, int B, int Hkv, int h, int64_t per_seq,
+                                             int64_t gid, int64_t stride, Lens lens) {
+  constexpr int per = DT == KVQ_F32 ? 4 : 8;
+  constexpr int esz = DT == KVQ_F32 ? 4 : 2;
   float m = 0.0f;
   for (int b0 = 0; b0 < B; b0 += 4) {
     const uint4* v[4];
@@ -260,12 +265,15 @@ __device__ __forceinline__ float absmax_runs(const void* base, int B, int Hkv, i
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int64_t e = i + k * stride;
-          w[u][k] = e < nv[u] ? v[u][e] : make_uint4(0u, 0u, 0u, 0u);
+          w[u][k] = v[u][e < nv[u] ? e : 0];
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m = fmaxf(m, absmax16(w[u][k], dtype, window));
+        for (int k = 0; k < 4; ++k) {
+          const float a = absmax16<DT, WIN>(w[u][k]);
+          m = i + k * stride < nv[u] ? fmaxf(m, a) : m;
+        }
     }
   }
   return m;

@@ -234,6 +234,7 @@ __global__ void fp8_zero(uint32_t* amax, int n) {
 }
 
 // absmax over (sequence, token, channel) of kv head h: grid (chunks, Hkv, 2 sides).
+template <int DT, bool WIN>
 __global__ void __launch_bounds__(256) fp8_absmax(Plan p, const void* kin, const void* vin, int n,
                                                    uint32_t* amax) {
   const int h = blockIdx.y, side = blockIdx.z;
@@ -241,8 +242,7 @@ __global__ void __launch_bounds__(256) fp8_absmax(Plan p, const void* kin, const
   // each sequence's run of n * D values (a multiple of 8, 16-byte aligned)
   const int64_t per_seq = (int64_t)n * p.D;
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
-  float m = absmax_runs(in, p.B, p.Hkv, h, per_seq, p.in_dtype, p.window != 0, gid, stride,
-                        [=](int) { return per_seq; });
+  float m = absmax_runs<DT, WIN>(in, p.B, p.Hkv, h, per_seq, gid, stride, [=](int) { return per_seq; });
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float sm[4];
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
@@ -342,8 +342,18 @@ hipError_t launch_fp8_setup(const Plan& p, void* arena, const void* k_new, const
       const hipError_t e = launch_fp8_absmax_lens(p, k_new, v_new, n_new, new_lens, amax, s);
       if (e != hipSuccess) return e;
     } else {
-      hipLaunchKernelGGL(fp8_absmax, dim3(fp8_absmax_blocks(p, n_new), p.Hkv, 2), dim3(256), 0, s, p, k_new, v_new,
-                         n_new, amax);
+      const dim3 grid(fp8_absmax_blocks(p, n_new), p.Hkv, 2);
+      const bool win = p.window != 0;
+      if (p.in_dtype == KVQ_F32) {
+        if (win) hipLaunchKernelGGL((fp8_absmax<KVQ_F32, true>), grid, dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+        else hipLaunchKernelGGL((fp8_absmax<KVQ_F32, false>), grid, dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+      } else if (p.in_dtype == KVQ_F16) {
+        if (win) hipLaunchKernelGGL((fp8_absmax<KVQ_F16, true>), grid, dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+        else hipLaunchKernelGGL((fp8_absmax<KVQ_F16, false>), grid, dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+      } else {
+        if (win) hipLaunchKernelGGL((fp8_absmax<KVQ_BF16, true>), grid, dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+        else hipLaunchKernelGGL((fp8_absmax<KVQ_BF16, false>), grid, dim3(256), 0, s, p, k_new, v_new, n_new, amax);
+      }
     }
   }
   return launch_fp8_finalize(p, arena, k_scale, v_scale, calibrate, s);
