@@ -644,23 +644,12 @@ attn_mfma(Plan p, Args a) {
   // below from them once the stage has landed
   const bool vm16 = VINT && p.v.meta16, km16 = KINT && p.k.meta16;
   const int vesz = vm16 ? 2 : 4, kesz = km16 ? 2 : 4;
-  // first token past the page the issue side is in (paged caches): the step
-  // loop compares against it instead of dividing by P every step
-  int64_t page_end = 0;
-  auto init_ptrs = [&](int64_t t0) __attribute__((always_inline)) {
-    // token row of t0: through this split's page table, or (b, h)'s own rows
-    int64_t tr;
-    if (paged) {
-      // every issued step lies below the split's end, inside the table; the
-      // clamp only keeps set-up lookups of unused pointers inside the array
-      const int64_t j = t0 / p.P;
-      page_end = (j + 1) * p.P;
-      int64_t jj = j - blk0;
-      jj = jj < 0 ? 0 : (jj > kMaxSplitPages - 1 ? kMaxSplitPages - 1 : jj);
-      tr = ((int64_t)page_s[jj] * p.Hkv + kvh) * p.P + (t0 - j * p.P);
-    } else {
-      tr = bh * p.Tc + t0;
-    }
+  // page the issue side is in and the first token past it (paged caches): the
+  // step loop compares against page_end instead of dividing by P every step
+  int64_t page_end = 0, page_j = 0;
+  // stream pointers of the step whose first token sits in token row tr, with
+  // its key group's metadata in row krow
+  auto set_ptrs = [&](int64_t tr, int64_t krow) __attribute__((always_inline)) {
     pk = arena + p.k.codes + tr * KROW + 16 * lane;
     pv = arena + p.v.codes + (tr >> 5) * SZ_V + 16 * lane;
     if constexpr (VINT) {
@@ -686,12 +675,46 @@ attn_mfma(Plan p, Args a) {
     if constexpr (KINT) {
       // scale row (lanes 0-31) and zero-point row (lanes 32-63) of the key
       // group; fp16 rows: lanes 0-15 and 16-31
-      const int64_t mrow = (tr / p.k.group) * D * kesz;
+      const int64_t mrow = krow * D * kesz;
       if (km16) pkm = lane < 16 ? arena + p.k.scale + mrow + 16 * lane : arena + p.k.zero + mrow + 16 * (lane - 16);
       else pkm = lane < 32 ? arena + p.k.scale + mrow + 16 * km_pos(lane)
                            : arena + p.k.zero + mrow + 16 * km_pos(lane - 32);
     }
+  };
+  auto init_ptrs = [&](int64_t t0) __attribute__((always_inline)) {
+    // token row of t0: through this split's page table, or (b, h)'s own rows
+    int64_t tr;
+    if (paged) {
+      // every issued step lies below the split's end, inside the table; the
+      // clamp only keeps set-up lookups of unused pointers inside the array
+      const int64_t j = t0 / p.P;
+      page_j = j;
+      page_end = (j + 1) * p.P;
+      int64_t jj = j - blk0;
+      jj = jj < 0 ? 0 : (jj > kMaxSplitPages - 1 ? kMaxSplitPages - 1 : jj);
+      tr = ((int64_t)page_s[jj] * p.Hkv + kvh) * p.P + (t0 - j * p.P);
+    } else {
+      tr = bh * p.Tc + t0;
+    }
+    set_ptrs(tr, KINT ? tr / p.k.group : 0);
     if constexpr (ROPE) prp = arena + p.rope + ((32 + (t0 >> 5)) * 64) * 8 + 16 * lane;
+  };
+  // key-group rows per page (pages hold whole key groups)
+  const int64_t page_groups = KINT && paged ? p.P / p.k.group : 0;
+  // The issue side has passed page_end (paged caches): the pointers of the
+  // page it entered, with no division.  Steps of caches with per-group key
+  // metadata advance 32 tokens at a time and pages are whole multiples of 32
+  // tokens, so such a step enters its page at the page's first token, where
+  // a key group starts; interleaved FP8 steps may enter further in.
+  auto next_page = [&](int64_t t0) __attribute__((always_inline)) {
+    do {
+      ++page_j;
+      page_end += p.P;
+    } while (t0 >= page_end);
+    int64_t jj = page_j - blk0;
+    jj = jj < 0 ? 0 : (jj > kMaxSplitPages - 1 ? kMaxSplitPages - 1 : jj);
+    const int64_t base = (int64_t)page_s[jj] * p.Hkv + kvh;
+    set_ptrs(base * p.P + (t0 - (page_end - p.P)), base * page_groups);
   };
   auto issue = [&](int sl) __attribute__((always_inline)) {
     const u32 sb = __builtin_amdgcn_readfirstlane(ring_lds + sl * SLOT);
@@ -1079,7 +1102,7 @@ attn_mfma(Plan p, Args a) {
       // a paged cache continues on another page: pointers from the page table
       // (steps only move forward, so leaving the page means passing its end)
       if (paged) {
-        if (i_pos < iss_end && i_pos >= page_end) init_ptrs(i_pos);
+        if (i_pos < iss_end && i_pos >= page_end) next_page(i_pos);
       }
     };
 #pragma unroll
