@@ -73,3 +73,102 @@ def _draw(i):
 def test_random_configuration_matches_the_oracle(i):
     case, T, sched, splits = _draw(i)
     run_case(case, T, _schedule(sched, T), seed=500 + i, num_splits=splits)
+
+
+N_PAGED = 16
+
+
+def _draw_paged(i):
+    """Paged configuration i: (case, page tokens, prefill lengths, chunk lengths, decode steps)."""
+    rng = np.random.default_rng((2029, i))
+    while True:
+        kk = rng.choice(["int_ch", "int_ch", "fp8", "e5m2", "sym8"])
+        if kk == "int_ch":
+            k = (A, int(rng.choice([2, 4, 8])), CH, int(rng.choice([32, 64, 128])))
+        elif kk == "fp8":
+            k = (F8, 8, 0, 0)
+        elif kk == "e5m2":
+            k = (E5, 8, 0, 0)
+        else:
+            k = (S, 8, TOK, 0)
+        vk = rng.choice(["int", "int", "fp8", "e5m2"])
+        if vk == "int":
+            v = (A, int(rng.choice([2, 4, 8])), TOK, int(rng.choice([16, 32, 64, 0])))
+        elif vk == "fp8":
+            v = (F8, 8, 0, 0)
+        else:
+            v = (E5, 8, 0, 0)
+        gt = k[3] if k[2] == CH else 32
+        P = gt * int(rng.choice([1, 2, 4])) if gt >= 32 else 32 * int(rng.choice([1, 2, 8]))
+        R = int(rng.choice([0, 1, 2])) * gt
+        pre_rope = bool(k[2] == CH or k[0] in (F8, E5)) and rng.random() < 0.35
+        meta16 = rng.random() < 0.25
+        Hkv = int(rng.choice([1, 2]))
+        n_rep = int(rng.choice([1, 4, 8, 12, 20]))
+        B = int(rng.choice([1, 2, 3, 4]))
+        pre = [int(x) for x in rng.integers(0, 900, B)]
+        chunk = [int(x) for x in rng.integers(0, 40, B)]
+        # every sequence holds a token before its first decode step
+        chunk = [c if p_ or c else 1 for p_, c in zip(pre, chunk)]
+        steps = int(rng.integers(1, 40))
+        case = Case(B=B, Hq=Hkv * n_rep, Hkv=Hkv, D=128, dtype="bf16", k=k, v=v, R=R, pre_rope=pre_rope,
+                    meta16=meta16)
+        try:
+            K.make_config(batch=B, num_q_heads=case.Hq, num_kv_heads=Hkv, head_dim=128, max_tokens=1024, k=k, v=v,
+                          in_dtype=K.BF16, out_dtype=K.F32, residual=R, pre_rope_k=pre_rope,
+                          meta_dtype=K.F16 if meta16 else K.F32, page_tokens=P, num_pages=B * 40)
+        except K.KvqError:
+            continue
+        return case, P, pre, chunk, steps
+
+
+@pytest.mark.parametrize("i", range(N_PAGED), ids=[f"paged{i:02d}" for i in range(N_PAGED)])
+def test_random_paged_configuration_matches_the_oracle(i):
+    """A ragged prefill, a ragged chunk and decode steps through the paged
+    entry points; each sequence's sections, dequantized values and attention
+    (after the steps, on every kernel, at a drawn split count) against the
+    oracle of that sequence alone."""
+    import math
+    import torch
+    import workloads as W
+    from oracle import attention as OA
+    from tests.kvq_harness import ATTN_TOL, PagedCache, compare_paged_sequence
+    from tests.test_gpu_paged import _fp8_scales, _kernels, _oracle_seq, _rows
+    case, P, pre, chunk, steps = _draw_paged(i)
+    seed = 700 + i
+    Tmax = max(p + c for p, c in zip(pre, chunk)) + steps
+    (Kf, Kp), (Vf, Vp) = W.random_case(seed, case.B, case.Hkv, Tmax, case.D, dtype="bf16")
+    pc = PagedCache(case, P, cap=Tmax + 8, seed=seed)
+    fp8 = case.k[0] == F8 or case.v[0] == F8
+    n0 = max(max(pre), 1)
+    pc.append(np.stack([_rows(Kp, b, 0, pre[b], n0) for b in range(case.B)]),
+              np.stack([_rows(Vp, b, 0, pre[b], n0) for b in range(case.B)]), pre,
+              K.INIT | (K.CALIBRATE if fp8 else 0))
+    scales = _fp8_scales(case, Kf, Vf, pre)
+    n1 = max(max(chunk), 1)
+    pc.append(np.stack([_rows(Kp, b, pre[b], pre[b] + chunk[b], n1) for b in range(case.B)]),
+              np.stack([_rows(Vp, b, pre[b], pre[b] + chunk[b], n1) for b in range(case.B)]), chunk)
+    ws = torch.zeros(K.kvq_workspace_bytes(pc.cfg, Tmax + 8), dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
+    for s in range(steps):
+        t = pc.lens.copy()
+        kn = np.stack([Kp[b, :, t[b]:t[b] + 1] for b in range(case.B)])
+        vn = np.stack([Vp[b, :, t[b]:t[b] + 1] for b in range(case.B)])
+        pc.step(kn, vn, W.random_queries(seed + 100 + s, case.B, case.Hq, case.D, dtype="bf16")[1], ws, out)
+    torch.cuda.synchronize()
+    kd, vd = pc.dequantize()
+    sm = 1.0 / math.sqrt(case.D)
+    qf, qp = W.random_queries(seed + 7, case.B, case.Hq, case.D, dtype="bf16")
+    splits = int(np.random.default_rng((2031, i)).choice([0, 1, 3, 9]))
+    outs = {kern: pc.attention(qp, kernel=kern, num_splits=splits) for kern in _kernels(pc.cfg, int(pc.lens.max()))}
+    for b in range(case.B):
+        T = int(pc.lens[b])
+        st = _oracle_seq(case, Kf, Vf, b, T, scales)
+        compare_paged_sequence(pc, b, st, None if scales is None else {"k": scales[0], "v": scales[1]})
+        assert np.array_equal(kd[b, :, :T], st["k_hat"][0]), f"seq {b}: dequantized K differs"
+        assert np.array_equal(vd[b, :, :T], st["v_hat"][0]), f"seq {b}: dequantized V differs"
+        ref = OA.decode_attention(qf[b:b + 1], st["k_hat"], st["v_hat"], sm,
+                                  pre_rope_base=case.rope_base if case.pre_rope else None)
+        for kern, o in outs.items():
+            err = OA.max_rel_l2_per_head(o[b:b + 1], ref)
+            assert err <= ATTN_TOL, (i, kern, splits, b, err)
