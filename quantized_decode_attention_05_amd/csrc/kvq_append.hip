@@ -1055,6 +1055,50 @@ __device__ __forceinline__ void asym_codes8_h(const _Float16 (&xh)[8], const flo
   }
 }
 
+// Group metadata of fp16-staged values without an IEEE division.  A group's
+// range d lies in [1e-8, 2^17] (fp16 magnitudes are at most 65504; the floor
+// is 1e-8) unless the input overflowed fp16 (then it is infinite or NaN):
+//   s = RN(d / qmax) by the correction step with yq = RN(1 / qmax), which
+//   gives the correctly rounded quotient for every fp32 d in [1e-8, 2^17]
+//   and qmax in {3, 15, 127, 255} (checked exhaustively against the
+//   division); an infinite or NaN d takes d * yq, which equals d / qmax there;
+//   1 / s by the hardware reciprocal and one Newton step with FMA, the
+//   correctly rounded reciprocal for every s in [2^-40, 2^21) (checked for
+//   every significand; the scales here lie in [2^-35, 2^16]); beyond, the
+//   bare reciprocal (1 / inf = 0).
+__device__ __forceinline__ float div_qmax(float d, float qm, float yq) {
+  const float q0 = d * yq;
+  const float r = __builtin_fmaf(-q0, qm, d);
+  const float q = __builtin_fmaf(r, yq, q0);
+  return d <= 0x1p17f ? q : q0;
+}
+__device__ __forceinline__ float recip_rn(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y0, 1.0f);
+  const float y1 = __builtin_fmaf(e, y0, y0);
+  return s < 0x1p21f ? y1 : y0;
+}
+// meta_values for fp16-staged groups (same results), yq = RN(1 / qmax) of
+// the side (1 / 127 for symmetric groups).
+__device__ __forceinline__ void meta_values_h(const SideFmt& f, float mn, float mx, float yq, float* s, float* z) {
+  if (f.scheme == KVQ_INT_ASYM) {
+    const float qm = (float)((1 << f.bits) - 1);
+    if (f.meta16) {
+      const _Float16 zh = f16_directed(mn, false);
+      const float sc = div_qmax(fmaxf(mx - (float)zh, 1e-8f), qm, yq);
+      *s = (float)f16_directed(sc, true);
+      *z = (float)zh;
+    } else {
+      *s = div_qmax(fmaxf(mx - mn, 1e-8f), qm, yq);
+      *z = mn;
+    }
+  } else {
+    const float sc = div_qmax(fmaxf(mx, 1e-8f), 127.0f, yq);
+    *s = f.meta16 ? (float)f16_directed(sc, true) : sc;
+    *z = 0.0f;
+  }
+}
+
 __device__ __forceinline__ void rows_minmax_h(uint32_t& mn, uint32_t& mx) {
   auto r = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
   mn = as_u32(__builtin_elementwise_min(as_h2(r[0]), as_h2(r[1])));
@@ -1128,6 +1172,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   {
     const SideFmt& fk = p.k;
     const float qmax = (float)((1 << fk.bits) - 1);
+    const float yqk = 1.0f / (fk.scheme == KVQ_INT_ASYM ? qmax : 127.0f);   // once per wavefront
     uint32_t umn[4], umx[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -1167,8 +1212,8 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int j = 2 * m + e;
-        meta_values(fk, (float)as_h2(umn[m])[e], (float)as_h2(umx[m])[e], &sc[j], &zc[j]);
-        rc[j] = 1.0f / sc[j];
+        meta_values_h(fk, (float)as_h2(umn[m])[e], (float)as_h2(umx[m])[e], yqk, &sc[j], &zc[j]);
+        rc[j] = recip_rn(sc[j]);
       }
     }
     if (pg >= 0) {
@@ -1204,6 +1249,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   // ---- values: per-token groups of Gc channels, words of 8 tokens formed in the lane ----
   const SideFmt& fv = p.v;
   const float qmax = (float)((1 << fv.bits) - 1);
+  const float yqv = 1.0f / (fv.scheme == KVQ_INT_ASYM ? qmax : 127.0f);
   float vs[8], vz[8], vr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -1213,8 +1259,8 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
                                         __builtin_elementwise_max(as_h2(hv[i][2]), as_h2(hv[i][3])));
     float fmn = fminf((float)mn[0], (float)mn[1]), fmx = fmaxf((float)mx[0], (float)mx[1]);
     lane_minmax(fmn, fmx, 1, fv.group / 8);
-    meta_values(fv, fmn, fmx, &vs[i], &vz[i]);
-    vr[i] = 1.0f / vs[i];
+    meta_values_h(fv, fmn, fmx, yqv, &vs[i], &vz[i]);
+    vr[i] = recip_rn(vs[i]);
     if (ok[i] && pg >= 0 && (cb % (fv.group / 8)) == 0)
       store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, us + 8 * r + i), 8 * cb),
                         vs[i], vz[i]);
