@@ -1250,6 +1250,12 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
   const SideFmt& fv = p.v;
   const float qmax = (float)((1 << fv.bits) - 1);
   const float yqv = 1.0f / (fv.scheme == KVQ_INT_ASYM ? qmax : 127.0f);
+  // the first lane of each value group stores the group's metadata; the
+  // lane's eight tokens are consecutive token rows (a unit never straddles a
+  // page), so their metadata indices step by the row's group count
+  const int gl = fv.group / 8;                       // lanes per value group
+  const bool vlane = pg >= 0 && (cb % gl) == 0;
+  const int64_t vmi0 = vlane ? row_of(p, pg, h, us + 8 * r) * fv.meta_cols + cb / gl : 0;
   float vs[8], vz[8], vr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -1261,9 +1267,7 @@ __global__ void __launch_bounds__(256) append_kivi_h(Plan p, AppendArgs a) {
     lane_minmax(fmn, fmx, 1, fv.group / 8);
     meta_values_h(fv, fmn, fmx, yqv, &vs[i], &vz[i]);
     vr[i] = recip_rn(vs[i]);
-    if (ok[i] && pg >= 0 && (cb % (fv.group / 8)) == 0)
-      store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, us + 8 * r + i), 8 * cb),
-                        vs[i], vz[i]);
+    if (ok[i] && vlane) store_meta_values(fv, a.arena, vmi0 + i * fv.meta_cols, vs[i], vz[i]);
   }
   if (pg < 0) return;
   uint32_t valid = 0;
