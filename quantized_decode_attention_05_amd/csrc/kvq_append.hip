@@ -864,12 +864,15 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
       if (ksch == KVQ_FP8_E5M2) fp8_rows<true>(xk, ok, st[0], rt[0], krow0, p.k_row_bytes, cb);
       else fp8_rows<false>(xk, ok, st[0], rt[0], krow0, p.k_row_bytes, cb);
     } else if (pg >= 0) {
+      // per-token key groups: the first lane of each group stores its
+      // metadata; the lane's tokens are consecutive token rows
+      const int gl = k_int ? fk.group / 8 : 1;
+      const bool klane = k_int && (cb % gl) == 0;
+      const int64_t kmi0 = klane ? row_of(p, pg, h, u0 + 8 * r) * fk.meta_cols + cb / gl : 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (!ok[i]) continue;
-        if (k_int && (cb % (fk.group / 8)) == 0)
-          store_meta_values(fk, a.arena, meta_index_row(p, fk, bh, h, row_of(p, pg, h, u0 + 8 * r + i), 8 * cb),
-                            st[i], zt[i]);
+        if (klane) store_meta_values(fk, a.arena, kmi0 + i * fk.meta_cols, st[i], zt[i]);
         uint32_t c[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) c[j] = code_t<KS>(fk, xk[i][j], st[i], rt[i], zt[i]);
@@ -885,11 +888,13 @@ __global__ void __launch_bounds__(256) append_wave(Plan p, AppendArgs a) {
   float vs[8], vz[8], vr[8];
   if (v_int) {
     token_groups<VS>(fv, xv, vs, vz, vr);
+    const int gl = fv.group / 8;
+    if (pg >= 0 && (cb % gl) == 0) {
+      const int64_t vmi0 = row_of(p, pg, h, u0 + 8 * r) * fv.meta_cols + cb / gl;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (ok[i] && pg >= 0 && (cb % (fv.group / 8)) == 0)
-        store_meta_values(fv, a.arena, meta_index_row(p, fv, bh, h, row_of(p, pg, h, u0 + 8 * r + i), 8 * cb),
-                          vs[i], vz[i]);
+      for (int i = 0; i < 8; ++i)
+        if (ok[i]) store_meta_values(fv, a.arena, vmi0 + i * fv.meta_cols, vs[i], vz[i]);
+    }
   } else {
     const float s8 = is_fp8(vsch) ? ((const float*)(a.arena + fv.scale))[h] : 1.0f;
     const float r8 = fp8_recip(s8);
