@@ -289,15 +289,17 @@ __device__ __forceinline__ void lane_minmax(float& mn, float& mx, int from, int 
 
 // Write the 8 codes of one granule (channels 8 cb .. 8 cb + 7) into a key row.
 __device__ __forceinline__ void write_k_granule(uint8_t* row, int cb, int bits, const uint32_t* c) {
+  // 2- and 4-bit codes come from the asymmetric encoders, clamped to
+  // [0, 2^bits - 1]: no mask before they are shifted into place
   if (bits == 2) {
     uint32_t v = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v |= (c[j] & 3u) << (2 * j);
+    for (int j = 0; j < 8; ++j) v |= c[j] << (2 * j);
     ((uint16_t*)row)[cb] = (uint16_t)v;
   } else if (bits == 4) {
     uint32_t v = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v |= (c[j] & 15u) << (4 * j);
+    for (int j = 0; j < 8; ++j) v |= c[j] << (4 * j);
     ((uint32_t*)row)[cb] = v;
   } else if (bits == 8) {
     uint32_t lo = 0, hi = 0;
