@@ -321,8 +321,8 @@ def main():
                     help="with --paged: sequence b holds T - (1021 b mod 8192) tokens instead of T")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
-              f"(the path shards over (sequence, kv head) pairs without communication; see DESIGN.md)",
+        print(f"bench.py: runs on one GPU; --gpus {a.gpus} is not supported "
+              f"(the path shards over (sequence, kv head) pairs without communication)",
               file=sys.stderr)
         sys.exit(2)
 
