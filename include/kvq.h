@@ -250,7 +250,11 @@ int kvq_workspace_bytes(const kvq_config* cfg, int64_t T, const kvq_attn_options
  *   out: device [B][Hq][D] in cfg->out_dtype (fp32 recommended).
  *   sm_scale: logit scale, normally 1/sqrt(D).
  *   workspace: device scratch of kvq_workspace_bytes (split partials).
- * T must satisfy 1 <= T <= max_tokens.
+ * T must satisfy 1 <= T <= max_tokens.  The query heads of a kv head are
+ * served together by each work-group when they fit its rows (16 (value
+ * group, head) rows, 32 for eight heads over four INT2/INT4 value groups);
+ * more heads are split into groups of near-equal size, each group streaming
+ * the kv head's cache itself.
  */
 int kvq_decode_attention(const kvq_config* cfg, const void* arena, int64_t T,
                          const void* q, void* out, float sm_scale,
@@ -284,11 +288,12 @@ int kvq_decode_attention_static(const kvq_config* cfg, const void* arena, int64_
  * followed by kvq_decode_attention(T) (the append order of the decode step:
  * "...Need Different Axes", section "What should I actually turn on in
  * production?", and the decode loop of the configs).  When the MFMA kernel
- * serves the shape and the new token needs no fold (it enters the fp16
- * window, or both sides are FP8 with no window), the append runs inside the
- * attention launch: the work-group whose token range holds t0 writes the
- * token before it reads the cache, so one launch does both; otherwise the
- * two calls run in turn.  Arguments as in the two calls (k_new, v_new:
+ * serves the shape with one work-group per (sequence, kv head, split) (at
+ * most 16 query heads per kv head, fewer with several value groups) and the
+ * new token needs no fold (it enters the fp16 window, or both sides are FP8
+ * with no window), the append runs inside the attention launch: the
+ * work-group whose token range holds t0 writes the token before it reads
+ * the cache, so one launch does both; otherwise the two calls run in turn.  Arguments as in the two calls (k_new, v_new:
  * [B][Hkv][1][D] in cfg->in_dtype; no FP8 scales or calibration here).
  */
 int kvq_decode_step(const kvq_config* cfg, void* arena, int64_t t0, const void* k_new,
