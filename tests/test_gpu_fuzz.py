@@ -172,3 +172,81 @@ def test_random_paged_configuration_matches_the_oracle(i):
         for kern, o in outs.items():
             err = OA.max_rel_l2_per_head(o[b:b + 1], ref)
             assert err <= ATTN_TOL, (i, kern, splits, b, err)
+
+
+N_STEP = 12
+
+
+def _draw_step(i):
+    """Decode-step configuration i: (case, prefill length, steps, splits)."""
+    rng = np.random.default_rng((2033, i))
+    while True:
+        kk = rng.choice(["int_ch", "int_ch", "fp8", "e5m2"])
+        if kk == "int_ch":
+            k = (A, int(rng.choice([2, 4, 8])), CH, int(rng.choice([32, 64, 128])))
+        elif kk == "fp8":
+            k = (F8, 8, 0, 0)
+        else:
+            k = (E5, 8, 0, 0)
+        vk = rng.choice(["int", "fp8", "e5m2"])
+        v = (A, int(rng.choice([2, 4, 8])), TOK, int(rng.choice([16, 32, 0]))) if vk == "int" else \
+            ((F8, 8, 0, 0) if vk == "fp8" else (E5, 8, 0, 0))
+        gt = k[3] if k[2] == CH else 32
+        R = int(rng.choice([0, 1, 2])) * gt
+        pre_rope = rng.random() < 0.3
+        Hkv = int(rng.choice([1, 2]))
+        n_rep = int(rng.choice([1, 4, 8, 16, 24]))
+        case = Case(B=int(rng.choice([1, 2, 3])), Hq=Hkv * n_rep, Hkv=Hkv, D=128, dtype="bf16", k=k, v=v, R=R,
+                    pre_rope=pre_rope, meta16=rng.random() < 0.2)
+        T0 = int(rng.integers(1, 700))
+        steps = int(rng.integers(5, 45))
+        splits = int(rng.choice([0, 1, 3, 7]))
+        try:
+            case.lib_cfg(T0 + steps)
+        except K.KvqError:
+            continue
+        return case, T0, steps, splits
+
+
+@pytest.mark.parametrize("i", range(N_STEP), ids=[f"step{i:02d}" for i in range(N_STEP)])
+def test_random_decode_steps_equal_append_then_attention(i):
+    """kvq_decode_step (the call bench.py times; the append runs inside the
+    attention launch when the shape allows) against kvq_quantize_append
+    followed by kvq_decode_attention on a second cache: the same cache bytes
+    and the same outputs, bit for bit, at every step; the final output within
+    tolerance of the oracle."""
+    import math
+    import torch
+    import workloads as W
+    from oracle import attention as OA
+    from oracle import cache as OC
+    from tests.kvq_harness import ATTN_TOL, GpuCache, to_dev
+    case, T0, steps, splits = _draw_step(i)
+    (Kf, Kp), (Vf, Vp) = W.random_case(900 + i, case.B, case.Hkv, T0 + steps, case.D, dtype="bf16")
+    ga, gb = GpuCache(case, cap=T0 + steps), GpuCache(case, cap=T0 + steps)
+    fp8 = case.k[0] == F8 or case.v[0] == F8
+    flags = K.CALIBRATE if fp8 else 0
+    ga.append(Kp[:, :, :T0], Vp[:, :, :T0], flags)
+    gb.append(Kp[:, :, :T0], Vp[:, :, :T0], flags)
+    sm = 1.0 / math.sqrt(case.D)
+    wa = torch.zeros(K.kvq_workspace_bytes(ga.cfg, T0 + steps, 0, splits), dtype=torch.uint8, device="cuda")
+    wb = torch.zeros(K.kvq_workspace_bytes(gb.cfg, T0 + steps, 0, splits), dtype=torch.uint8, device="cuda")
+    oa = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    for s in range(steps):
+        t = T0 + s
+        kn, vn = to_dev(Kp[:, :, t:t + 1], "bf16"), to_dev(Vp[:, :, t:t + 1], "bf16")
+        qf, qp = W.random_queries(3000 + 50 * i + s, case.B, case.Hq, case.D, dtype="bf16")
+        q = to_dev(qp, "bf16")
+        oa.fill_(float("nan"))
+        ob.fill_(float("nan"))
+        K.kvq_decode_step(ga.cfg, ga.arena, t, kn, vn, q, oa, sm, wa, 0, splits)
+        K.kvq_quantize_append(gb.cfg, gb.arena, t, kn, vn)
+        K.kvq_decode_attention(gb.cfg, gb.arena, t + 1, q, ob, sm, wb, 0, splits)
+        torch.cuda.synchronize()
+        assert torch.equal(ga.arena, gb.arena), (i, t, "cache bytes differ")
+        assert torch.isfinite(oa).all() and torch.equal(oa, ob), (i, t, "outputs differ")
+    T = T0 + steps
+    st = OC.quantize_cache(case.oracle_cfg(), Kf, Vf, T, calibrate_tokens=T0 if fp8 else 0)
+    ref = OA.decode_attention(qf, st["k_hat"], st["v_hat"], sm, pre_rope_base=case.rope_base if case.pre_rope else None)
+    assert OA.max_rel_l2_per_head(oa.cpu().numpy(), ref) <= ATTN_TOL
