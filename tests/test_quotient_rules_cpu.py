@@ -145,3 +145,44 @@ def test_correction_step_loses_the_sign_of_zero_and_copysign_restores_it():
     ss = np.full(xs.shape, s, F32)
     q = _correction_step(np.abs(xs), ss) * np.sign(xs).astype(F32)
     assert np.array_equal(np.signbit(q), np.signbit(xs))
+
+
+def test_scale_by_correction_step_with_reciprocal_of_qmax():
+    """The fp16-staged append takes s = RN(range / qmax) as the correction
+    step with y = RN(1 / qmax): correctly rounded for ranges in [1e-8, 2^17]
+    (random ranges over the whole span, and ranges planted next to the
+    quotient midpoints; the GPU probe checks every fp32 range there)."""
+    rng = np.random.default_rng(16)
+    n = 1 << 16
+    for qmax in (3, 15, 127, 255):
+        d = (2.0 ** rng.uniform(np.log2(1e-8), 17, n)).astype(F32)
+        # ranges whose quotient sits next to a midpoint between two fp32 values
+        qv = (2.0 ** rng.uniform(np.log2(1e-8 / qmax), np.log2(2.0 ** 17 / qmax), n)).astype(F32)
+        half_ulp = (np.nextafter(qv, F32(np.inf)).astype(F64) - qv.astype(F64)) / 2
+        mid = ((qv.astype(F64) + half_ulp) * qmax).astype(F32)
+        for x in (d, mid, np.nextafter(mid, F32(np.inf)), np.nextafter(mid, F32(0))):
+            x = x[(x >= F32(1e-8)) & (x <= F32(2.0 ** 17))]
+            s = np.full(x.shape, F32(qmax))
+            ref = (x.astype(F64) / F64(qmax)).astype(F32)
+            assert np.array_equal(_correction_step(x, s), ref), qmax
+
+
+def test_newton_reciprocal_depends_on_the_hardware_estimate():
+    """One Newton step y0 + y0 (1 - s y0) from the correctly rounded 1/s gives
+    it back, but from an estimate one ulp away it is not always correctly
+    rounded (the all-ones significand is such a case): the kernels' use of the
+    hardware reciprocal rests on the GPU probe, which checks every
+    significand against the correctly rounded reciprocal."""
+    from fractions import Fraction
+    s = np.array([np.nextafter(F32(2.0), F32(0)) * F32(2.0) ** k for k in range(-30, 16)] +
+                 [F32(1.5), F32(1.1), F32(3.0)], F32)
+    ref = (F64(1) / s.astype(F64)).astype(F32)
+
+    def step(y0):
+        e = (F64(1) - s.astype(F64) * y0.astype(F64)).astype(F32)      # one rounding (exact product and sum)
+        return np.array([F32(_rn32(Fraction(float(a)) + Fraction(float(b)) * Fraction(float(a))))
+                         if (Fraction(float(a)) + Fraction(float(b)) * Fraction(float(a))) > 0 else F32(0)
+                         for a, b in zip(y0, e)], F32)
+    assert np.array_equal(step(ref), ref)
+    low = np.nextafter(ref, F32(0))
+    assert not np.array_equal(step(low)[:46], ref[:46])               # the all-ones significands fail from below
