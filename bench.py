@@ -41,7 +41,7 @@ LIMITER = {
     "c3_fp8_e4m3_gqa_8k": "hbm streaming (~6.7 TB/s marginal) plus ~8.6 us fixed per-launch cost",
     "c3_fp8_e5m2_gqa_8k": "hbm streaming plus fixed per-launch cost, as the E4M3 cache",
     "c4_int4_llama70b_128k": "~11 us fixed per-launch cost at batch 1 (two kernels, start-up) over ~5.1 TB/s streaming, latency-bound 32-token steps at two wavefronts per SIMD",
-    "c5_int2_kivi_prerope_32k": "vector-ALU issue (~634 VALU instructions per 32-token step, ~67% of SIMD cycles): pre-RoPE dequantize, rotation and fp16 split per key pair",
+    "c5_int2_kivi_prerope_32k": "vector-ALU issue (~634 VALU instructions per 32-token step, ~67% of SIMD cycles: pre-RoPE dequantize, rotation and fp16 split per key pair) and the step's dependent chain at two wavefronts per SIMD (a variant with the rotation on the matrix unit, 455 per step, ran in equal time)",
 }
 DESCR = {
     "c3_fp8_e4m3_gqa_8k": "FP8 E4M3 K/V, per-kv-head calibrated scales",
